@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Throughput of the top-k sparse MQA hot path (forward + backward) on one MI355X.
+
+One step = one pass of the whole path over one batch of seeded synthetic input: the forward
+(O, LSE), then the backward on those outputs (Delta preprocess, accumulator clear, dQ kernel,
+dKV scatter kernel, fp32 -> bf16 postprocess). Inputs are resident in HBM before timing starts.
+
+Prints one JSON line. `value` is the step's algorithmic TFLOP/s: (4 + 10) * H * D flops per valid
+(token, slot) pair (forward 4HD: QK^T and PV; backward 10HD: score recompute, dP, dQ, dKV) divided
+by the measured step time. Per-kernel times come from HIP events recorded on the stream the
+kernels run on.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+METRIC = "sparse-MQA fwd/bwd TFLOP/s and % bf16 MFMA peak @ H=64 D=512 topk=2048"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
+KERNELS = ("fwd", "bwd_preprocess", "bwd_zero", "bwd_dq", "bwd_dkv", "bwd_postprocess")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="causal_h64_d512_k2048")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+class Step:
+    """Preallocated buffers and the library calls of one fwd+bwd step (no allocation inside)."""
+
+    def __init__(self, smqa, w, x):
+        self.lib = smqa.load_library()
+        self.w = w
+        dev = torch.device("cuda:0")
+        self.q = x["q"].to(dev)
+        self.kv = x["kv"].to(dev)
+        self.sink = x["attn_sink"].to(dev)
+        self.idx = x["topk_idxs"].to(dev)
+        self.do = x["do"].to(dev)
+        B, S, S_kv, H, D = w.B, w.S, w.S_kv, w.H, w.D
+        self.o = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B, S, H), dtype=torch.float32, device=dev)
+        self.delta = torch.empty((B, S, H), dtype=torch.float32, device=dev)
+        self.dq = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev)
+        self.acc = torch.empty((B, S_kv, D), dtype=torch.float32, device=dev)
+        self.dkv = torch.empty((B, S_kv, D), dtype=torch.bfloat16, device=dev)
+        self.stream = torch.cuda.current_stream()
+        self.events = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for k in KERNELS}
+        self.times = {k: 0.0 for k in KERNELS}
+        self.nan = float("nan")
+
+    def _check(self, name, st):
+        if st != 0:
+            raise RuntimeError(f"{name}: status {st} {self.lib.sparse_mqa_status_string(st).decode()}")
+
+    def run(self, timed: bool):
+        w, L, h = self.w, self.lib, self.stream.cuda_stream
+        B, S, S_kv, H, D, K = w.B, w.S, w.S_kv, w.H, w.D, w.topk
+        p = lambda t: t.data_ptr()  # noqa: E731
+        calls = {
+            "fwd": lambda: L.sparse_mqa_fwd(p(self.q), p(self.kv), p(self.sink), p(self.idx), p(self.o),
+                                            p(self.lse), B, S, S_kv, H, D, K, self.nan, h),
+            "bwd_preprocess": lambda: L.sparse_mqa_bwd_preprocess(p(self.o), p(self.do), p(self.delta), B, S, H, D, h),
+            "bwd_zero": lambda: (self.acc.zero_(), 0)[1],
+            "bwd_dq": lambda: L.sparse_mqa_bwd_dq(p(self.q), p(self.kv), p(self.do), p(self.idx), p(self.lse),
+                                                  p(self.delta), p(self.dq), B, S, S_kv, H, D, K, self.nan, h),
+            "bwd_dkv": lambda: L.sparse_mqa_bwd_dkv(p(self.q), p(self.kv), p(self.do), p(self.idx), p(self.lse),
+                                                    p(self.delta), p(self.acc), B, S, S_kv, H, D, K, self.nan, h),
+            "bwd_postprocess": lambda: L.sparse_mqa_bwd_postprocess(p(self.acc), p(self.dkv), B, S_kv, D, h),
+        }
+        for k in KERNELS:
+            if timed:
+                self.events[k][0].record(self.stream)
+            self._check(k, calls[k]())
+            if timed:
+                self.events[k][1].record(self.stream)
+
+    def collect(self):
+        for k in KERNELS:
+            self.times[k] += self.events[k][0].elapsed_time(self.events[k][1])
+
+
+def cpu_baseline(x, w, valid_per_token):
+    """The oracle as it stands, on a bounded sample of the same workload."""
+    import oracle
+
+    n_tok = min(256, w.B * w.S)
+    toks = list(range(w.B * w.S - n_tok, w.B * w.S))
+    rows = list(range(0, 16))
+    t0 = time.perf_counter()
+    o, lse = oracle.fwd(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], tokens=toks)
+    O = torch.zeros(w.B * w.S, w.H, w.D, dtype=torch.bfloat16)
+    Ls = torch.zeros(w.B * w.S, w.H)
+    O[toks] = o.to(torch.bfloat16)
+    Ls[toks] = lse
+    t1 = time.perf_counter()
+    oracle.dq(x["q"], x["kv"], O.view(w.B, w.S, w.H, w.D), x["do"], x["topk_idxs"], Ls.view(w.B, w.S, w.H),
+              tokens=toks)
+    t2 = time.perf_counter()
+    # dKV rows: every token referencing them needs O/LSE; the sample's LSE rows are filled only for
+    # the sampled tokens, which is enough to time the arithmetic (the values are not checked here)
+    oracle.dkv(x["q"], x["kv"], O.view(w.B, w.S, w.H, w.D), x["do"], x["topk_idxs"], Ls.view(w.B, w.S, w.H),
+               rows=rows)
+    t3 = time.perf_counter()
+    pairs = int(valid_per_token[toks].sum())
+    v = ((x["topk_idxs"] >= 0) & (x["topk_idxs"] < w.S_kv))
+    refs = 0
+    for r in rows:
+        b, j = divmod(r, w.S_kv)
+        refs += int(((x["topk_idxs"][b] == j) & v[b]).sum())
+    flops = 4 * w.H * w.D * pairs + 6 * w.H * w.D * pairs + 10 * w.H * w.D * refs
+    secs = t3 - t0
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": (f"fp32 oracle: forward + dQ for the last {n_tok} tokens ({pairs} valid pairs) and dKV for "
+                       f"kv rows 0..{len(rows) - 1} ({refs} references); {secs:.1f} s "
+                       f"(fwd {t1 - t0:.1f} s, dQ {t2 - t1:.1f} s, dKV {t3 - t2:.1f} s)")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); multi-GPU runs are not part of "
+              "this build", file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import top_sparse_mqa_amd as smqa
+    from top_sparse_mqa_amd import synthetic as syn
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w = syn.WORKLOADS[args.workload]
+    x = syn.workload_inputs(w)
+    valid = ((x["topk_idxs"] >= 0) & (x["topk_idxs"] < w.S_kv)).sum(-1).view(-1)
+    n_valid = int(valid.sum())
+    step = Step(smqa, w, x)
+    for _ in range(args.warmup):
+        step.run(timed=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step.run(timed=True)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    # per-kernel event times (each kernel bracketed on its own stream)
+    step.times = {k: 0.0 for k in KERNELS}
+    step.collect()
+    ms = {k: step.times[k] / args.steps for k in KERNELS}
+    ms_step = total_ms / args.steps
+
+    HD = w.H * w.D
+    fl_fwd = 4 * HD * n_valid
+    fl_bwd = 10 * HD * n_valid
+    fl_kernel = {"fwd": fl_fwd, "bwd_dq": 6 * HD * n_valid, "bwd_dkv": 4 * HD * n_valid}
+    ms_fwd = ms["fwd"]
+    ms_bwd = sum(ms[k] for k in KERNELS if k.startswith("bwd"))
+    tflops = (fl_fwd + fl_bwd) / (ms_step * 1e-3) / 1e12
+    dom = max(("fwd", "bwd_dq", "bwd_dkv"), key=lambda k: ms[k])
+    ach = fl_kernel[dom] / (ms[dom] * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": dict(w.describe(), valid_pairs=n_valid, step="forward + backward"),
+        "fwd_ms": round(ms_fwd, 4),
+        "bwd_ms": round(ms_bwd, 4),
+        "fwd_tflops": round(fl_fwd / (ms_fwd * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(fl_bwd / (ms_bwd * 1e-3) / 1e12, 2),
+        "fwd_frac_mfma_peak": round(fl_fwd / (ms_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "bwd_frac_mfma_peak": round(fl_bwd / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "step_frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "fwd_gather_GBps": round(n_valid * 2 * w.D / (ms_fwd * 1e-3) / 1e9, 1),
+        "kernel_ms": {k: round(v, 4) for k, v in ms.items()},
+        "wall_s_timed": round(wall, 3),
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(ach, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if dom == "bwd_dkv":
+        # the scatter-add payload (4 bytes per valid pair per d) against the measured fp32 atomic rate
+        out["roofline"]["atomic_payload_TBps"] = round(n_valid * w.D * 4 / (ms[dom] * 1e-3) / 1e12, 3)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, w, valid)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,120 @@
+/* Top-k sparse multi-query attention, forward and backward, for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libsparse_mqa.so. Every function takes plain device pointers, sizes and a HIP
+ * stream (passed as void*, a hipStream_t; NULL = the default stream), enqueues its kernels on
+ * that stream and returns an int status (SMQA_OK = 0). Nothing here allocates, frees or
+ * synchronises; the caller owns every buffer. All tensors are dense, contiguous, row-major,
+ * in exactly the layouts below; bf16 tensors are passed as raw 16-bit words.
+ *
+ * The operation is the one documented on two NeMo AutoModel DeepSeek-V4 kernel pages:
+ * "...kernels.tilelang_sparse_mla_fwd" (API entry sparse_mqa_fwd_interface) and
+ * "...kernels.tilelang_sparse_mla_bwd" (API entry sparse_mqa_bwd_interface and the
+ * preprocess / bwd / postprocess factories). For batch b, token s, head h, and slot t with
+ * i = topk_idxs[b,s,t]:
+ *   - slot t takes part iff 0 <= i < S_kv; any other value (negative, >= S_kv) is masked
+ *     and its kv row is never read (fwd page, topk_idxs note);
+ *   - score z_t = sm_scale * <q[b,s,h,:], kv[b,i,:]>; kv is both key and value (kv note);
+ *   - the softmax denominator is Z = sum_t exp(z_t) + exp(attn_sink[h]) (attn_sink note);
+ *   - O[b,s,h,:] = sum_t exp(z_t)/Z * kv[b,i,:] (bf16), LSE[b,s,h] = log2 Z (fp32; the
+ *     reference_rounding note says the kept LSE is base 2);
+ *   - sm_scale: a NaN value selects the default D^-0.5 (sm_scale note).
+ * A token with no valid slot gets O = 0; its LSE is attn_sink[h]*log2(e), or -inf if the sink
+ * is -inf. Duplicate indices within a token count once per slot.
+ * Backward (bwd page): given dO, the forward's bf16 O and fp32 LSE,
+ *   Delta = <O, dO>, P_t = 2^(z_t*log2 e - LSE), dS_t = P_t*(<dO, kv_i> - Delta),
+ *   dQ = sm_scale * sum_t dS_t kv_i (bf16), dKV[b,j,:] = sum over (s,t) with i = j of
+ *   sum_h (sm_scale*dS_t*q[b,s,h,:] + P_t*dO[b,s,h,:]), accumulated in fp32 (accum_dtype)
+ *   and returned as bf16, or as the fp32 accumulator itself (return_dkv_accum_dtype).
+ *
+ * Shapes (all int64): B batch, S query tokens, S_kv kv rows, H heads, D head dim, topk slots.
+ *   q, O, dO, dQ : [B, S, H, D] bf16       kv, dKV  : [B, S_kv, D] bf16 (dKV fp32 if asked)
+ *   attn_sink    : [H] fp32                topk_idxs: [B, S, topk] int32
+ *   LSE, Delta   : [B, S, H] fp32          dKV accumulator: [B, S_kv, D] fp32
+ * Supported (H, D): D = 512 with H in {16, 32, 64, 128}; D = 64 with H in {16, 32}.
+ * 1 <= topk <= 2^30, S_kv <= 2^31 - 1, B*S <= 2^28.
+ * Pointers to bf16 tensors (q, kv, O, dO, dQ, dKV), the fp32 dKV accumulator and the workspace
+ * must be 16-byte aligned; fp32 vectors (attn_sink, LSE, Delta) and topk_idxs 4-byte aligned.
+ * Outputs must not overlap inputs or each other (SMQA_ERR_ALIAS).
+ * Out-of-range indices are data, not errors. Results are undefined if q, kv or dO hold
+ * non-finite values. Calls on one stream are ordered; concurrent calls writing the same
+ * outputs race.
+ */
+#ifndef SPARSE_MQA_H
+#define SPARSE_MQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SMQA_OK = 0,
+  SMQA_ERR_NULL = 1,        /* a required pointer is NULL */
+  SMQA_ERR_SHAPE = 2,       /* a size is <= 0 or beyond a stated limit */
+  SMQA_ERR_UNSUPPORTED = 3, /* (H, D) has no compiled kernel */
+  SMQA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
+  SMQA_ERR_ALIAS = 5,       /* an output overlaps an input or another output */
+  SMQA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than sparse_mqa_bwd_workspace_bytes */
+  SMQA_ERR_HIP = 7,         /* a kernel launch failed (hipGetLastError) */
+  SMQA_ERR_ARG = 8          /* another invalid argument (e.g. a non-finite, non-NaN sm_scale) */
+};
+
+/* Forward (fwd page, sparse_mqa_fwd_interface). Reads q, kv, attn_sink, topk_idxs; writes
+ * o [B,S,H,D] bf16 and lse [B,S,H] fp32 (log2 units). sm_scale = NaN selects D^-0.5. */
+int sparse_mqa_fwd(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs,
+                   void* o, float* lse, int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D,
+                   int64_t topk, float sm_scale, void* stream);
+
+/* Bytes of device workspace sparse_mqa_bwd needs: Delta [B,S,H] fp32 plus, for the bf16 dKV
+ * output, the fp32 dKV accumulator [B,S_kv,D], each rounded up to 256 bytes. Returns 0 for
+ * invalid sizes. */
+size_t sparse_mqa_bwd_workspace_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D);
+
+/* Backward (bwd page, sparse_mqa_bwd_interface): preprocess (Delta), zero the accumulator,
+ * the main kernels (dQ; dKV scatter-add), then postprocess (fp32 -> bf16) unless dkv_fp32.
+ * dq [B,S,H,D] bf16. dkv [B,S_kv,D]: bf16 if dkv_fp32 == 0, else fp32 (and then it is the
+ * accumulator itself). The call overwrites dq and dkv; it never accumulates into them.
+ * attn_sink is accepted for the documented signature; the LSE already includes the sink, so
+ * dQ and dKV do not read it. */
+int sparse_mqa_bwd(const void* q, const void* kv, const float* attn_sink, const void* o,
+                   const void* d_o, const int32_t* topk_idxs, const float* lse, void* dq, void* dkv,
+                   int dkv_fp32, void* workspace, size_t workspace_bytes, int64_t B, int64_t S,
+                   int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale, void* stream);
+
+/* Stage: Delta[b,s,h] = sum_d O*dO in fp32 (bwd page, preprocess factory). */
+int sparse_mqa_bwd_preprocess(const void* o, const void* d_o, float* delta, int64_t B, int64_t S,
+                              int64_t H, int64_t D, void* stream);
+
+/* Stage: the main backward (bwd page, bwd factory). Writes dq (bf16) and adds every valid
+ * slot's dKV contribution into dkv_accum [B,S_kv,D] fp32 with atomic adds. dkv_accum must be
+ * zeroed by the caller first (it is not cleared here); rows no slot references are untouched. */
+int sparse_mqa_bwd_main(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs,
+                        const float* lse, const float* delta, void* dq, float* dkv_accum, int64_t B,
+                        int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale,
+                        void* stream);
+
+/* The two halves of sparse_mqa_bwd_main, exported so each kernel can be timed or tested on its
+ * own: sparse_mqa_bwd_dq writes dq only; sparse_mqa_bwd_dkv only adds into dkv_accum.
+ * Arguments, layouts and errors as for sparse_mqa_bwd_main. */
+int sparse_mqa_bwd_dq(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs,
+                      const float* lse, const float* delta, void* dq, int64_t B, int64_t S,
+                      int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale, void* stream);
+int sparse_mqa_bwd_dkv(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs,
+                       const float* lse, const float* delta, float* dkv_accum, int64_t B, int64_t S,
+                       int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale, void* stream);
+
+/* Stage: dkv[b,j,d] = bf16(dkv_accum[b,j,d]) with round-to-nearest-even (bwd page,
+ * postprocess factory). */
+int sparse_mqa_bwd_postprocess(const float* dkv_accum, void* dkv, int64_t B, int64_t S_kv,
+                               int64_t D, void* stream);
+
+/* Static string naming a status code. */
+const char* sparse_mqa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_MQA_H */

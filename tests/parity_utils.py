@@ -1,0 +1,83 @@
+"""Helpers for the GPU parity tests: tolerance checks against the oracle and sample choice."""
+from __future__ import annotations
+
+import math
+import sys
+from typing import Iterable, List
+
+import torch
+
+# Floating-point bar: |err| <= 2e-2 + 2e-2 |ref| for bf16 O, dQ and dKV; 1e-3 absolute for the
+# fp32 (base-2) LSE. A relative-L2 gate of 1e-2 is applied as well so that an error hidden by the
+# absolute term on small-magnitude outputs still fails.
+BF16_ATOL = 2e-2
+BF16_RTOL = 2e-2
+LSE_ATOL = 1e-3
+REL_L2_MAX = 1e-2
+
+
+def say(*a) -> None:
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def check_bf16(name: str, got: torch.Tensor, ref: torch.Tensor, rel_l2_max: float = REL_L2_MAX) -> float:
+    g = got.detach().double().cpu()
+    r = ref.detach().double().cpu()
+    assert g.shape == r.shape, (name, g.shape, r.shape)
+    assert not torch.isnan(g).any(), f"{name}: NaN in GPU output"
+    err = (g - r).abs()
+    bad = err > BF16_ATOL + BF16_RTOL * r.abs()
+    nbad = int(bad.sum())
+    rel = float((g - r).norm() / max(float(r.norm()), 1e-30))
+    say(f"  {name}: max|err| {float(err.max()):.3e}  rel-L2 {rel:.3e}  n={r.numel()}")
+    assert nbad == 0, f"{name}: {nbad} of {r.numel()} elements outside |err| <= {BF16_ATOL} + {BF16_RTOL}|ref|"
+    assert rel <= rel_l2_max, f"{name}: relative L2 error {rel:.3e} > {rel_l2_max}"
+    return rel
+
+
+def check_lse(name: str, got: torch.Tensor, ref: torch.Tensor) -> None:
+    g = got.detach().double().cpu()
+    r = ref.detach().double().cpu()
+    assert g.shape == r.shape
+    inf_r = torch.isinf(r)
+    assert torch.equal(torch.isinf(g), inf_r) and torch.equal(g[inf_r], r[inf_r]), f"{name}: infinite entries differ"
+    fin = ~inf_r
+    err = (g[fin] - r[fin]).abs()
+    m = float(err.max()) if err.numel() else 0.0
+    say(f"  {name}: max|err| {m:.3e}")
+    assert not torch.isnan(g).any()
+    assert m <= LSE_ATOL, f"{name}: max |err| {m} > {LSE_ATOL}"
+
+
+def sample_tokens(n_tokens: int, extra: int, seed: int, fixed: Iterable[int] = ()) -> List[int]:
+    g = torch.Generator().manual_seed(seed)
+    base = [t for t in fixed if 0 <= t < n_tokens]
+    rnd = torch.randperm(n_tokens, generator=g)[:extra].tolist()
+    return sorted(set(base + rnd))
+
+
+def bf16_round(t: torch.Tensor) -> torch.Tensor:
+    return t.to(torch.bfloat16)
+
+
+def valid_mask(idx: torch.Tensor, s_kv: int) -> torch.Tensor:
+    return (idx >= 0) & (idx < s_kv)
+
+
+def referenced_rows(idx: torch.Tensor, s_kv: int) -> torch.Tensor:
+    """Boolean [B, S_kv]: rows that at least one valid slot references."""
+    B = idx.shape[0]
+    v = valid_mask(idx, s_kv)
+    hit = torch.zeros(B, s_kv, dtype=torch.int64)
+    hit.scatter_add_(1, torch.where(v, idx, torch.zeros_like(idx)).long().view(B, -1), v.long().view(B, -1))
+    return hit > 0
+
+
+def conservation_rhs(q, o, do, lse, sink, sm_scale):
+    """sum_{s,h} (sm_scale * Delta * P_sink * q + (1 - P_sink) * dO) per batch, in float64."""
+    qd, od, dod = q.double(), o.double(), do.double()
+    delta = (od * dod).sum(-1)
+    p_sink = torch.exp2(sink.double() / math.log(2.0) - lse.double())
+    p_sink = torch.where(torch.isinf(lse), torch.zeros_like(p_sink), p_sink)
+    return (sm_scale * (delta * p_sink)[..., None] * qd + (1 - p_sink)[..., None] * dod).sum((1, 2))

@@ -1,0 +1,113 @@
+"""Host-side checks of libsparse_mqa that need no GPU: the library loads, exports every entry
+point include/sparse_mqa.h declares, and rejects invalid arguments with the documented status
+before any HIP call (every call below is invalid in at least one checked way)."""
+import ctypes
+import math
+import re
+from pathlib import Path
+
+import pytest
+
+import top_sparse_mqa_amd as smqa
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "sparse_mqa.h"
+OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, WORKSPACE, HIP, ARG = range(9)
+
+# fake, never dereferenced device addresses (validation fails before any use)
+A = 0x10000000
+Bp = 0x20000000
+C = 0x30000000
+Dp = 0x40000000
+E = 0x50000000
+F_ = 0x60000000
+G = 0x70000000
+NAN = float("nan")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not smqa.LIB_PATH.exists():
+        pytest.fail("libsparse_mqa.so is not built (python -m top_sparse_mqa_amd.build)")
+    return smqa.load_library()
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(sparse_mqa_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(smqa.EXPORTED) == names
+
+
+def test_status_strings(lib):
+    for st in range(9):
+        assert lib.sparse_mqa_status_string(st)
+    assert lib.sparse_mqa_status_string(99) == b"unknown status"
+
+
+def fwd(lib, q=A, kv=Bp, sink=C, idx=Dp, o=E, lse=F_, B=1, S=8, S_kv=16, H=64, D=512, topk=4, scale=NAN):
+    return lib.sparse_mqa_fwd(q, kv, sink, idx, o, lse, B, S, S_kv, H, D, topk, scale, None)
+
+
+def test_fwd_validation(lib):
+    assert fwd(lib, q=None) == NULL
+    assert fwd(lib, lse=None) == NULL
+    assert fwd(lib, B=0) == SHAPE
+    assert fwd(lib, topk=-1) == SHAPE
+    assert fwd(lib, S_kv=2 ** 31) == SHAPE
+    assert fwd(lib, H=48) == UNSUP
+    assert fwd(lib, D=128) == UNSUP
+    assert fwd(lib, H=64, D=64) == UNSUP
+    assert fwd(lib, q=A + 8) == ALIGN
+    assert fwd(lib, idx=Dp + 2) == ALIGN
+    assert fwd(lib, scale=math.inf) == ARG
+    # o overlaps q; lse overlaps kv; o overlaps lse
+    assert fwd(lib, o=A + 1024) == ALIAS
+    assert fwd(lib, lse=Bp + 64) == ALIAS
+    assert fwd(lib, lse=E + 4096) == ALIAS
+
+
+def test_workspace_bytes(lib):
+    n = lib.sparse_mqa_bwd_workspace_bytes(1, 4096, 4096, 64, 512)
+    assert n == 4096 * 64 * 4 + 4096 * 512 * 4
+    assert lib.sparse_mqa_bwd_workspace_bytes(1, 3, 5, 16, 64) == 256 + 5 * 64 * 4 + (256 - (5 * 64 * 4) % 256) % 256
+    assert lib.sparse_mqa_bwd_workspace_bytes(0, 1, 1, 1, 1) == 0
+
+
+def bwd(lib, dkv_fp32=0, ws=G, wsb=1 << 30, dq=0x71000000, dkv=0x72000000, o=E, B=1, S=8, S_kv=16, H=64, D=512,
+        topk=4, scale=NAN):
+    return lib.sparse_mqa_bwd(A, Bp, C, o, 0x11000000, Dp, F_, dq, dkv, dkv_fp32, ws, wsb, B, S, S_kv, H, D, topk,
+                              scale, None)
+
+
+def test_bwd_validation(lib):
+    assert bwd(lib, dq=None) == NULL
+    assert bwd(lib, S=0) == SHAPE
+    assert bwd(lib, H=8) == UNSUP
+    assert bwd(lib, ws=None) == WORKSPACE
+    assert bwd(lib, wsb=100) == WORKSPACE
+    assert bwd(lib, ws=G + 4) == ALIGN
+    assert bwd(lib, dq=A) == ALIAS
+    assert bwd(lib, dkv=0x71000000 + 64) == ALIAS
+    assert bwd(lib, ws=0x72000000) == ALIAS
+    assert bwd(lib, scale=-math.inf) == ARG
+
+
+def test_stage_validation(lib):
+    assert lib.sparse_mqa_bwd_preprocess(None, A, Bp, 1, 8, 64, 512, None) == NULL
+    assert lib.sparse_mqa_bwd_preprocess(A, Bp, C, 1, 8, 64, 100, None) == UNSUP
+    assert lib.sparse_mqa_bwd_preprocess(A, Bp, A + 64, 1, 8, 64, 512, None) == ALIAS
+    assert lib.sparse_mqa_bwd_main(A, Bp, C, Dp, E, F_, G, None, 1, 8, 16, 64, 512, 4, NAN, None) == NULL
+    assert lib.sparse_mqa_bwd_main(A, Bp, C, Dp, E, F_, G, A, 1, 8, 16, 64, 512, 4, NAN, None) == ALIAS
+    assert lib.sparse_mqa_bwd_dq(A, Bp, C, Dp, E, F_, None, 1, 8, 16, 64, 512, 4, NAN, None) == NULL
+    assert lib.sparse_mqa_bwd_dq(A, Bp, C, Dp, E, F_, G + 2, 1, 8, 16, 64, 512, 4, NAN, None) == ALIGN
+    assert lib.sparse_mqa_bwd_dkv(A, Bp, C, Dp, E, F_, None, 1, 8, 16, 64, 512, 4, NAN, None) == NULL
+    assert lib.sparse_mqa_bwd_dkv(A, Bp, C, Dp, E, F_, G, 1, 8, 16, 64, 512, 0, NAN, None) == SHAPE
+    assert lib.sparse_mqa_bwd_postprocess(None, A, 1, 16, 512, None) == NULL
+    assert lib.sparse_mqa_bwd_postprocess(A, Bp, 1, 16, 12, None) == SHAPE
+    assert lib.sparse_mqa_bwd_postprocess(A, A + 16, 1, 16, 512, None) == ALIAS

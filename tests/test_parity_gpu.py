@@ -1,0 +1,279 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Small cases are compared element by element over every output. The full-size workloads are
+compared on sampled tokens (forward, dQ) and sampled kv rows (dKV) that the oracle computes one
+by one, plus the dKV conservation identity over every row. Masking and index handling are
+checked bit-exactly (zero outputs, untouched rows, NaN-poisoned unreferenced kv rows).
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import top_sparse_mqa_amd as smqa
+from top_sparse_mqa_amd import synthetic as syn
+from parity_utils import (check_bf16, check_lse, conservation_rhs, referenced_rows, sample_tokens, say,
+                          valid_mask)
+
+pytestmark = pytest.mark.gpu
+
+I32MIN, I32MAX = -(2 ** 31), 2 ** 31 - 1
+
+
+def gpu(x):
+    return {k: v.cuda() for k, v in x.items()}
+
+
+def fwd_gpu(xg, scale=None):
+    o, lse = smqa.sparse_mqa_fwd_interface(xg["q"], xg["kv"], xg["attn_sink"], xg["topk_idxs"], sm_scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def bwd_gpu(xg, o, lse, scale=None, fp32=False):
+    dq, dkv = smqa.sparse_mqa_bwd_interface(xg["q"], xg["kv"], xg["attn_sink"], o, xg["do"], xg["topk_idxs"], lse,
+                                            sm_scale=scale, return_dkv_accum_dtype=fp32)
+    torch.cuda.synchronize()
+    return dq, dkv
+
+
+def full_parity(x, scale=None, tag=""):
+    """Forward and backward over every output element against the fp32 oracle."""
+    B, S, H, D = x["q"].shape
+    S_kv = x["kv"].shape[1]
+    xg = gpu(x)
+    o, lse = fwd_gpu(xg, scale)
+    o_ref, lse_ref = oracle.fwd(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], sm_scale=scale)
+    check_bf16(f"{tag} O", o.view(-1, H, D), o_ref)
+    check_lse(f"{tag} LSE", lse.view(-1, H), lse_ref)
+    # backward on the oracle's forward outputs (O rounded to bf16, as the interface takes it)
+    ob = o_ref.view(B, S, H, D).to(torch.bfloat16)
+    lb = lse_ref.view(B, S, H)
+    dq, dkv = bwd_gpu(xg, ob.cuda(), lb.cuda(), scale)
+    dq_ref, delta_ref = oracle.dq(x["q"], x["kv"], ob, x["do"], x["topk_idxs"], lb, sm_scale=scale)
+    dkv_ref = oracle.dkv(x["q"], x["kv"], ob, x["do"], x["topk_idxs"], lb, sm_scale=scale)
+    check_bf16(f"{tag} dQ", dq.view(-1, H, D), dq_ref)
+    check_bf16(f"{tag} dKV", dkv.view(-1, D), dkv_ref)
+    ref_rows = referenced_rows(x["topk_idxs"], S_kv).view(-1)
+    assert torch.count_nonzero(dkv.view(-1, D).cpu()[~ref_rows]) == 0, "unreferenced dKV rows must be exactly 0"
+    # fp32 accumulator output
+    dq2, dkv32 = bwd_gpu(xg, ob.cuda(), lb.cuda(), scale, fp32=True)
+    assert dkv32.dtype == torch.float32
+    check_bf16(f"{tag} dKV fp32", dkv32.view(-1, D), dkv_ref)
+    assert torch.equal(dq2, dq), "dQ must be deterministic"
+    # preprocess stage alone
+    delta = smqa.bwd_preprocess(ob.cuda(), xg["do"])
+    torch.cuda.synchronize()
+    torch.testing.assert_close(delta.view(-1, H).cpu().double(), delta_ref.double(), rtol=1e-4, atol=1e-4)
+    return o, lse
+
+
+def test_tiny_full(gpu_lib):
+    w = syn.WORKLOADS["tiny_h16_d64"]
+    say("case", w.describe())
+    x = syn.workload_inputs(w)
+    o, lse = full_parity(x, tag=w.name)
+    # forward is deterministic bit for bit
+    o2, lse2 = fwd_gpu(gpu(x))
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+def test_mid_full(gpu_lib):
+    w = syn.WORKLOADS["mid_h64_d512_k300"]
+    say("case", w.describe())
+    full_parity(syn.workload_inputs(w), tag=w.name)
+
+
+EDGE = [
+    # name, B, S, S_kv, H, D, topk
+    ("h32_d512_k65", 2, 9, 70, 32, 512, 65),
+    ("h128_d512_k130", 1, 6, 300, 128, 512, 130),
+    ("h16_d512_k1", 1, 7, 40, 16, 512, 1),
+    ("h32_d64_k200_dups", 1, 11, 100, 32, 64, 200),
+    ("h64_d512_k33", 1, 5, 33, 64, 512, 33),
+]
+
+
+def edge_inputs(name, B, S, S_kv, H, D, topk, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = {
+        "q": torch.randn(B, S, H, D, generator=g).to(torch.bfloat16),
+        "kv": torch.randn(B, S_kv, D, generator=g).to(torch.bfloat16),
+        "attn_sink": torch.randn(H, generator=g),
+        "do": torch.randn(B, S, H, D, generator=g).to(torch.bfloat16),
+    }
+    idx = torch.randint(-2, S_kv + 2, (B, S, topk), generator=g)
+    pick = torch.rand(B, S, topk, generator=g)
+    idx = torch.where(pick < 0.04, torch.full_like(idx, I32MIN), idx)
+    idx = torch.where((pick > 0.96), torch.full_like(idx, I32MAX), idx)
+    idx[0, 0] = -1  # a fully masked token
+    x["topk_idxs"] = idx.to(torch.int32)
+    x["attn_sink"][0] = -math.inf  # one head without a sink
+    return x
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_edge_shapes_full(gpu_lib, case):
+    name, B, S, S_kv, H, D, topk = case
+    say("case", name, dict(B=B, S=S, S_kv=S_kv, H=H, D=D, topk=topk))
+    x = edge_inputs(*case, seed=zlib.crc32(name.encode()) % 1000)
+    # NaN-poison every kv row that no valid slot references: such rows must never be read
+    ref_rows = referenced_rows(x["topk_idxs"], S_kv)
+    kv = x["kv"].clone()
+    kv[~ref_rows] = float("nan")
+    x["kv"] = kv
+    o, lse = full_parity(x, tag=name)
+    # the fully masked token: O exactly +0, LSE = sink*log2(e) (or -inf for the sinkless head)
+    o0 = o[0, 0].cpu()
+    assert torch.count_nonzero(o0) == 0 and not torch.signbit(o0.float()).any()
+    l0 = lse[0, 0].cpu()
+    assert l0[0] == -math.inf
+    torch.testing.assert_close(l0[1:].double(), x["attn_sink"][1:].double() / math.log(2), rtol=0, atol=1e-5)
+
+
+def test_explicit_scale_and_int64_indices(gpu_lib):
+    w = syn.WORKLOADS["tiny_h16_d64"]
+    x = syn.workload_inputs(w)
+    xg = gpu(x)
+    o, lse = fwd_gpu(xg, scale=0.2)
+    o_ref, lse_ref = oracle.fwd(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], sm_scale=0.2)
+    check_bf16("O scale=0.2", o.view(-1, w.H, w.D), o_ref)
+    check_lse("LSE scale=0.2", lse.view(-1, w.H), lse_ref)
+    # int64 indices, including values that int32 narrowing alone would wrap into range
+    idx64 = x["topk_idxs"].long()
+    idx64[:, :, -1] = 2 ** 32 + 3
+    xg["topk_idxs"] = idx64.cuda()
+    o64, _ = fwd_gpu(xg)
+    x32 = dict(x)
+    x32["topk_idxs"] = torch.where(idx64 >= w.S_kv, -1, idx64).to(torch.int32)
+    o32, _ = fwd_gpu(gpu(x32))
+    assert torch.equal(o64, o32)
+
+
+def test_non_default_stream(gpu_lib):
+    w = syn.WORKLOADS["mid_h64_d512_k300"]
+    x = syn.workload_inputs(w)
+    xg = gpu(x)
+    o_ref, lse_ref = fwd_gpu(xg)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, lse = smqa.sparse_mqa_fwd_interface(xg["q"], xg["kv"], xg["attn_sink"], xg["topk_idxs"])
+    s.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
+
+
+# ------------------------------------------------------------------------------------------------
+# full-size workloads
+HEADLINE = syn.WORKLOADS["causal_h64_d512_k2048"]
+
+
+@pytest.fixture(scope="module")
+def headline():
+    say("generating", HEADLINE.describe())
+    return syn.workload_inputs(HEADLINE)
+
+
+@pytest.mark.timeout(600)
+def test_headline_forward_sampled(gpu_lib, headline):
+    w, x = HEADLINE, headline
+    say("case", w.name, "forward")
+    o, lse = fwd_gpu(gpu(x))
+    toks = sample_tokens(w.B * w.S, 24, seed=7, fixed=[0, 1, 2, 3, 63, 64, 1023, 2046, 2047, 2048, 2049, 4094, 4095])
+    o_ref, lse_ref = oracle.fwd(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], tokens=toks)
+    check_bf16("O", o.view(-1, w.H, w.D)[toks], o_ref)
+    check_lse("LSE", lse.view(-1, w.H)[toks], lse_ref)
+    o2, lse2 = fwd_gpu(gpu(x))
+    assert torch.equal(o, o2) and torch.equal(lse, lse2), "forward must be deterministic"
+
+
+@pytest.mark.timeout(900)
+def test_headline_backward_sampled(gpu_lib, headline):
+    """Backward at the headline shapes on the oracle's forward outputs (O as bf16, LSE fp32)."""
+    w, x = HEADLINE, headline
+    say("case", w.name, "backward: oracle forward over all tokens")
+    o_ref, lse_ref = oracle.fwd(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"])
+    ob = o_ref.view(w.B, w.S, w.H, w.D).to(torch.bfloat16)
+    lb = lse_ref.view(w.B, w.S, w.H)
+    xg = gpu(x)
+    dq, dkv32 = bwd_gpu(xg, ob.cuda(), lb.cuda(), fp32=True)
+    toks = sample_tokens(w.B * w.S, 16, seed=8, fixed=[0, 1, 5, 2047, 2048, 4095])
+    dq_ref, _ = oracle.dq(x["q"], x["kv"], ob, x["do"], x["topk_idxs"], lb, tokens=toks)
+    check_bf16("dQ", dq.view(-1, w.H, w.D)[toks], dq_ref)
+    rows = sample_tokens(w.B * w.S_kv, 10, seed=9, fixed=[0, 1, 2047, 2048, 4094, 4095])
+    dkv_ref = oracle.dkv(x["q"], x["kv"], ob, x["do"], x["topk_idxs"], lb, rows=rows)
+    check_bf16("dKV fp32", dkv32.view(-1, w.D)[rows], dkv_ref)
+    # conservation over every row (holds up to the bf16 rounding of O)
+    rhs = conservation_rhs(x["q"], ob, x["do"], lb, x["attn_sink"], 1.0 / math.sqrt(w.D))
+    lhs = dkv32.double().sum(1).cpu()
+    rel = float((lhs - rhs).norm() / rhs.norm())
+    say(f"  conservation rel-L2 {rel:.3e}")
+    assert rel < 1e-2
+    # bf16 output path equals the round-to-nearest-even of an fp32 accumulation
+    _, dkv16 = bwd_gpu(xg, ob.cuda(), lb.cuda())
+    check_bf16("dKV bf16", dkv16.view(-1, w.D)[rows], dkv_ref)
+
+
+def _rows_refs(idx: torch.Tensor, S: int, S_kv: int, flat_rows):
+    """For each flat kv row b*S_kv + j, the flat tokens b*S + s whose slots reference it."""
+    v = valid_mask(idx, S_kv).numpy()
+    idn = idx.numpy()
+    out = []
+    for r in flat_rows:
+        b, j = divmod(r, S_kv)
+        s = np.nonzero(((idn[b] == j) & v[b]).any(-1))[0]
+        out.append((b * S + s).tolist())
+    return out
+
+
+def end_to_end_sampled(w, x, toks, rows):
+    """GPU forward -> GPU backward against oracle forward -> oracle backward, on sampled tokens
+    and kv rows. The oracle computes its own forward for every token it needs."""
+    xg = gpu(x)
+    o, lse = fwd_gpu(xg)
+    o_ref, lse_ref = oracle.fwd(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], tokens=toks)
+    check_bf16("O", o.view(-1, w.H, w.D)[toks], o_ref)
+    check_lse("LSE", lse.view(-1, w.H)[toks], lse_ref)
+    dq, dkv32 = bwd_gpu(xg, o, lse, fp32=True)
+    del xg
+    # oracle inputs: its own forward for the tokens each check needs (zeros elsewhere, never read)
+    refs = _rows_refs(x["topk_idxs"], w.S, w.S_kv, rows)
+    need = sorted(set(toks) | {t for r in refs for t in r})
+    say(f"  oracle forward for {len(need)} tokens")
+    on, ln = oracle.fwd(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], tokens=need)
+    O = torch.zeros(w.B * w.S, w.H, w.D, dtype=torch.bfloat16)
+    L = torch.zeros(w.B * w.S, w.H, dtype=torch.float32)
+    O[need] = on.to(torch.bfloat16)
+    L[need] = ln
+    O, L = O.view(w.B, w.S, w.H, w.D), L.view(w.B, w.S, w.H)
+    dq_ref, _ = oracle.dq(x["q"], x["kv"], O, x["do"], x["topk_idxs"], L, tokens=toks)
+    check_bf16("dQ", dq.view(-1, w.H, w.D)[toks], dq_ref)
+    dkv_ref = oracle.dkv(x["q"], x["kv"], O, x["do"], x["topk_idxs"], L, rows=rows)
+    check_bf16("dKV fp32", dkv32.view(-1, w.D)[rows], dkv_ref)
+    return o, lse, dkv32
+
+
+@pytest.mark.timeout(900)
+def test_long_context_h128_sampled(gpu_lib):
+    w = syn.WORKLOADS["long_h128_s16k"]
+    say("case", w.describe())
+    x = syn.workload_inputs(w)
+    toks = sample_tokens(w.S, 12, seed=10, fixed=[0, 1, 2047, 2048, 2049, 16383])
+    # tail rows are referenced by few tokens (the recent window only), so the oracle can
+    # afford them; row 0 and a middle row exercise the long reference lists
+    rows = [w.S_kv - 1, w.S_kv - 2, w.S_kv - 17, w.S_kv - 40]
+    end_to_end_sampled(w, x, toks, rows)
+
+
+@pytest.mark.timeout(900)
+def test_gather_b4_masked_sampled(gpu_lib):
+    w = syn.WORKLOADS["gather_b4_skv64k"]
+    say("case", w.describe())
+    x = syn.workload_inputs(w)
+    toks = sample_tokens(w.B * w.S, 16, seed=11, fixed=[0, 2047, 2048, 8191])
+    rows = sample_tokens(w.B * w.S_kv, 10, seed=12, fixed=[0, 65535, 65536, 4 * 65536 - 1])
+    o, lse, dkv32 = end_to_end_sampled(w, x, toks, rows)
+    ref_rows = referenced_rows(x["topk_idxs"], w.S_kv).view(-1)
+    assert torch.count_nonzero(dkv32.view(-1, w.D).cpu()[~ref_rows]) == 0

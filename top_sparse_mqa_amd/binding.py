@@ -1,0 +1,258 @@
+"""Python binding of libsparse_mqa (ctypes). Argument marshalling only: every step of the
+computation runs in the HIP kernels behind the C ABI (include/sparse_mqa.h). PyTorch supplies
+device memory and the current stream.
+
+The interface functions mirror the NeMo AutoModel DeepSeek-V4 pages
+"...kernels.tilelang_sparse_mla_fwd" (sparse_mqa_fwd_interface) and
+"...kernels.tilelang_sparse_mla_bwd" (sparse_mqa_bwd_interface).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from pathlib import Path
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = Path(__file__).resolve().parent / "libsparse_mqa.so"
+
+_c_void_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+_SIGS = {
+    "sparse_mqa_fwd": [_c_void_p] * 6 + [_i64] * 6 + [ctypes.c_float, _c_void_p],
+    "sparse_mqa_bwd_workspace_bytes": [_i64] * 5,
+    "sparse_mqa_bwd": [_c_void_p] * 9 + [ctypes.c_int, _c_void_p, ctypes.c_size_t] + [_i64] * 6
+    + [ctypes.c_float, _c_void_p],
+    "sparse_mqa_bwd_preprocess": [_c_void_p] * 3 + [_i64] * 4 + [_c_void_p],
+    "sparse_mqa_bwd_main": [_c_void_p] * 8 + [_i64] * 6 + [ctypes.c_float, _c_void_p],
+    "sparse_mqa_bwd_dq": [_c_void_p] * 7 + [_i64] * 6 + [ctypes.c_float, _c_void_p],
+    "sparse_mqa_bwd_dkv": [_c_void_p] * 7 + [_i64] * 6 + [ctypes.c_float, _c_void_p],
+    "sparse_mqa_bwd_postprocess": [_c_void_p] * 2 + [_i64] * 3 + [_c_void_p],
+    "sparse_mqa_status_string": [ctypes.c_int],
+}
+EXPORTED = tuple(_SIGS)
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class SparseMQAError(RuntimeError):
+    """A non-zero status returned by libsparse_mqa."""
+
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed with status {status}: {message}")
+        self.status = status
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the in-tree libsparse_mqa.so. There is no fallback: a missing library is an error."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m top_sparse_mqa_amd.build` "
+                "(the HIP library is required; there is no CPU fallback)")
+        lib = ctypes.CDLL(str(LIB_PATH))
+        for name, args in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        lib.sparse_mqa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.sparse_mqa_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        msg = load_library().sparse_mqa_status_string(status).decode()
+        raise SparseMQAError(fn, status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _scale_arg(sm_scale: Optional[float]) -> float:
+    return float("nan") if sm_scale is None else float(sm_scale)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _indices_int32(topk_idxs: torch.Tensor, s_kv: int) -> torch.Tensor:
+    """int32 indices for the ABI. int64 input is narrowed after every value outside
+    [0, S_kv) is replaced by -1, so narrowing cannot turn a masked index into a valid one."""
+    if topk_idxs.device.type != "cuda":
+        raise ValueError("topk_idxs must be a GPU tensor")
+    if topk_idxs.dtype == torch.int32:
+        if not topk_idxs.is_contiguous():
+            raise ValueError("topk_idxs must be contiguous")
+        return topk_idxs
+    if topk_idxs.dtype != torch.int64:
+        raise TypeError(f"topk_idxs must be int32 or int64, got {topk_idxs.dtype}")
+    bad = (topk_idxs < 0) | (topk_idxs >= s_kv)
+    return torch.where(bad, torch.full_like(topk_idxs, -1), topk_idxs).to(torch.int32).contiguous()
+
+
+def sparse_mqa_fwd_interface(q: torch.Tensor, kv: torch.Tensor, attn_sink: torch.Tensor,
+                             topk_idxs: torch.Tensor, sm_scale: Optional[float] = None,
+                             block_I: int = 64, num_stages: int = 2, threads: int = 256,
+                             reference_rounding: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Forward: returns (O [B,S,H,D] bf16, LSE [B,S,H] fp32 in log2 units).
+
+    block_I, num_stages and threads are tuning knobs of the pages' kernel generator; they are
+    accepted and ignored (the gfx950 kernels pick their own tiling)."""
+    del block_I, num_stages, threads
+    if reference_rounding:
+        raise NotImplementedError("reference_rounding=True is not implemented")
+    _need(q, "q", torch.bfloat16, 4)
+    _need(kv, "kv", torch.bfloat16, 3)
+    _need(attn_sink, "attn_sink", torch.float32, 1)
+    B, S, H, D = q.shape
+    if kv.shape[0] != B or kv.shape[2] != D:
+        raise ValueError(f"kv shape {tuple(kv.shape)} does not match q {tuple(q.shape)}")
+    S_kv = kv.shape[1]
+    if attn_sink.shape[0] != H:
+        raise ValueError("attn_sink must have H entries")
+    if topk_idxs.dim() != 3 or topk_idxs.shape[0] != B or topk_idxs.shape[1] != S:
+        raise ValueError(f"topk_idxs must be [B,S,topk], got {tuple(topk_idxs.shape)}")
+    idx = _indices_int32(topk_idxs, S_kv)
+    topk = idx.shape[2]
+    o = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, S, H), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    _check("sparse_mqa_fwd", lib.sparse_mqa_fwd(
+        _ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(idx), _ptr(o), _ptr(lse),
+        B, S, S_kv, H, D, topk, _scale_arg(sm_scale), _stream()))
+    return o, lse
+
+
+def sparse_mqa_bwd_interface(q: torch.Tensor, kv: torch.Tensor, attn_sink: torch.Tensor, o: torch.Tensor,
+                             do: torch.Tensor, topk_idxs: torch.Tensor, lse: torch.Tensor,
+                             sm_scale: Optional[float] = None,
+                             return_dkv_accum_dtype: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Backward: returns (dQ [B,S,H,D] bf16, dKV [B,S_kv,D] bf16, or fp32 when
+    return_dkv_accum_dtype)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(kv, "kv", torch.bfloat16, 3)
+    _need(attn_sink, "attn_sink", torch.float32, 1)
+    _need(o, "o", torch.bfloat16, 4)
+    _need(do, "do", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    B, S, H, D = q.shape
+    S_kv = kv.shape[1]
+    if o.shape != q.shape or do.shape != q.shape:
+        raise ValueError("o and do must have the shape of q")
+    if tuple(lse.shape) != (B, S, H):
+        raise ValueError("lse must be [B,S,H]")
+    if topk_idxs.dim() != 3 or topk_idxs.shape[0] != B or topk_idxs.shape[1] != S:
+        raise ValueError(f"topk_idxs must be [B,S,topk], got {tuple(topk_idxs.shape)}")
+    idx = _indices_int32(topk_idxs, S_kv)
+    topk = idx.shape[2]
+    lib = load_library()
+    dq = torch.empty_like(q)
+    dkv = torch.empty((B, S_kv, D), dtype=torch.float32 if return_dkv_accum_dtype else torch.bfloat16,
+                      device=q.device)
+    ws_bytes = lib.sparse_mqa_bwd_workspace_bytes(B, S, S_kv, H, D)
+    if ws_bytes == 0:
+        raise ValueError("invalid sizes for the backward workspace")
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _check("sparse_mqa_bwd", lib.sparse_mqa_bwd(
+        _ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(o), _ptr(do), _ptr(idx), _ptr(lse), _ptr(dq), _ptr(dkv),
+        1 if return_dkv_accum_dtype else 0, _ptr(ws), ws_bytes, B, S, S_kv, H, D, topk,
+        _scale_arg(sm_scale), _stream()))
+    return dq, dkv
+
+
+def bwd_preprocess(o: torch.Tensor, do: torch.Tensor) -> torch.Tensor:
+    """Delta[b,s,h] = sum_d O*dO (fp32)."""
+    _need(o, "o", torch.bfloat16, 4)
+    _need(do, "do", torch.bfloat16, 4)
+    B, S, H, D = o.shape
+    delta = torch.empty((B, S, H), dtype=torch.float32, device=o.device)
+    _check("sparse_mqa_bwd_preprocess", load_library().sparse_mqa_bwd_preprocess(
+        _ptr(o), _ptr(do), _ptr(delta), B, S, H, D, _stream()))
+    return delta
+
+
+def bwd_main(q: torch.Tensor, kv: torch.Tensor, do: torch.Tensor, topk_idxs: torch.Tensor, lse: torch.Tensor,
+             delta: torch.Tensor, dkv_accum: torch.Tensor, sm_scale: Optional[float] = None) -> torch.Tensor:
+    """Main backward stage: returns dQ and adds the dKV contributions into dkv_accum (fp32,
+    which the caller zeroes beforehand)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(kv, "kv", torch.bfloat16, 3)
+    _need(do, "do", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    _need(delta, "delta", torch.float32, 3)
+    _need(dkv_accum, "dkv_accum", torch.float32, 3)
+    B, S, H, D = q.shape
+    S_kv = kv.shape[1]
+    idx = _indices_int32(topk_idxs, S_kv)
+    dq = torch.empty_like(q)
+    _check("sparse_mqa_bwd_main", load_library().sparse_mqa_bwd_main(
+        _ptr(q), _ptr(kv), _ptr(do), _ptr(idx), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dkv_accum),
+        B, S, S_kv, H, D, idx.shape[2], _scale_arg(sm_scale), _stream()))
+    return dq
+
+
+def _main_stage_args(q, kv, do, topk_idxs, lse, delta):
+    _need(q, "q", torch.bfloat16, 4)
+    _need(kv, "kv", torch.bfloat16, 3)
+    _need(do, "do", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    _need(delta, "delta", torch.float32, 3)
+    return _indices_int32(topk_idxs, kv.shape[1])
+
+
+def bwd_dq(q: torch.Tensor, kv: torch.Tensor, do: torch.Tensor, topk_idxs: torch.Tensor, lse: torch.Tensor,
+           delta: torch.Tensor, sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dQ kernel of the main backward stage alone."""
+    idx = _main_stage_args(q, kv, do, topk_idxs, lse, delta)
+    B, S, H, D = q.shape
+    dq = torch.empty_like(q) if out is None else out
+    _check("sparse_mqa_bwd_dq", load_library().sparse_mqa_bwd_dq(
+        _ptr(q), _ptr(kv), _ptr(do), _ptr(idx), _ptr(lse), _ptr(delta), _ptr(dq),
+        B, S, kv.shape[1], H, D, idx.shape[2], _scale_arg(sm_scale), _stream()))
+    return dq
+
+
+def bwd_dkv(q: torch.Tensor, kv: torch.Tensor, do: torch.Tensor, topk_idxs: torch.Tensor, lse: torch.Tensor,
+            delta: torch.Tensor, dkv_accum: torch.Tensor, sm_scale: Optional[float] = None) -> torch.Tensor:
+    """dKV scatter kernel of the main backward stage alone: adds into dkv_accum (fp32)."""
+    idx = _main_stage_args(q, kv, do, topk_idxs, lse, delta)
+    _need(dkv_accum, "dkv_accum", torch.float32, 3)
+    B, S, H, D = q.shape
+    _check("sparse_mqa_bwd_dkv", load_library().sparse_mqa_bwd_dkv(
+        _ptr(q), _ptr(kv), _ptr(do), _ptr(idx), _ptr(lse), _ptr(delta), _ptr(dkv_accum),
+        B, S, kv.shape[1], H, D, idx.shape[2], _scale_arg(sm_scale), _stream()))
+    return dkv_accum
+
+
+def bwd_postprocess(dkv_accum: torch.Tensor) -> torch.Tensor:
+    """bf16 (round to nearest even) copy of the fp32 dKV accumulator."""
+    _need(dkv_accum, "dkv_accum", torch.float32, 3)
+    B, S_kv, D = dkv_accum.shape
+    out = torch.empty((B, S_kv, D), dtype=torch.bfloat16, device=dkv_accum.device)
+    _check("sparse_mqa_bwd_postprocess", load_library().sparse_mqa_bwd_postprocess(
+        _ptr(dkv_accum), _ptr(out), B, S_kv, D, _stream()))
+    return out
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)

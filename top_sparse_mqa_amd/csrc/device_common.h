@@ -1,0 +1,72 @@
+// Device-side helpers shared by the gfx950 kernels of libsparse_mqa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define SMQA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// v_mfma_f32_32x32x16_bf16. Operand lane layout: lane l holds row/col (l & 31) and eight
+// k-values of k-group (l >> 5); C lane l holds column (l & 31), rows 8*(r/4) + 4*(l>>5) + r%4.
+// Any k-permutation is fine as long as A and B use the same one.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// v_mfma_f32_16x16x32_bf16. Lane l holds row/col (l & 15) and k-group (l >> 4); C lane l holds
+// column (l & 15), rows 4*(l>>4) + r.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 lds_load16(const char* p) {
+  return *(const SMQA_LDS bf16x8*)(const SMQA_LDS char*)p;
+}
+// ds_read_b64_tr_b16. Within each group of 16 lanes, lane 4*r + c points at row r, columns
+// 4c..4c+3 of a 4x16 block of 16-bit elements; lane j receives column j of rows 0..3.
+__device__ __forceinline__ s16x4 lds_load_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((SMQA_LDS s16x4*)(SMQA_LDS char*)p);
+}
+// Concatenate two 4-element transposing reads into one 8-element MFMA operand. Built with a
+// whole-vector shuffle and one bitcast: element-wise insertion of bit-cast halves has been
+// observed to compile into lane-duplicating v_perm sequences.
+__device__ __forceinline__ bf16x8 join_tr(s16x4 lo, s16x4 hi) {
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+// 16-byte global -> LDS copy without a register round trip (global_load_lds_dwordx4).
+// lds_base must be the same for the whole wave; lane l lands at lds_base + 16*l.
+__device__ __forceinline__ void dma16(const void* gsrc, char* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (SMQA_LDS void*)(SMQA_LDS char*)lds_base, 16, 0, 0);
+}
+// Wait for all outstanding memory operations of this wave (including LDS DMA).
+__device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *(const uint4*)p);
+}
+__device__ __forceinline__ bf16x8 zero_bf16x8() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
+
+__device__ __forceinline__ bool slot_in_range(int32_t i, int64_t S_kv) {
+  return i >= 0 && (int64_t)i < S_kv;
+}
+
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = (__bf16)a; v[1] = (__bf16)b; v[2] = (__bf16)c; v[3] = (__bf16)d;
+  return __builtin_bit_cast(uint2, v);
+}
+
+__device__ __forceinline__ float wave_max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+
+}  // namespace smqa
