@@ -59,9 +59,7 @@ class Step:
         self.acc = torch.empty((B, S_kv, D), dtype=torch.float32, device=dev)
         self.dkv = torch.empty((B, S_kv, D), dtype=torch.bfloat16, device=dev)
         self.stream = torch.cuda.current_stream()
-        self.events = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                       for k in KERNELS}
-        self.times = {k: 0.0 for k in KERNELS}
+        self.events = []  # one {kernel: (start, end)} per timed step
         self.nan = float("nan")
 
     def _check(self, name, st):
@@ -83,16 +81,21 @@ class Step:
                                                     p(self.delta), p(self.acc), B, S, S_kv, H, D, K, self.nan, h),
             "bwd_postprocess": lambda: L.sparse_mqa_bwd_postprocess(p(self.acc), p(self.dkv), B, S_kv, D, h),
         }
+        ev = {}
         for k in KERNELS:
             if timed:
-                self.events[k][0].record(self.stream)
+                ev[k] = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                ev[k][0].record(self.stream)
             self._check(k, calls[k]())
             if timed:
-                self.events[k][1].record(self.stream)
+                ev[k][1].record(self.stream)
+        if timed:
+            self.events.append(ev)
 
-    def collect(self):
-        for k in KERNELS:
-            self.times[k] += self.events[k][0].elapsed_time(self.events[k][1])
+    def kernel_ms(self):
+        """Average event-timed duration of each kernel over the timed steps."""
+        n = len(self.events)
+        return {k: sum(e[k][0].elapsed_time(e[k][1]) for e in self.events) / n for k in KERNELS}
 
 
 def cpu_baseline(x, w, valid_per_token):
@@ -161,10 +164,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
-    # per-kernel event times (each kernel bracketed on its own stream)
-    step.times = {k: 0.0 for k in KERNELS}
-    step.collect()
-    ms = {k: step.times[k] / args.steps for k in KERNELS}
+    # per-kernel event times (each kernel bracketed on the stream it runs on)
+    ms = step.kernel_ms()
     ms_step = total_ms / args.steps
 
     HD = w.H * w.D

@@ -193,7 +193,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
 #pragma unroll
       for (int r = 0; r < 4; r++) {
         const int t = 16 * mt + 4 * g + r;
-        const float p = ((mask >> t) & 1ull) ? exp2f(sacc[mt][r] * scale_log2 - lse_h) : 0.f;
+        const float p = ((mask >> t) & 1ull) ? fast_exp2(sacc[mt][r] * scale_log2 - lse_h) : 0.f;
         dsb[4 * mt + r] = (__bf16)(p * (dpacc[mt][r] - delta_h));
       }
     const int t0 = 4 * g + ((lane & 15) >> 2);
@@ -324,7 +324,7 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
 #pragma unroll
       for (int r = 0; r < 4; r++) {
         const int t = 16 * mt + 4 * g + r;
-        p[r] = ((mask >> t) & 1ull) ? exp2f(sacc[mt][r] * scale_log2 - lse_h) : 0.f;
+        p[r] = ((mask >> t) & 1ull) ? fast_exp2(sacc[mt][r] * scale_log2 - lse_h) : 0.f;
         ds[r] = sm_scale * p[r] * (dpacc[mt][r] - delta_h);
       }
       float plr[4], dslr[4];

@@ -69,4 +69,8 @@ __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) 
 
 __device__ __forceinline__ float wave_max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 
+// 2^x with the hardware v_exp_f32 (no denormal-range fix-up): used for softmax weights, whose
+// arguments are <= 8 here and whose tiny results only feed bf16 operands and fp32 sums.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 }  // namespace smqa

@@ -6,9 +6,10 @@
 //   S^T[slot, head] = K[slot, :] . Q[head, :]^T    bf16 MFMA 32x32x16, K from LDS, Q in VGPRs
 //   online softmax in log2 units, sink folded into the running max and sum
 //   O^T[d, head]   += V^T[d, slot] . P^T[slot, head]  bf16 MFMA, V^T read with ds_read_b64_tr_b16
-// Waves are (head group of 32) x (half). For S^T a wave owns 32 slots of the block; for the
-// P.V product it owns half of D. The two halves of a head group swap their block maxima and
-// their bf16 P through LDS.
+// Waves are (head group of 32) x (half of D). Each wave keeps Q for its half of D, computes a
+// partial S^T over that half for all 64 slots, and swaps the fp32 partials with the other half
+// through LDS; both then hold the full scores, run the softmax redundantly and accumulate O for
+// their own half of D.
 #include "device_common.h"
 #include "launch.h"
 
@@ -21,30 +22,24 @@ __device__ __forceinline__ int fwd_swz(int row) {
   const int r = row & 15;
   return ((r & 3) << 2) | (r >> 2);
 }
-template <int D>
-__device__ __forceinline__ int fwd_off(int row, int chunk) {
-  return row * (D * 2) + ((chunk ^ (fwd_swz(row) & (D / 8 - 1))) << 4);
-}
 
 template <int D, int NHG>
 __global__ void __launch_bounds__(NHG * 128)
 fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const float* __restrict__ sink,
            const int32_t* __restrict__ idx, uint16_t* __restrict__ out, float* __restrict__ lse, int S,
            int64_t S_kv, int H, int topk, float scale_log2, int n_hblk, int n_tokens) {
-  constexpr int T = 64;
-  constexpr int NW = 2 * NHG;
+  constexpr int T = 64;           // slots per block
+  constexpr int NW = 2 * NHG;     // waves
+  constexpr int DH = D / 2;       // d-columns owned by one wave of a head-group pair
   constexpr int ROWB = D * 2;
   constexpr int CPR = D / 8;
   constexpr int TB = T * ROWB;
   constexpr int RPI = 1024 / ROWB;
   constexpr int NINSTR = T / RPI;
-  constexpr int MAXB = NHG * 2 * 32 * 4;
-  constexpr int PB = NHG * 2 * 2 * 64 * 16;
-  __shared__ __attribute__((aligned(16))) char smem[2 * TB + MAXB + PB + MAXB];
+  constexpr int XB = 2 * 16 * 64 * 4;  // one wave's partial S^T: 2 tiles x 16 regs x 64 lanes fp32
+  __shared__ __attribute__((aligned(16))) char smem[2 * TB + NW * XB];
   char* tiles = smem;
-  float* maxbuf = (float*)(smem + 2 * TB);
-  uint4* pbuf = (uint4*)(smem + 2 * TB + MAXB);
-  float* lbuf = (float*)(smem + 2 * TB + MAXB + PB);
+  char* xbuf = smem + 2 * TB;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -57,21 +52,22 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
   const int head = hblk * 32 * NHG + 32 * hg + (lane & 31);
   const bool head_ok = head < H;
 
-  // Q as the B operand of S^T = K Q^T: lane holds head (lane & 31), d = 16 ks + 8 kg .. +7.
-  bf16x8 qb[D / 16];
+  // Q for this wave's half of D, as the B operand of S^T = K Q^T:
+  // lane holds head (lane & 31), d = half*DH + 16 ks + 8 kg .. +7.
+  bf16x8 qb[DH / 16];
   {
-    const uint16_t* qrow = q + (token * H + (head_ok ? head : 0)) * (int64_t)D + 8 * kg;
+    const uint16_t* qrow = q + (token * H + (head_ok ? head : 0)) * (int64_t)D + half * DH + 8 * kg;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ks++) qb[ks] = head_ok ? load_bf16x8(qrow + 16 * ks) : zero_bf16x8();
+    for (int ks = 0; ks < DH / 16; ks++) qb[ks] = head_ok ? load_bf16x8(qrow + 16 * ks) : zero_bf16x8();
   }
   const float sink2 = head_ok ? sink[head] * kLog2e : 0.f;
   float m_run = sink2;
-  // The sink's term of the denominator is carried by one lane per head.
-  float l_run = (half == 0 && kg == 0 && sink2 != -INFINITY) ? 1.f : 0.f;
+  // The sink's share of the denominator is carried by the kg == 0 lane of each head.
+  float l_run = (kg == 0 && sink2 != -INFINITY) ? 1.f : 0.f;
 
-  f32x16 oacc[D / 64];
+  f32x16 oacc[DH / 32];
 #pragma unroll
-  for (int dt = 0; dt < D / 64; dt++)
+  for (int dt = 0; dt < DH / 32; dt++)
 #pragma unroll
     for (int r = 0; r < 16; r++) oacc[dt][r] = 0.f;
 
@@ -83,18 +79,58 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
     const int t = blk * T + lane;
     return t < topk ? idx_tok[t] : -1;
   };
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // wave index as a scalar
   auto issue_tile = [&](int32_t my_idx, uint64_t mask, int buf) {
     char* tile = tiles + buf * TB;
-    for (int ins = w; ins < NINSTR; ins += NW) {
-      const int r = ins * RPI + lane / CPR;
-      const int p = lane % CPR;
-      const int c = p ^ (fwd_swz(r) & (CPR - 1));
-      const int32_t ri = __shfl(my_idx, r);
-      const bool v = (mask >> r) & 1ull;
-      const char* src = v ? kv_b + (int64_t)ri * ROWB + c * 16 : (const char*)g_zero_row + c * 16;
-      dma16(src, tile + ins * 1024);
+    if constexpr (RPI == 1) {
+      // One kv row per instruction: row index and validity are wave-uniform (scalar registers).
+      // The lane id is passed through an empty asm so the per-row lane offsets are computed
+      // here (two VALU ops each) instead of being hoisted out of the block loop, where they
+      // would hold 16 registers for the whole kernel.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+#pragma unroll
+      for (int i = 0; i < NINSTR / NW; i++) {
+        const int r = wu + NW * i;
+        const int32_t ri = __builtin_amdgcn_readlane(my_idx, r);
+        const char* row = ((mask >> r) & 1ull) ? kv_b + (int64_t)ri * ROWB : (const char*)g_zero_row;
+        dma16(row + (uint32_t)((ln ^ (fwd_swz(r) & (CPR - 1))) << 4), tile + r * ROWB);
+      }
+    } else {
+      for (int ins = wu; ins < NINSTR; ins += NW) {
+        const int r = ins * RPI + lane / CPR;
+        const int p = lane % CPR;
+        const int c = p ^ (fwd_swz(r) & (CPR - 1));
+        const int32_t ri = __shfl(my_idx, r);
+        const bool v = (mask >> r) & 1ull;
+        const char* src = v ? kv_b + (int64_t)ri * ROWB + c * 16 : (const char*)g_zero_row + c * 16;
+        dma16(src, tile + ins * 1024);
+      }
     }
   };
+
+  // Per-lane parts of the LDS addresses, fixed for the whole kernel. The XOR swizzle only touches
+  // the low four chunk bits, so chunks 16 apart differ by 256 bytes (an instruction offset).
+  // S^T reads: row (lane & 31) (+32 for the second tile), chunk half*DH/8 + 2 ks + kg.
+  constexpr int KSJ = (DH / 16) < 8 ? (DH / 16) : 8;
+  const int arow = lane & 31;
+  int qk_off[KSJ];
+#pragma unroll
+  for (int j = 0; j < KSJ; j++)
+    qk_off[j] = arow * ROWB + (((half * (DH / 8) + 2 * j + kg) ^ (fwd_swz(arow) & (CPR - 1))) << 4);
+  // V^T reads: row t0 (+8 for the upper k-half), chunk c0 + 4 dt; pv_off[a][k] covers dt % NK == k.
+  const int t0 = 4 * kg + ((lane & 15) >> 2);
+  const int c0 = (half * DH + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) >> 3;
+  const int hoff = (lane & 1) ? 8 : 0;
+  constexpr int NK = (DH / 32) < 4 ? (DH / 32) : 4;
+  int pv_off[2][NK];
+#pragma unroll
+  for (int a = 0; a < 2; a++)
+#pragma unroll
+    for (int k = 0; k < NK; k++)
+      pv_off[a][k] = (t0 + 8 * a) * ROWB + (((c0 + 4 * k) ^ (fwd_swz(t0 + 8 * a) & (CPR - 1))) << 4) + hoff;
+  float4* xmine = (float4*)(xbuf + w * XB);
+  const float4* xpart = (const float4*)(xbuf + (w ^ 1) * XB);
 
   int32_t idx_cur = load_idx(0);
   uint64_t mask_cur = __ballot(slot_in_range(idx_cur, S_kv));
@@ -117,97 +153,98 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
     if (mask == 0) continue;
 
     const char* tile = tiles + buf * TB;
-    // ---- S^T for this wave's 32 slots x 32 heads
-    f32x16 sacc0, sacc1;
+    // ---- partial S^T over this wave's half of D, for all 64 slots (two 32-slot tiles)
+    f32x16 sacc[2];
 #pragma unroll
-    for (int r = 0; r < 16; r++) { sacc0[r] = 0.f; sacc1[r] = 0.f; }
-    const int arow = 32 * half + (lane & 31);
+    for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ks += 2) {
-      const bf16x8 a0 = lds_load16(tile + fwd_off<D>(arow, 2 * ks + kg));
-      const bf16x8 a1 = lds_load16(tile + fwd_off<D>(arow, 2 * ks + 2 + kg));
-      sacc0 = mfma32(a0, qb[ks], sacc0);
-      sacc1 = mfma32(a1, qb[ks + 1], sacc1);
+      for (int r = 0; r < 16; r++) sacc[mt][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < DH / 16; ks++) {
+      const int off = qk_off[ks % KSJ] + 256 * (ks / KSJ);
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++)
+        sacc[mt] = mfma32(lds_load16(tile + off + 32 * mt * ROWB), qb[ks], sacc[mt]);
     }
-    // ---- masked scores in log2 units, block max per head
-    float s2[16];
+    // ---- swap partial sums with the other half of the head group
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; r4++)
+        xmine[(mt * 4 + r4) * 64 + lane] = make_float4(sacc[mt][4 * r4], sacc[mt][4 * r4 + 1],
+                                                       sacc[mt][4 * r4 + 2], sacc[mt][4 * r4 + 3]);
+    __syncthreads();
+    float s2[2][16];
     float bmax = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const int t = 32 * half + 8 * (r >> 2) + 4 * kg + (r & 3);
-      const float v = (sacc0[r] + sacc1[r]) * scale_log2;
-      s2[r] = ((mask >> t) & 1ull) ? v : -INFINITY;
-      bmax = fmaxf(bmax, s2[r]);
-    }
-    bmax = wave_max_xor32(bmax);
-    float* mb = maxbuf + hg * 64;
-    if (kg == 0) mb[half * 32 + (lane & 31)] = bmax;
-    __syncthreads();
-    const float pmax = mb[(half ^ 1) * 32 + (lane & 31)];
-    const float m_new = fmaxf(m_run, fmaxf(bmax, pmax));  // finite: the block has a valid slot
-    const float alpha = exp2f(m_run - m_new);
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; r4++) {
+        const float4 o = xpart[(mt * 4 + r4) * 64 + lane];
+        const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int r = 4 * r4 + i;
+          const int t = 32 * mt + 8 * r4 + 4 * kg + i;
+          const float v = (sacc[mt][r] + ov[i]) * scale_log2;
+          s2[mt][r] = ((mask >> t) & 1ull) ? v : -INFINITY;
+          bmax = fmaxf(bmax, s2[mt][r]);
+        }
+      }
+    bmax = wave_max_xor32(bmax);  // block max of this head over the 64 slots
+    // The running max only moves when the block exceeds it by more than 8 (log2 units), so P
+    // stays <= 2^8 and the O rescale below runs on a few blocks only; O / l and m + log2(l)
+    // do not depend on where the max sits.
+    const float m_new = (bmax > m_run + 8.f) ? bmax : m_run;  // bmax is finite: a slot is valid
+    const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
 
     float psum = 0.f;
-    bf16x8 pown[2];
+    bf16x8 pb[2][2];  // B operand of O^T += V^T P^T: k-step (mt, j)
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const float p = exp2f(s2[r] - m_new);
-      psum += p;
-      pown[r >> 3][r & 7] = (__bf16)p;
-    }
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const float p = fast_exp2(s2[mt][r] - m_new);
+        psum += p;
+        pb[mt][r >> 3][r & 7] = (__bf16)p;
+      }
     l_run = l_run * alpha + psum;
-
-    uint4* pb = pbuf + hg * 256;
-    pb[half * 128 + lane] = __builtin_bit_cast(uint4, pown[0]);
-    pb[half * 128 + 64 + lane] = __builtin_bit_cast(uint4, pown[1]);
     if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int dt = 0; dt < D / 64; dt++)
+      for (int dt = 0; dt < DH / 32; dt++)
 #pragma unroll
         for (int r = 0; r < 16; r++) oacc[dt][r] *= alpha;
     }
-    __syncthreads();
-    bf16x8 ppart[2];
-    ppart[0] = __builtin_bit_cast(bf16x8, pb[(half ^ 1) * 128 + lane]);
-    ppart[1] = __builtin_bit_cast(bf16x8, pb[(half ^ 1) * 128 + 64 + lane]);
 
-    // ---- O^T[d, head] += V^T[d, slot] P^T[slot, head] over the 64 slots, for this wave's half of D.
-    // k-order of a 16-slot step (hs, j): element e <-> slot 32 hs + 16 j + 8 (e>>2) + 4 kg + (e&3),
-    // which is the C-layout order of S^T, so P needs no shuffle.
-    const int dbase = half * (D / 2);
+    // ---- O^T[d, head] += V^T[d, slot] P^T[slot, head] over the 64 slots, this wave's half of D.
+    // k-order of step (mt, j): element e <-> slot 32 mt + 16 j + 8 (e>>2) + 4 kg + (e&3), the
+    // C-layout order of S^T, so P needs no shuffle.
 #pragma unroll
-    for (int hs = 0; hs < 2; hs++) {
+    for (int mt = 0; mt < 2; mt++)
 #pragma unroll
       for (int j = 0; j < 2; j++) {
-        const bf16x8 bop = (hs == half) ? pown[j] : ppart[j];
-        const int t0 = 32 * hs + 16 * j + 4 * kg + ((lane & 15) >> 2);
+        const int rowb = (32 * mt + 16 * j) * ROWB;
 #pragma unroll
-        for (int dt = 0; dt < D / 64; dt++) {
-          const int d = dbase + 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-          const int hoff = (d & 4) ? 8 : 0;
-          const s16x4 lo = lds_load_tr(tile + fwd_off<D>(t0, d >> 3) + hoff);
-          const s16x4 hi = lds_load_tr(tile + fwd_off<D>(t0 + 8, d >> 3) + hoff);
-          oacc[dt] = mfma32(join_tr(lo, hi), bop, oacc[dt]);
+        for (int dt = 0; dt < DH / 32; dt++) {
+          const int imm = rowb + 256 * (dt / NK);
+          const s16x4 lo = lds_load_tr(tile + pv_off[0][dt % NK] + imm);
+          const s16x4 hi = lds_load_tr(tile + pv_off[1][dt % NK] + imm);
+          oacc[dt] = mfma32(join_tr(lo, hi), pb[mt][j], oacc[dt]);
         }
       }
-    }
   }
 
-  // ---- epilogue: total denominator, normalise, store O (bf16) and LSE (log2)
-  float ltot = l_run + __shfl_xor(l_run, 32);
-  float* lb = lbuf + hg * 64;
-  if (kg == 0) lb[half * 32 + (lane & 31)] = ltot;
-  __syncthreads();
-  ltot += lb[(half ^ 1) * 32 + (lane & 31)];
+  // ---- epilogue: normalise, store O (bf16) and LSE (log2)
+  const float ltot = l_run + __shfl_xor(l_run, 32);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   if (head_ok) {
     uint16_t* orow = out + (token * H + head) * (int64_t)D;
 #pragma unroll
-    for (int dt = 0; dt < D / 64; dt++)
+    for (int dt = 0; dt < DH / 32; dt++)
 #pragma unroll
       for (int r4 = 0; r4 < 4; r4++) {
-        const int d = half * (D / 2) + 32 * dt + 8 * r4 + 4 * kg;
+        const int d = half * DH + 32 * dt + 8 * r4 + 4 * kg;
         *(uint2*)(orow + d) = pack4_bf16(oacc[dt][4 * r4] * inv, oacc[dt][4 * r4 + 1] * inv,
                                          oacc[dt][4 * r4 + 2] * inv, oacc[dt][4 * r4 + 3] * inv);
       }
