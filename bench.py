@@ -2,8 +2,9 @@
 """Throughput of the top-k sparse MQA hot path (forward + backward) on one MI355X.
 
 One step = one pass of the whole path over one batch of seeded synthetic input: the forward
-(O, LSE), then the backward on those outputs (Delta preprocess, accumulator clear, dQ kernel,
-dKV scatter kernel, fp32 -> bf16 postprocess). Inputs are resident in HBM before timing starts.
+(O, LSE), then the backward on those outputs (Delta preprocess, dQ kernel, and the dKV stage:
+row ranking and scan, the dKV kernel writing each pair's contribution row, and the per-row
+reduction that also emits the bf16 dKV). Inputs are resident in HBM before timing starts.
 
 Prints one JSON line. `value` is the step's algorithmic TFLOP/s: (4 + 10) * H * D flops per valid
 (token, slot) pair (forward 4HD: QK^T and PV; backward 10HD: score recompute, dP, dQ, dKV) divided
@@ -26,7 +27,7 @@ import torch
 METRIC = "sparse-MQA fwd/bwd TFLOP/s and % bf16 MFMA peak @ H=64 D=512 topk=2048"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
-KERNELS = ("fwd", "bwd_preprocess", "bwd_zero", "bwd_dq", "bwd_dkv", "bwd_postprocess")
+KERNELS = ("fwd", "bwd_preprocess", "bwd_dq", "bwd_dkv")
 
 
 def parse():
@@ -56,8 +57,9 @@ class Step:
         self.lse = torch.empty((B, S, H), dtype=torch.float32, device=dev)
         self.delta = torch.empty((B, S, H), dtype=torch.float32, device=dev)
         self.dq = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev)
-        self.acc = torch.empty((B, S_kv, D), dtype=torch.float32, device=dev)
         self.dkv = torch.empty((B, S_kv, D), dtype=torch.bfloat16, device=dev)
+        self.ws_bytes = smqa.bwd_workspace_bytes(B, S, S_kv, H, D, w.topk)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
         self.stream = torch.cuda.current_stream()
         self.events = []  # one {kernel: (start, end)} per timed step
         self.nan = float("nan")
@@ -74,12 +76,11 @@ class Step:
             "fwd": lambda: L.sparse_mqa_fwd(p(self.q), p(self.kv), p(self.sink), p(self.idx), p(self.o),
                                             p(self.lse), B, S, S_kv, H, D, K, self.nan, h),
             "bwd_preprocess": lambda: L.sparse_mqa_bwd_preprocess(p(self.o), p(self.do), p(self.delta), B, S, H, D, h),
-            "bwd_zero": lambda: (self.acc.zero_(), 0)[1],
             "bwd_dq": lambda: L.sparse_mqa_bwd_dq(p(self.q), p(self.kv), p(self.do), p(self.idx), p(self.lse),
                                                   p(self.delta), p(self.dq), B, S, S_kv, H, D, K, self.nan, h),
             "bwd_dkv": lambda: L.sparse_mqa_bwd_dkv(p(self.q), p(self.kv), p(self.do), p(self.idx), p(self.lse),
-                                                    p(self.delta), p(self.acc), B, S, S_kv, H, D, K, self.nan, h),
-            "bwd_postprocess": lambda: L.sparse_mqa_bwd_postprocess(p(self.acc), p(self.dkv), B, S_kv, D, h),
+                                                    p(self.delta), p(self.dkv), 0, p(self.ws), self.ws_bytes,
+                                                    B, S, S_kv, H, D, K, self.nan, h),
         }
         ev = {}
         for k in KERNELS:
@@ -211,9 +212,7 @@ def main():
             "traffic": None,
         },
     }
-    if dom == "bwd_dkv":
-        # the scatter-add payload (4 bytes per valid pair per d) against the measured fp32 atomic rate
-        out["roofline"]["atomic_payload_TBps"] = round(n_valid * w.D * 4 / (ms[dom] * 1e-3) / 1e12, 3)
+    out["dkv_scatter_payload_TBps"] = round(n_valid * w.D * 4 / (ms["bwd_dkv"] * 1e-3) / 1e12, 3)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, w, valid)
     print(json.dumps(out), flush=True)

@@ -67,17 +67,23 @@ int sparse_mqa_fwd(const void* q, const void* kv, const float* attn_sink, const 
                    void* o, float* lse, int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D,
                    int64_t topk, float sm_scale, void* stream);
 
-/* Bytes of device workspace sparse_mqa_bwd needs: Delta [B,S,H] fp32 plus, for the bf16 dKV
- * output, the fp32 dKV accumulator [B,S_kv,D], each rounded up to 256 bytes. Returns 0 for
- * invalid sizes. */
-size_t sparse_mqa_bwd_workspace_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D);
+/* Backward workspace. sparse_mqa_bwd and sparse_mqa_bwd_dkv take a device workspace: Delta
+ * [B,S,H] fp32 (sparse_mqa_bwd only), per-row counters and offsets, and the staging rows of the
+ * segmented dKV scatter-add (one fp32 row of D per valid (token, slot) pair and 64-head block).
+ * sparse_mqa_bwd_workspace_bytes is the size for one pass over all tokens (an upper bound that
+ * assumes every slot valid); any size >= sparse_mqa_bwd_workspace_min_bytes also works, and the
+ * tokens are then processed in chunks with an fp32 running sum. Both return 0 for invalid sizes. */
+size_t sparse_mqa_bwd_workspace_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D,
+                                      int64_t topk);
+size_t sparse_mqa_bwd_workspace_min_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D,
+                                          int64_t topk);
 
-/* Backward (bwd page, sparse_mqa_bwd_interface): preprocess (Delta), zero the accumulator,
- * the main kernels (dQ; dKV scatter-add), then postprocess (fp32 -> bf16) unless dkv_fp32.
- * dq [B,S,H,D] bf16. dkv [B,S_kv,D]: bf16 if dkv_fp32 == 0, else fp32 (and then it is the
- * accumulator itself). The call overwrites dq and dkv; it never accumulates into them.
- * attn_sink is accepted for the documented signature; the LSE already includes the sink, so
- * dQ and dKV do not read it. */
+/* Backward (bwd page, sparse_mqa_bwd_interface): preprocess (Delta), the dQ kernel, and the dKV
+ * kernel with its segmented scatter-add and per-row reduction (which also performs the fp32 ->
+ * bf16 postprocess). dq [B,S,H,D] bf16. dkv [B,S_kv,D]: bf16 if dkv_fp32 == 0, else fp32 (the
+ * fp32 sums themselves). The call overwrites dq and dkv; it never accumulates into them. Rows no
+ * valid slot references come out exactly 0. attn_sink is accepted for the documented signature;
+ * the LSE already includes the sink, so dQ and dKV do not read it. */
 int sparse_mqa_bwd(const void* q, const void* kv, const float* attn_sink, const void* o,
                    const void* d_o, const int32_t* topk_idxs, const float* lse, void* dq, void* dkv,
                    int dkv_fp32, void* workspace, size_t workspace_bytes, int64_t B, int64_t S,
@@ -87,23 +93,27 @@ int sparse_mqa_bwd(const void* q, const void* kv, const float* attn_sink, const 
 int sparse_mqa_bwd_preprocess(const void* o, const void* d_o, float* delta, int64_t B, int64_t S,
                               int64_t H, int64_t D, void* stream);
 
-/* Stage: the main backward (bwd page, bwd factory). Writes dq (bf16) and adds every valid
- * slot's dKV contribution into dkv_accum [B,S_kv,D] fp32 with atomic adds. dkv_accum must be
- * zeroed by the caller first (it is not cleared here); rows no slot references are untouched. */
+/* Stage: dQ alone (bwd page, bwd factory): writes dq (bf16) from q, kv, dO, indices, LSE, Delta. */
+int sparse_mqa_bwd_dq(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs,
+                      const float* lse, const float* delta, void* dq, int64_t B, int64_t S,
+                      int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale, void* stream);
+
+/* Stage: dKV alone (bwd page, bwd and postprocess factories) with the segmented scatter-add:
+ * writes dkv (bf16, or fp32 if dkv_fp32) completely. Workspace as for sparse_mqa_bwd without the
+ * Delta part (sparse_mqa_bwd_workspace_bytes minus Delta's bytes is enough for one pass). */
+int sparse_mqa_bwd_dkv(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs,
+                       const float* lse, const float* delta, void* dkv, int dkv_fp32, void* workspace,
+                       size_t workspace_bytes, int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D,
+                       int64_t topk, float sm_scale, void* stream);
+
+/* Stage, workspace-free variant of the main backward: writes dq and adds every valid slot's dKV
+ * contribution into dkv_accum [B,S_kv,D] fp32 with fp32 atomic adds. dkv_accum must be zeroed by
+ * the caller first; rows no slot references are untouched. Slower than the staged path on MI355X
+ * (the fp32 atomic rate bounds it) but needs no staging memory. */
 int sparse_mqa_bwd_main(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs,
                         const float* lse, const float* delta, void* dq, float* dkv_accum, int64_t B,
                         int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale,
                         void* stream);
-
-/* The two halves of sparse_mqa_bwd_main, exported so each kernel can be timed or tested on its
- * own: sparse_mqa_bwd_dq writes dq only; sparse_mqa_bwd_dkv only adds into dkv_accum.
- * Arguments, layouts and errors as for sparse_mqa_bwd_main. */
-int sparse_mqa_bwd_dq(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs,
-                      const float* lse, const float* delta, void* dq, int64_t B, int64_t S,
-                      int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale, void* stream);
-int sparse_mqa_bwd_dkv(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs,
-                       const float* lse, const float* delta, float* dkv_accum, int64_t B, int64_t S,
-                       int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale, void* stream);
 
 /* Stage: dkv[b,j,d] = bf16(dkv_accum[b,j,d]) with round-to-nearest-even (bwd page,
  * postprocess factory). */

@@ -72,11 +72,23 @@ def test_fwd_validation(lib):
     assert fwd(lib, lse=E + 4096) == ALIAS
 
 
+def r256(n):
+    return (n + 255) // 256 * 256
+
+
 def test_workspace_bytes(lib):
-    n = lib.sparse_mqa_bwd_workspace_bytes(1, 4096, 4096, 64, 512)
-    assert n == 4096 * 64 * 4 + 4096 * 512 * 4
-    assert lib.sparse_mqa_bwd_workspace_bytes(1, 3, 5, 16, 64) == 256 + 5 * 64 * 4 + (256 - (5 * 64 * 4) % 256) % 256
-    assert lib.sparse_mqa_bwd_workspace_bytes(0, 1, 1, 1, 1) == 0
+    B, S, S_kv, H, D, K = 1, 4096, 4096, 64, 512, 2048
+    n_cnt = 16 * B * S_kv  # sixteen rank counters per kv row
+    fixed = r256((n_cnt + 4) * 4) + r256((n_cnt + 1) * 4) + r256(((n_cnt + 4095) // 4096) * 4)
+    full = lib.sparse_mqa_bwd_workspace_bytes(B, S, S_kv, H, D, K)
+    assert full == r256(B * S * H * 4) + fixed + r256(B * S * K * 4) + r256(B * S * K * D * 4) + 512
+    low = lib.sparse_mqa_bwd_workspace_min_bytes(B, S, S_kv, H, D, K)
+    assert low == r256(B * S * H * 4) + fixed + r256(B * S_kv * D * 4) + r256(K * 4) + r256(K * D * 4) + 512
+    # H = 128 runs two 64-head workgroups per token: two staging rows per valid slot
+    assert (lib.sparse_mqa_bwd_workspace_bytes(1, 8, 16, 128, 512, 4)
+            - lib.sparse_mqa_bwd_workspace_bytes(1, 8, 16, 64, 512, 4)) == r256(8 * 4 * 2 * 512 * 4) - r256(8 * 4 * 512 * 4) + r256(8 * 128 * 4) - r256(8 * 64 * 4)
+    assert lib.sparse_mqa_bwd_workspace_bytes(0, 1, 1, 16, 64, 1) == 0
+    assert lib.sparse_mqa_bwd_workspace_min_bytes(1, 1, 1, 48, 512, 1) == 0
 
 
 def bwd(lib, dkv_fp32=0, ws=G, wsb=1 << 30, dq=0x71000000, dkv=0x72000000, o=E, B=1, S=8, S_kv=16, H=64, D=512,
@@ -91,6 +103,8 @@ def test_bwd_validation(lib):
     assert bwd(lib, H=8) == UNSUP
     assert bwd(lib, ws=None) == WORKSPACE
     assert bwd(lib, wsb=100) == WORKSPACE
+    low = lib.sparse_mqa_bwd_workspace_min_bytes(1, 8, 16, 64, 512, 4)
+    assert bwd(lib, wsb=low - 256, ws=0x7A000000) == WORKSPACE
     assert bwd(lib, ws=G + 4) == ALIGN
     assert bwd(lib, dq=A) == ALIAS
     assert bwd(lib, dkv=0x71000000 + 64) == ALIAS
@@ -106,8 +120,11 @@ def test_stage_validation(lib):
     assert lib.sparse_mqa_bwd_main(A, Bp, C, Dp, E, F_, G, A, 1, 8, 16, 64, 512, 4, NAN, None) == ALIAS
     assert lib.sparse_mqa_bwd_dq(A, Bp, C, Dp, E, F_, None, 1, 8, 16, 64, 512, 4, NAN, None) == NULL
     assert lib.sparse_mqa_bwd_dq(A, Bp, C, Dp, E, F_, G + 2, 1, 8, 16, 64, 512, 4, NAN, None) == ALIGN
-    assert lib.sparse_mqa_bwd_dkv(A, Bp, C, Dp, E, F_, None, 1, 8, 16, 64, 512, 4, NAN, None) == NULL
-    assert lib.sparse_mqa_bwd_dkv(A, Bp, C, Dp, E, F_, G, 1, 8, 16, 64, 512, 0, NAN, None) == SHAPE
+    assert lib.sparse_mqa_bwd_dkv(A, Bp, C, Dp, E, F_, None, 0, G, 1 << 30, 1, 8, 16, 64, 512, 4, NAN, None) == NULL
+    assert lib.sparse_mqa_bwd_dkv(A, Bp, C, Dp, E, F_, G, 0, G, 1 << 30, 1, 8, 16, 64, 512, 0, NAN, None) == SHAPE
+    assert lib.sparse_mqa_bwd_dkv(A, Bp, C, Dp, E, F_, G, 0, None, 1 << 30, 1, 8, 16, 64, 512, 4, NAN, None) == WORKSPACE
+    assert lib.sparse_mqa_bwd_dkv(A, Bp, C, Dp, E, F_, G, 0, 0x7C000000, 64, 1, 8, 16, 64, 512, 4, NAN, None) == WORKSPACE
+    assert lib.sparse_mqa_bwd_dkv(A, Bp, C, Dp, E, F_, G, 0, A, 1 << 30, 1, 8, 16, 64, 512, 4, NAN, None) == ALIAS
     assert lib.sparse_mqa_bwd_postprocess(None, A, 1, 16, 512, None) == NULL
     assert lib.sparse_mqa_bwd_postprocess(A, Bp, 1, 16, 12, None) == SHAPE
     assert lib.sparse_mqa_bwd_postprocess(A, A + 16, 1, 16, 512, None) == ALIAS

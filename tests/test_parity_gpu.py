@@ -153,6 +153,36 @@ def test_explicit_scale_and_int64_indices(gpu_lib):
     assert torch.equal(o64, o32)
 
 
+def test_dkv_paths_agree(gpu_lib):
+    """Staged dKV in one pass, in forced token chunks (bf16 and fp32 outputs), and the atomic
+    stage all match the oracle."""
+    w = syn.WORKLOADS["mid_h64_d512_k300"]
+    say("case", w.name, "dKV paths")
+    x = syn.workload_inputs(w)
+    o_ref, lse_ref = oracle.fwd(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"])
+    ob = o_ref.view(w.B, w.S, w.H, w.D).to(torch.bfloat16)
+    lb = lse_ref.view(w.B, w.S, w.H)
+    dkv_ref = oracle.dkv(x["q"], x["kv"], ob, x["do"], x["topk_idxs"], lb)
+    xg = gpu(x)
+    og, lg = ob.cuda(), lb.cuda()
+    delta = smqa.bwd_preprocess(og, xg["do"])
+    args = (xg["q"], xg["kv"], xg["do"], xg["topk_idxs"], lg, delta)
+    one = smqa.bwd_dkv(*args)
+    lib = smqa.load_library()
+    low = lib.sparse_mqa_bwd_workspace_min_bytes(w.B, w.S, w.S_kv, w.H, w.D, w.topk)
+    per_tok = w.topk * 4 + w.topk * w.D * 4
+    for fp32 in (False, True):
+        ws = torch.empty(low + 37 * per_tok, dtype=torch.uint8, device="cuda")  # 38 tokens per chunk
+        chunked = smqa.bwd_dkv(*args, dkv_fp32=fp32, workspace=ws)
+        torch.cuda.synchronize()
+        check_bf16(f"dKV chunked fp32={fp32}", chunked.view(-1, w.D), dkv_ref)
+    acc = torch.zeros(w.B, w.S_kv, w.D, dtype=torch.float32, device="cuda")
+    smqa.bwd_main(xg["q"], xg["kv"], xg["do"], xg["topk_idxs"], lg, delta, acc)
+    torch.cuda.synchronize()
+    check_bf16("dKV one pass", one.view(-1, w.D), dkv_ref)
+    check_bf16("dKV atomic", acc.view(-1, w.D), dkv_ref)
+
+
 def test_non_default_stream(gpu_lib):
     w = syn.WORKLOADS["mid_h64_d512_k300"]
     x = syn.workload_inputs(w)

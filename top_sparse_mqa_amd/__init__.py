@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     bwd_dq,
     bwd_main,
     bwd_postprocess,
+    bwd_workspace_bytes,
     bwd_preprocess,
     default_scale,
     load_library,

@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import ctypes
 import math
+import os
 from pathlib import Path
 from typing import Optional, Tuple
 
@@ -22,13 +23,15 @@ _i64 = ctypes.c_int64
 
 _SIGS = {
     "sparse_mqa_fwd": [_c_void_p] * 6 + [_i64] * 6 + [ctypes.c_float, _c_void_p],
-    "sparse_mqa_bwd_workspace_bytes": [_i64] * 5,
+    "sparse_mqa_bwd_workspace_bytes": [_i64] * 6,
+    "sparse_mqa_bwd_workspace_min_bytes": [_i64] * 6,
     "sparse_mqa_bwd": [_c_void_p] * 9 + [ctypes.c_int, _c_void_p, ctypes.c_size_t] + [_i64] * 6
     + [ctypes.c_float, _c_void_p],
     "sparse_mqa_bwd_preprocess": [_c_void_p] * 3 + [_i64] * 4 + [_c_void_p],
     "sparse_mqa_bwd_main": [_c_void_p] * 8 + [_i64] * 6 + [ctypes.c_float, _c_void_p],
     "sparse_mqa_bwd_dq": [_c_void_p] * 7 + [_i64] * 6 + [ctypes.c_float, _c_void_p],
-    "sparse_mqa_bwd_dkv": [_c_void_p] * 7 + [_i64] * 6 + [ctypes.c_float, _c_void_p],
+    "sparse_mqa_bwd_dkv": [_c_void_p] * 7 + [ctypes.c_int, _c_void_p, ctypes.c_size_t] + [_i64] * 6
+    + [ctypes.c_float, _c_void_p],
     "sparse_mqa_bwd_postprocess": [_c_void_p] * 2 + [_i64] * 3 + [_c_void_p],
     "sparse_mqa_status_string": [ctypes.c_int],
 }
@@ -59,6 +62,7 @@ def load_library() -> ctypes.CDLL:
             fn.argtypes = args
             fn.restype = ctypes.c_int
         lib.sparse_mqa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.sparse_mqa_bwd_workspace_min_bytes.restype = ctypes.c_size_t
         lib.sparse_mqa_status_string.restype = ctypes.c_char_p
         _lib = lib
     return _lib
@@ -76,6 +80,23 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
+
+
+# Largest backward workspace the binding allocates on its own; above it the library processes the
+# tokens in chunks (set SMQA_BWD_WORKSPACE_CAP_GIB to change).
+WORKSPACE_CAP = int(float(os.environ.get("SMQA_BWD_WORKSPACE_CAP_GIB", "32")) * 2 ** 30)
+
+
+def bwd_workspace_bytes(B: int, S: int, S_kv: int, H: int, D: int, topk: int, cap: Optional[int] = None) -> int:
+    """Workspace the binding uses: one pass over all tokens if that fits under the cap, else the
+    cap (at least the library's minimum), which the library turns into token chunks."""
+    lib = load_library()
+    full = lib.sparse_mqa_bwd_workspace_bytes(B, S, S_kv, H, D, topk)
+    low = lib.sparse_mqa_bwd_workspace_min_bytes(B, S, S_kv, H, D, topk)
+    if full == 0 or low == 0:
+        raise ValueError("invalid sizes for the backward workspace")
+    cap = WORKSPACE_CAP if cap is None else cap
+    return full if full <= cap else max(low, cap)
 
 
 def _scale_arg(sm_scale: Optional[float]) -> float:
@@ -169,9 +190,7 @@ def sparse_mqa_bwd_interface(q: torch.Tensor, kv: torch.Tensor, attn_sink: torch
     dq = torch.empty_like(q)
     dkv = torch.empty((B, S_kv, D), dtype=torch.float32 if return_dkv_accum_dtype else torch.bfloat16,
                       device=q.device)
-    ws_bytes = lib.sparse_mqa_bwd_workspace_bytes(B, S, S_kv, H, D)
-    if ws_bytes == 0:
-        raise ValueError("invalid sizes for the backward workspace")
+    ws_bytes = bwd_workspace_bytes(B, S, S_kv, H, D, topk)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     _check("sparse_mqa_bwd", lib.sparse_mqa_bwd(
         _ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(o), _ptr(do), _ptr(idx), _ptr(lse), _ptr(dq), _ptr(dkv),
@@ -233,15 +252,19 @@ def bwd_dq(q: torch.Tensor, kv: torch.Tensor, do: torch.Tensor, topk_idxs: torch
 
 
 def bwd_dkv(q: torch.Tensor, kv: torch.Tensor, do: torch.Tensor, topk_idxs: torch.Tensor, lse: torch.Tensor,
-            delta: torch.Tensor, dkv_accum: torch.Tensor, sm_scale: Optional[float] = None) -> torch.Tensor:
-    """dKV scatter kernel of the main backward stage alone: adds into dkv_accum (fp32)."""
+            delta: torch.Tensor, sm_scale: Optional[float] = None, dkv_fp32: bool = False,
+            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dKV stage alone (segmented scatter-add and per-row reduction): returns dKV."""
     idx = _main_stage_args(q, kv, do, topk_idxs, lse, delta)
-    _need(dkv_accum, "dkv_accum", torch.float32, 3)
     B, S, H, D = q.shape
+    S_kv, topk = kv.shape[1], idx.shape[2]
+    dkv = torch.empty((B, S_kv, D), dtype=torch.float32 if dkv_fp32 else torch.bfloat16, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(bwd_workspace_bytes(B, S, S_kv, H, D, topk), dtype=torch.uint8, device=q.device)
     _check("sparse_mqa_bwd_dkv", load_library().sparse_mqa_bwd_dkv(
-        _ptr(q), _ptr(kv), _ptr(do), _ptr(idx), _ptr(lse), _ptr(delta), _ptr(dkv_accum),
-        B, S, kv.shape[1], H, D, idx.shape[2], _scale_arg(sm_scale), _stream()))
-    return dkv_accum
+        _ptr(q), _ptr(kv), _ptr(do), _ptr(idx), _ptr(lse), _ptr(delta), _ptr(dkv), 1 if dkv_fp32 else 0,
+        _ptr(workspace), workspace.numel(), B, S, S_kv, H, D, topk, _scale_arg(sm_scale), _stream()))
+    return dkv
 
 
 def bwd_postprocess(dkv_accum: torch.Tensor) -> torch.Tensor:

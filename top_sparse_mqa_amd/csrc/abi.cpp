@@ -101,11 +101,122 @@ int sparse_mqa_fwd(const void* q, const void* kv, const float* attn_sink, const 
   return smqa::launch_fwd(a, (hipStream_t)stream) == hipSuccess ? SMQA_OK : SMQA_ERR_HIP;
 }
 
-size_t sparse_mqa_bwd_workspace_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D) {
-  if (B <= 0 || S <= 0 || S_kv <= 0 || H <= 0 || D <= 0) return 0;
-  const int64_t nd = count({B, S, H}), na = count({B, S_kv, D});
-  if (nd < 0 || na < 0) return 0;
-  return round256((size_t)nd * 4) + round256((size_t)na * 4);
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// Backward workspace: [Delta (full bwd only)] [count] [offset] [scan tiles] [acc (multi-chunk, bf16
+// output only)] [pos: chunk*topk int32] [staging: chunk*topk*n_hblk rows of D fp32].
+
+namespace {
+
+struct DkvPlan {
+  size_t count, offset, tiles, acc, pos, stage;  // byte offsets into the workspace
+  int64_t chunk;                                  // tokens per chunk
+  bool use_acc;                                   // a separate fp32 accumulator in the workspace
+  size_t end;                                     // bytes used
+};
+
+size_t fixed_dkv_bytes(int64_t B, int64_t S_kv) {
+  const int64_t n_cnt = smqa::rank_counters(B * S_kv);
+  return round256((size_t)(n_cnt + 4) * 4) + round256((size_t)(n_cnt + 1) * 4) +
+         round256((size_t)smqa::scan_tiles(n_cnt) * 4);
+}
+
+size_t per_token_dkv_bytes(int64_t H, int64_t D, int64_t topk) {
+  return (size_t)topk * 4 + (size_t)topk * smqa::bwd_hblocks(H) * D * 4;
+}
+
+// Lay out the dKV part of the workspace starting at `base`; false if `bytes` cannot hold even one
+// token's staging.
+bool plan_dkv(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, bool dkv_fp32, size_t base,
+              size_t bytes, DkvPlan* p) {
+  const int64_t n_rows = B * S_kv, tokens = B * S, n_cnt = smqa::rank_counters(n_rows);
+  size_t o = base;
+  p->count = o;
+  o += round256((size_t)(n_cnt + 4) * 4);
+  p->offset = o;
+  o += round256((size_t)(n_cnt + 1) * 4);
+  p->tiles = o;
+  o += round256((size_t)smqa::scan_tiles(n_cnt) * 4);
+  const size_t per_tok = per_token_dkv_bytes(H, D, topk);
+  // one pass over all tokens if it fits, else token chunks with an fp32 running sum
+  if (o + per_tok * tokens + 512 <= bytes) {
+    p->chunk = tokens;
+    p->use_acc = false;
+    p->acc = 0;
+  } else {
+    p->use_acc = !dkv_fp32;
+    p->acc = o;
+    if (p->use_acc) o += round256((size_t)n_rows * D * 4);
+    if (o + per_tok + 512 > bytes) return false;
+    p->chunk = (int64_t)((bytes - o - 512) / per_tok);
+    if (p->chunk > tokens) p->chunk = tokens;
+  }
+  p->pos = o;
+  o += round256((size_t)p->chunk * topk * 4);
+  p->stage = o;
+  o += round256((size_t)p->chunk * topk * smqa::bwd_hblocks(H) * D * 4);
+  p->end = o;
+  return o <= bytes;
+}
+
+size_t delta_bytes(int64_t B, int64_t S, int64_t H) { return round256((size_t)(B * S * H) * 4); }
+
+bool sizes_ok(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk) {
+  return check_shapes(B, S, S_kv, H, D, topk) == SMQA_OK;
+}
+
+// The staged dKV pass over all tokens, chunked as the plan says. dkv: bf16 or fp32 output.
+int run_dkv(const void* q, const void* kv, const void* d_o, const int32_t* idx, const float* lse, const float* delta,
+            void* dkv, int dkv_fp32, char* ws, const DkvPlan& p, int64_t B, int64_t S, int64_t S_kv, int64_t H,
+            int64_t D, int64_t topk, float scale, hipStream_t st) {
+  const int64_t tokens = B * S, n_rows = B * S_kv;
+  int32_t* count = (int32_t*)(ws + p.count);
+  int32_t* offset = (int32_t*)(ws + p.offset);
+  int32_t* tiles = (int32_t*)(ws + p.tiles);
+  int32_t* pos = (int32_t*)(ws + p.pos);
+  float* stage = (float*)(ws + p.stage);
+  float* acc = dkv_fp32 ? (float*)dkv : (p.use_acc ? (float*)(ws + p.acc) : nullptr);
+  for (int64_t t0 = 0; t0 < tokens; t0 += p.chunk) {
+    const int64_t n = (tokens - t0) < p.chunk ? (tokens - t0) : p.chunk;
+    if (smqa::launch_dkv_prepare(idx, count, offset, tiles, pos, B, S, S_kv, topk, smqa::bwd_hblocks(H), t0, n, st) !=
+        hipSuccess)
+      return SMQA_ERR_HIP;
+    smqa::BwdMainArgs a{q, kv, d_o, idx, lse, delta, nullptr, nullptr, pos, stage, B, S, S_kv, H, D, topk, scale,
+                        t0, n};
+    if (smqa::launch_bwd_main(a, 2, st) != hipSuccess) return SMQA_ERR_HIP;
+    const bool last = t0 + n >= tokens;
+    void* out16 = (!dkv_fp32 && last) ? dkv : nullptr;
+    if (smqa::launch_reduce_rows(stage, offset, acc, out16, t0 > 0 ? 1 : 0, n_rows, D, st) != hipSuccess)
+      return SMQA_ERR_HIP;
+  }
+  return SMQA_OK;
+}
+
+int check_bwd_inputs(const void* q, const void* kv, const void* d_o, const int32_t* idx, const float* lse,
+                     int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale,
+                     float* scale) {
+  if (!q || !kv || !d_o || !idx || !lse) return SMQA_ERR_NULL;
+  int st = check_shapes(B, S, S_kv, H, D, topk);
+  if (st) return st;
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(d_o) || !aligned4(lse) || !aligned4(idx)) return SMQA_ERR_ALIGN;
+  return resolve_scale(sm_scale, D, scale);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sparse_mqa_bwd_workspace_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk) {
+  if (!sizes_ok(B, S, S_kv, H, D, topk)) return 0;
+  return delta_bytes(B, S, H) + fixed_dkv_bytes(B, S_kv) + round256((size_t)(B * S) * topk * 4) +
+         round256((size_t)(B * S) * topk * smqa::bwd_hblocks(H) * D * 4) + 512;
+}
+
+size_t sparse_mqa_bwd_workspace_min_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk) {
+  if (!sizes_ok(B, S, S_kv, H, D, topk)) return 0;
+  return delta_bytes(B, S, H) + fixed_dkv_bytes(B, S_kv) + round256((size_t)(B * S_kv) * D * 4) +
+         round256((size_t)topk * 4) + round256((size_t)topk * smqa::bwd_hblocks(H) * D * 4) + 512;
 }
 
 int sparse_mqa_bwd_preprocess(const void* o, const void* d_o, float* delta, int64_t B, int64_t S, int64_t H,
@@ -122,59 +233,66 @@ int sparse_mqa_bwd_preprocess(const void* o, const void* d_o, float* delta, int6
                                                                                                  : SMQA_ERR_HIP;
 }
 
-static int bwd_main_checked(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs,
-                            const float* lse, const float* delta, void* dq, float* dkv_accum, int64_t B,
-                            int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, float scale, int which,
-                            hipStream_t stream) {
-  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, dkv_accum, B, S, S_kv, H, D, topk, scale};
-  return smqa::launch_bwd_main(a, which, stream) == hipSuccess ? SMQA_OK : SMQA_ERR_HIP;
-}
-
-// Validation shared by the main-stage entry points; which = 1 (dQ), 2 (dKV) or 3 (both).
-static int bwd_main_entry(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs,
-                          const float* lse, const float* delta, void* dq, float* dkv_accum, int64_t B, int64_t S,
-                          int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale, int which,
-                          void* stream) {
-  if (!q || !kv || !d_o || !topk_idxs || !lse || !delta) return SMQA_ERR_NULL;
-  if (((which & 1) && !dq) || ((which & 2) && !dkv_accum)) return SMQA_ERR_NULL;
-  int st = check_shapes(B, S, S_kv, H, D, topk);
-  if (st) return st;
-  if (!aligned16(q) || !aligned16(kv) || !aligned16(d_o) || !aligned4(lse) || !aligned4(delta) ||
-      !aligned4(topk_idxs))
-    return SMQA_ERR_ALIGN;
-  if (((which & 1) && !aligned16(dq)) || ((which & 2) && !aligned16(dkv_accum))) return SMQA_ERR_ALIGN;
+int sparse_mqa_bwd_dq(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs, const float* lse,
+                      const float* delta, void* dq, int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D,
+                      int64_t topk, float sm_scale, void* stream) {
   float scale;
-  if ((st = resolve_scale(sm_scale, D, &scale))) return st;
-  const int64_t qb = count({B, S, H, D}) * 2, ab = count({B, S_kv, D}) * 4;
-  const Span sdq{(which & 1) ? dq : nullptr, qb}, sacc{(which & 2) ? dkv_accum : nullptr, ab};
+  int st = check_bwd_inputs(q, kv, d_o, topk_idxs, lse, B, S, S_kv, H, D, topk, sm_scale, &scale);
+  if (st) return st;
+  if (!delta || !dq) return SMQA_ERR_NULL;
+  if (!aligned4(delta) || !aligned16(dq)) return SMQA_ERR_ALIGN;
+  const int64_t qb = count({B, S, H, D}) * 2;
+  const Span sdq{dq, qb};
   const Span ins[] = {{q, qb}, {kv, count({B, S_kv, D}) * 2}, {d_o, qb}, {topk_idxs, count({B, S, topk}) * 4},
                       {lse, count({B, S, H}) * 4}, {delta, count({B, S, H}) * 4}};
   for (const Span& s : ins)
-    if (overlap(sdq, s) || overlap(sacc, s)) return SMQA_ERR_ALIAS;
-  if (overlap(sdq, sacc)) return SMQA_ERR_ALIAS;
-  return bwd_main_checked(q, kv, d_o, topk_idxs, lse, delta, dq, dkv_accum, B, S, S_kv, H, D, topk, scale, which,
-                          (hipStream_t)stream);
+    if (overlap(sdq, s)) return SMQA_ERR_ALIAS;
+  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, nullptr, nullptr, nullptr, B, S, S_kv, H, D, topk,
+                      scale, 0, B * S};
+  return smqa::launch_bwd_main(a, 1, (hipStream_t)stream) == hipSuccess ? SMQA_OK : SMQA_ERR_HIP;
+}
+
+int sparse_mqa_bwd_dkv(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs, const float* lse,
+                       const float* delta, void* dkv, int dkv_fp32, void* workspace, size_t workspace_bytes,
+                       int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale,
+                       void* stream) {
+  float scale;
+  int st = check_bwd_inputs(q, kv, d_o, topk_idxs, lse, B, S, S_kv, H, D, topk, sm_scale, &scale);
+  if (st) return st;
+  if (!delta || !dkv) return SMQA_ERR_NULL;
+  if (!workspace) return SMQA_ERR_WORKSPACE;
+  if (!aligned4(delta) || !aligned16(dkv) || !aligned16(workspace)) return SMQA_ERR_ALIGN;
+  DkvPlan p;
+  if (!plan_dkv(B, S, S_kv, H, D, topk, dkv_fp32 != 0, 0, workspace_bytes, &p)) return SMQA_ERR_WORKSPACE;
+  const int64_t qb = count({B, S, H, D}) * 2, nkv = count({B, S_kv, D});
+  const Span sdkv{dkv, nkv * (dkv_fp32 ? 4 : 2)}, sws{workspace, (int64_t)p.end};
+  const Span ins[] = {{q, qb}, {kv, nkv * 2}, {d_o, qb}, {topk_idxs, count({B, S, topk}) * 4},
+                      {lse, count({B, S, H}) * 4}, {delta, count({B, S, H}) * 4}};
+  for (const Span& s : ins)
+    if (overlap(sdkv, s) || overlap(sws, s)) return SMQA_ERR_ALIAS;
+  if (overlap(sdkv, sws)) return SMQA_ERR_ALIAS;
+  return run_dkv(q, kv, d_o, topk_idxs, lse, delta, dkv, dkv_fp32, (char*)workspace, p, B, S, S_kv, H, D, topk, scale,
+                 (hipStream_t)stream);
 }
 
 int sparse_mqa_bwd_main(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs,
                         const float* lse, const float* delta, void* dq, float* dkv_accum, int64_t B, int64_t S,
                         int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale, void* stream) {
-  return bwd_main_entry(q, kv, d_o, topk_idxs, lse, delta, dq, dkv_accum, B, S, S_kv, H, D, topk, sm_scale, 3,
-                        stream);
-}
-
-int sparse_mqa_bwd_dq(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs, const float* lse,
-                      const float* delta, void* dq, int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D,
-                      int64_t topk, float sm_scale, void* stream) {
-  return bwd_main_entry(q, kv, d_o, topk_idxs, lse, delta, dq, nullptr, B, S, S_kv, H, D, topk, sm_scale, 1,
-                        stream);
-}
-
-int sparse_mqa_bwd_dkv(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs,
-                       const float* lse, const float* delta, float* dkv_accum, int64_t B, int64_t S, int64_t S_kv,
-                       int64_t H, int64_t D, int64_t topk, float sm_scale, void* stream) {
-  return bwd_main_entry(q, kv, d_o, topk_idxs, lse, delta, nullptr, dkv_accum, B, S, S_kv, H, D, topk, sm_scale,
-                        2, stream);
+  float scale;
+  int st = check_bwd_inputs(q, kv, d_o, topk_idxs, lse, B, S, S_kv, H, D, topk, sm_scale, &scale);
+  if (st) return st;
+  if (!delta || !dq || !dkv_accum) return SMQA_ERR_NULL;
+  if (!aligned4(delta) || !aligned16(dq) || !aligned16(dkv_accum)) return SMQA_ERR_ALIGN;
+  const int64_t qb = count({B, S, H, D}) * 2, ab = count({B, S_kv, D}) * 4;
+  const Span sdq{dq, qb}, sacc{dkv_accum, ab};
+  const Span ins[] = {{q, qb}, {kv, count({B, S_kv, D}) * 2}, {d_o, qb}, {topk_idxs, count({B, S, topk}) * 4},
+                      {lse, count({B, S, H}) * 4}, {delta, count({B, S, H}) * 4}};
+  for (const Span& s : ins)
+    if (overlap(sdq, s) || overlap(sacc, s)) return SMQA_ERR_ALIAS;
+  if (overlap(sdq, sacc)) return SMQA_ERR_ALIAS;
+  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, dkv_accum, nullptr, nullptr, B, S, S_kv, H, D, topk,
+                      scale, 0, B * S};
+  return smqa::launch_bwd_main(a, 3, (hipStream_t)stream) == hipSuccess ? SMQA_OK : SMQA_ERR_HIP;
 }
 
 int sparse_mqa_bwd_postprocess(const float* dkv_accum, void* dkv, int64_t B, int64_t S_kv, int64_t D,
@@ -191,22 +309,21 @@ int sparse_mqa_bwd_postprocess(const float* dkv_accum, void* dkv, int64_t B, int
 
 int sparse_mqa_bwd(const void* q, const void* kv, const float* attn_sink, const void* o, const void* d_o,
                    const int32_t* topk_idxs, const float* lse, void* dq, void* dkv, int dkv_fp32, void* workspace,
-                   size_t workspace_bytes, int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D,
-                   int64_t topk, float sm_scale, void* stream) {
-  if (!q || !kv || !attn_sink || !o || !d_o || !topk_idxs || !lse || !dq || !dkv) return SMQA_ERR_NULL;
-  int st = check_shapes(B, S, S_kv, H, D, topk);
-  if (st) return st;
-  if (!aligned16(q) || !aligned16(kv) || !aligned16(o) || !aligned16(d_o) || !aligned16(dq) || !aligned16(dkv) ||
-      !aligned4(lse) || !aligned4(attn_sink) || !aligned4(topk_idxs))
-    return SMQA_ERR_ALIGN;
+                   size_t workspace_bytes, int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk,
+                   float sm_scale, void* stream) {
   float scale;
-  if ((st = resolve_scale(sm_scale, D, &scale))) return st;
-  const size_t need_delta = round256((size_t)count({B, S, H}) * 4);
-  const size_t need = dkv_fp32 ? need_delta : sparse_mqa_bwd_workspace_bytes(B, S, S_kv, H, D);
-  if (!workspace || workspace_bytes < need) return SMQA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return SMQA_ERR_ALIGN;
+  int st = check_bwd_inputs(q, kv, d_o, topk_idxs, lse, B, S, S_kv, H, D, topk, sm_scale, &scale);
+  if (st) return st;
+  if (!attn_sink || !o || !dq || !dkv) return SMQA_ERR_NULL;
+  if (!workspace) return SMQA_ERR_WORKSPACE;
+  if (!aligned16(o) || !aligned16(dq) || !aligned16(dkv) || !aligned4(attn_sink) || !aligned16(workspace))
+    return SMQA_ERR_ALIGN;
+  const size_t dbytes = delta_bytes(B, S, H);
+  DkvPlan p;
+  if (workspace_bytes < dbytes || !plan_dkv(B, S, S_kv, H, D, topk, dkv_fp32 != 0, dbytes, workspace_bytes, &p))
+    return SMQA_ERR_WORKSPACE;
   const int64_t qb = count({B, S, H, D}) * 2, nkv = count({B, S_kv, D});
-  const Span sdq{dq, qb}, sdkv{dkv, nkv * (dkv_fp32 ? 4 : 2)}, sws{workspace, (int64_t)need};
+  const Span sdq{dq, qb}, sdkv{dkv, nkv * (dkv_fp32 ? 4 : 2)}, sws{workspace, (int64_t)p.end};
   const Span ins[] = {{q, qb}, {kv, nkv * 2}, {attn_sink, H * 4}, {o, qb}, {d_o, qb},
                       {topk_idxs, count({B, S, topk}) * 4}, {lse, count({B, S, H}) * 4}};
   for (const Span& s : ins)
@@ -215,14 +332,13 @@ int sparse_mqa_bwd(const void* q, const void* kv, const float* attn_sink, const 
 
   hipStream_t hs = (hipStream_t)stream;
   float* delta = (float*)workspace;
-  float* acc = dkv_fp32 ? (float*)dkv : (float*)((char*)workspace + need_delta);
-  const int64_t rows = count({B, S, H});
-  if (smqa::launch_bwd_preprocess(o, d_o, delta, rows, D, hs) != hipSuccess) return SMQA_ERR_HIP;
-  if (smqa::launch_fill_zero_f32(acc, nkv, hs) != hipSuccess) return SMQA_ERR_HIP;
-  if ((st = bwd_main_checked(q, kv, d_o, topk_idxs, lse, delta, dq, acc, B, S, S_kv, H, D, topk, scale, 3, hs)))
+  if (smqa::launch_bwd_preprocess(o, d_o, delta, count({B, S, H}), D, hs) != hipSuccess) return SMQA_ERR_HIP;
+  if ((st = run_dkv(q, kv, d_o, topk_idxs, lse, delta, dkv, dkv_fp32, (char*)workspace, p, B, S, S_kv, H, D, topk,
+                    scale, hs)))
     return st;
-  if (!dkv_fp32 && smqa::launch_bwd_postprocess(acc, dkv, nkv, hs) != hipSuccess) return SMQA_ERR_HIP;
-  return SMQA_OK;
+  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, nullptr, nullptr, nullptr, B, S, S_kv, H, D, topk,
+                      scale, 0, B * S};
+  return smqa::launch_bwd_main(a, 1, hs) == hipSuccess ? SMQA_OK : SMQA_ERR_HIP;
 }
 
 }  // extern "C"

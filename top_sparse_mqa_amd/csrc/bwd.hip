@@ -220,8 +220,9 @@ template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64)
 bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ dout,
                const int32_t* __restrict__ idx, const float* __restrict__ lse, const float* __restrict__ delta,
-               float* __restrict__ dkv_acc, int S, int64_t S_kv, int H, int topk, float sm_scale,
-               float scale_log2, int n_hblk, int n_tokens) {
+               float* __restrict__ dkv_acc, const int32_t* __restrict__ pos, float* __restrict__ stage,
+               int S, int64_t S_kv, int H, int topk, float sm_scale, float scale_log2, int n_hblk,
+               int token0, int n_tokens) {
   using C = BwdCommon<D, NW>;
   constexpr int T = C::T;
   constexpr int HB = 16 * NW;   // heads of this workgroup
@@ -239,10 +240,13 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, kg = lane >> 5;
   const int item = blockIdx.x;
-  const int64_t token = (int64_t)n_tokens - 1 - item / n_hblk;
+  const int64_t ctok = (int64_t)n_tokens - 1 - item / n_hblk;  // token within the chunk
+  const int64_t token = token0 + ctok;
   const int hblk = item % n_hblk;
   const int64_t b = token / S;
   const int hrow = 16 * w + (lane & 15);          // head within the workgroup's block
+  // staging mode: every valid slot owns n_hblk consecutive staging rows from pos[]
+  const int32_t* pos_tok = stage ? pos + ctok * (int64_t)topk : nullptr;
   const int head = hblk * HB + hrow;
 
   // (1) Q and dO with heads along k, as B operands of dKV = (sm_scale dS)^T Q + P^T dO:
@@ -287,12 +291,18 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
   const int nblk = (topk + T - 1) / T;
   const int32_t* idx_tok = idx + token * (int64_t)topk;
   const char* kv_b = (const char*)(kv + b * S_kv * D);
-  float* acc_b = dkv_acc + b * S_kv * D;
+  float* acc_b = stage ? nullptr : dkv_acc + b * S_kv * D;
   auto load_idx = [&](int blk) -> int32_t {
     const int t = blk * T + lane;
     return (lane < T && t < topk) ? idx_tok[t] : -1;
   };
+  auto load_pos = [&](int blk) -> int32_t {
+    const int t = blk * T + lane;
+    return (stage && lane < T && t < topk) ? pos_tok[t] : -1;
+  };
 
+  int32_t pos_cur = load_pos(0);
+  int32_t pos_nxt = nblk > 1 ? load_pos(1) : -1;
   int32_t idx_cur = load_idx(0);
   uint64_t mask_cur = __ballot(slot_in_range(idx_cur, S_kv));
   if (mask_cur) bwd_issue_tile<D, NW>(kv_b, idx_cur, mask_cur, smem, lane, w);
@@ -310,6 +320,9 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
     const int32_t idx_this = idx_cur;
     idx_cur = idx_nxt;
     idx_nxt = blk + 2 < nblk ? load_idx(blk + 2) : -1;
+    const int32_t pos_this = pos_cur;
+    pos_cur = pos_nxt;
+    pos_nxt = blk + 2 < nblk ? load_pos(blk + 2) : -1;
     const uint64_t mask = mask_cur;
     mask_cur = mask_nxt;
     if (mask == 0) continue;
@@ -343,9 +356,11 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
 
     // dKV rows of the block for this wave's d-range. A operand = [slot][head] via transposing
     // reads of the [head][slot] buffers: lane l holds slot (l & 31), heads 16 ks + 8 kg .. +7.
+    // destination row of each C row: the kv row (atomic mode) or the staging row (staging mode)
+    const int32_t dst_this = stage ? pos_this + hblk : idx_this;
     int32_t rowi[16];
 #pragma unroll
-    for (int r = 0; r < 16; r++) rowi[r] = __shfl(idx_this, 8 * (r >> 2) + 4 * kg + (r & 3));
+    for (int r = 0; r < 16; r++) rowi[r] = __shfl(dst_this, 8 * (r >> 2) + 4 * kg + (r & 3));
     const int hl = 8 * kg + ((lane & 15) >> 2);
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
@@ -367,12 +382,168 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
       }
       // C layout: lane holds d = w*DW + 32 dt + (lane & 31), slots 8 (r>>2) + 4 kg + (r&3).
       const int d = w * DW + 32 * dt + (lane & 31);
+      if (stage) {
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int t = 8 * (r >> 2) + 4 * kg + (r & 3);
-        if ((mask >> t) & 1ull) unsafeAtomicAdd(acc_b + (int64_t)rowi[r] * D + d, c[r]);
+        for (int r = 0; r < 16; r++) {
+          const int t = 8 * (r >> 2) + 4 * kg + (r & 3);
+          if ((mask >> t) & 1ull) __builtin_nontemporal_store(c[r], stage + (int64_t)rowi[r] * D + d);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int t = 8 * (r >> 2) + 4 * kg + (r & 3);
+          if ((mask >> t) & 1ull) unsafeAtomicAdd(acc_b + (int64_t)rowi[r] * D + d, c[r]);
+        }
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Segmented scatter-add of dKV. Every valid (token, slot) pair gets n_hblk consecutive rows of a
+// staging buffer, grouped by kv row: rank (per-row counter, int atomics) -> exclusive scan of the
+// counts (row offsets) -> pos = offset + rank. The dKV kernel stores each contribution row there
+// with plain stores, and reduce_rows sums each kv row's segment. This moves the payload through
+// the store and streaming-read paths instead of the fp32 atomic units.
+
+// Each kv row has RANK_SUB counters (picked by token), stored sub-major so that the counters of
+// one row sit on different cache lines: a causal workload sends thousands of increments to its
+// first rows, and same-address atomics serialise. Offsets are scanned in (row, sub) order, so a
+// row's staging segment stays contiguous.
+constexpr int RANK_SUB = 16;
+
+__global__ void __launch_bounds__(256)
+rank_kernel(const int32_t* __restrict__ idx, int32_t* __restrict__ count, int32_t* __restrict__ rank,
+            int64_t token0, int64_t n_slots, int64_t S, int64_t S_kv, int topk, int n_hblk, int64_t n_rows) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_slots; i += (int64_t)gridDim.x * 256) {
+    const int64_t slot = token0 * topk + i;
+    const int32_t v = idx[slot];
+    int32_t r = -1;
+    if (slot_in_range(v, S_kv)) {
+      const int64_t token = slot / topk;
+      const int64_t b = token / S;
+      r = atomicAdd(count + (token % RANK_SUB) * n_rows + b * S_kv + v, n_hblk);
+    }
+    rank[i] = r;
+  }
+}
+
+// In place: rank[i] -> offset[(row, sub)] + rank[i] for valid slots (stays -1 otherwise).
+__global__ void __launch_bounds__(256)
+position_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ offset, int32_t* __restrict__ rank,
+                int64_t token0, int64_t n_slots, int64_t S, int64_t S_kv, int topk) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_slots; i += (int64_t)gridDim.x * 256) {
+    const int32_t r = rank[i];
+    if (r < 0) continue;
+    const int64_t slot = token0 * topk + i;
+    const int64_t token = slot / topk;
+    const int64_t b = token / S;
+    rank[i] = offset[(b * S_kv + idx[slot]) * RANK_SUB + token % RANK_SUB] + r;
+  }
+}
+
+// Exclusive scan of n int32 counts into offset[0..n] (offset[n] = total), three passes:
+// per-tile scans of SCAN_TILE elements, a scan of the tile totals, then the tile bases.
+constexpr int SCAN_TILE = 4096;  // 256 threads x 16
+
+__device__ __forceinline__ int32_t block_exclusive_scan_256(int32_t v, int32_t* sh, int32_t* total) {
+  // v: this thread's value; returns the exclusive prefix over the 256 threads of the block.
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sh[w] = x;
+  __syncthreads();
+  int32_t base = 0;
+  for (int i = 0; i < w; i++) base += sh[i];
+  *total = sh[0] + sh[1] + sh[2] + sh[3];
+  __syncthreads();
+  return base + x - v;
+}
+
+// Element e = row * RANK_SUB + sub of the scan reads count[sub * n_rows + row].
+__global__ void __launch_bounds__(256)
+scan_tiles_kernel(const int32_t* __restrict__ in, int32_t* __restrict__ out, int32_t* __restrict__ tile_sum,
+                  int64_t n, int64_t n_rows) {
+  __shared__ int32_t sh[4];
+  const int64_t base = (int64_t)blockIdx.x * SCAN_TILE + threadIdx.x * 16;
+  int32_t v[16];
+  int32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const int64_t e = base + i;
+    v[i] = e < n ? in[(e % RANK_SUB) * n_rows + e / RANK_SUB] : 0;
+    s += v[i];
+  }
+  int32_t total;
+  int32_t run = block_exclusive_scan_256(s, sh, &total);
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    if (base + i < n) out[base + i] = run;
+    run += v[i];
+  }
+  if (threadIdx.x == 0) tile_sum[blockIdx.x] = total;
+}
+
+// Single workgroup: exclusive scan of the tile totals (in place), total into out[n].
+__global__ void __launch_bounds__(256)
+scan_totals_kernel(int32_t* __restrict__ tile_sum, int64_t n_tiles, int32_t* __restrict__ out, int64_t n) {
+  __shared__ int32_t sh[4];
+  int32_t carry = 0;
+  for (int64_t b0 = 0; b0 < n_tiles; b0 += 256) {
+    const int64_t i = b0 + threadIdx.x;
+    const int32_t v = i < n_tiles ? tile_sum[i] : 0;
+    int32_t total;
+    const int32_t ex = block_exclusive_scan_256(v, sh, &total);
+    if (i < n_tiles) tile_sum[i] = carry + ex;
+    carry += total;
+  }
+  if (threadIdx.x == 0) out[n] = carry;
+}
+
+__global__ void __launch_bounds__(256)
+scan_add_kernel(int32_t* __restrict__ out, const int32_t* __restrict__ tile_sum, int64_t n) {
+  const int64_t base = (int64_t)blockIdx.x * SCAN_TILE + threadIdx.x * 16;
+  const int32_t add = tile_sum[blockIdx.x];
+#pragma unroll
+  for (int i = 0; i < 16; i++)
+    if (base + i < n) out[base + i] += add;
+}
+
+// One workgroup per kv row: sum the row's staging segment in fp32 (fixed order), optionally add
+// the running accumulator (earlier token chunks), then write fp32 and/or bf16 output.
+template <int D>
+__global__ void __launch_bounds__(256)
+reduce_rows_kernel(const f32x4* __restrict__ stage, const int32_t* __restrict__ offset,
+                   f32x4* __restrict__ acc, uint2* __restrict__ out_bf16, int accumulate) {
+  // offset is indexed by (row, sub): the row's segment is [offset[row*RANK_SUB], offset[(row+1)*RANK_SUB]).
+  constexpr int F4 = D / 4;         // 16-byte pieces per row
+  constexpr int NG = 256 / F4;      // thread groups, each taking every NG-th contribution
+  static_assert(NG >= 1 && 256 % F4 == 0, "row width");
+  __shared__ f32x4 part[NG][F4];
+  const int64_t row = blockIdx.x;
+  const int g = threadIdx.x / F4, c = threadIdx.x % F4;
+  const int32_t beg = offset[row * RANK_SUB], end = offset[(row + 1) * RANK_SUB];
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, s2 = s0, s3 = s0;
+  int32_t i = beg + g;
+  for (; i + 3 * NG < end; i += 4 * NG) {
+    s0 += __builtin_nontemporal_load(stage + (int64_t)i * F4 + c);
+    s1 += __builtin_nontemporal_load(stage + (int64_t)(i + NG) * F4 + c);
+    s2 += __builtin_nontemporal_load(stage + (int64_t)(i + 2 * NG) * F4 + c);
+    s3 += __builtin_nontemporal_load(stage + (int64_t)(i + 3 * NG) * F4 + c);
+  }
+  for (; i < end; i += NG) s0 += __builtin_nontemporal_load(stage + (int64_t)i * F4 + c);
+  part[g][c] = (s0 + s1) + (s2 + s3);
+  __syncthreads();
+  if (g == 0) {
+    f32x4 t = part[0][c];
+    for (int k = 1; k < NG; k++) t += part[k][c];
+    if (accumulate) t += acc[row * F4 + c];
+    if (acc) acc[row * F4 + c] = t;
+    if (out_bf16) out_bf16[row * F4 + c] = pack4_bf16(t[0], t[1], t[2], t[3]);
   }
 }
 
@@ -411,25 +582,25 @@ hipError_t launch_bwd_postprocess(const float* acc, void* dkv, int64_t n, hipStr
 template <int D, int NW>
 static hipError_t launch_bwd_main_t(const BwdMainArgs& a, int which, hipStream_t st) {
   const int n_hblk = (int)(a.H / (16 * NW));
-  const int n_tokens = (int)(a.B * a.S);
-  const dim3 grid((unsigned)(n_tokens * n_hblk)), block(NW * 64);
   const float sl2 = a.sm_scale * kLog2e;
   if (which & 1) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), grid, block, 0, st, (const uint16_t*)a.q, (const uint16_t*)a.kv,
-                       (const uint16_t*)a.d_o, a.idx, a.lse, a.delta, (uint16_t*)a.dq, (int)a.S, a.S_kv, (int)a.H,
-                       (int)a.topk, a.sm_scale, sl2, n_hblk, n_tokens);
+    const int n_tokens = (int)(a.B * a.S);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3((unsigned)(n_tokens * n_hblk)), dim3(NW * 64), 0, st,
+                       (const uint16_t*)a.q, (const uint16_t*)a.kv, (const uint16_t*)a.d_o, a.idx, a.lse, a.delta,
+                       (uint16_t*)a.dq, (int)a.S, a.S_kv, (int)a.H, (int)a.topk, a.sm_scale, sl2, n_hblk, n_tokens);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (!(which & 2)) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, NW>), grid, block, 0, st, (const uint16_t*)a.q, (const uint16_t*)a.kv,
-                     (const uint16_t*)a.d_o, a.idx, a.lse, a.delta, a.dkv_accum, (int)a.S, a.S_kv, (int)a.H,
-                     (int)a.topk, a.sm_scale, sl2, n_hblk, n_tokens);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, NW>), dim3((unsigned)(a.n_chunk * n_hblk)), dim3(NW * 64), 0, st,
+                     (const uint16_t*)a.q, (const uint16_t*)a.kv, (const uint16_t*)a.d_o, a.idx, a.lse, a.delta,
+                     a.dkv_accum, a.pos, a.stage, (int)a.S, a.S_kv, (int)a.H, (int)a.topk, a.sm_scale, sl2, n_hblk,
+                     (int)a.token0, (int)a.n_chunk);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_main(const BwdMainArgs& a, int which, hipStream_t st) {
-  const int hb = a.H >= 64 ? 64 : (int)a.H;
+  const int hb = bwd_heads_per_wg(a.H);
   if (a.D == 512) {
     if (hb == 64) return launch_bwd_main_t<512, 4>(a, which, st);
     if (hb == 32) return launch_bwd_main_t<512, 2>(a, which, st);
@@ -439,6 +610,53 @@ hipError_t launch_bwd_main(const BwdMainArgs& a, int which, hipStream_t st) {
     if (hb == 16) return launch_bwd_main_t<64, 1>(a, which, st);
   }
   return hipErrorInvalidValue;
+}
+
+static unsigned grid_for(int64_t n, int64_t per_block, int64_t cap = 65536) {
+  int64_t g = (n + per_block - 1) / per_block;
+  if (g > cap) g = cap;
+  return (unsigned)(g < 1 ? 1 : g);
+}
+
+int64_t scan_tiles(int64_t n) { return (n + SCAN_TILE - 1) / SCAN_TILE; }
+int64_t rank_counters(int64_t n_rows) { return n_rows * RANK_SUB; }
+
+hipError_t launch_dkv_prepare(const int32_t* idx, int32_t* count, int32_t* offset, int32_t* tile_sum, int32_t* pos,
+                              int64_t B, int64_t S, int64_t S_kv, int64_t topk, int n_hblk, int64_t token0,
+                              int64_t n_chunk, hipStream_t st) {
+  const int64_t n_rows = B * S_kv;
+  const int64_t n_cnt = n_rows * RANK_SUB;
+  const int64_t n_slots = n_chunk * topk;
+  hipError_t e = launch_fill_zero_f32((float*)count, (n_cnt + 3) / 4 * 4, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(rank_kernel, dim3(grid_for(n_slots, 256)), dim3(256), 0, st, idx, count, pos, token0, n_slots, S,
+                     S_kv, (int)topk, n_hblk, n_rows);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t tiles = scan_tiles(n_cnt);
+  hipLaunchKernelGGL(scan_tiles_kernel, dim3((unsigned)tiles), dim3(256), 0, st, (const int32_t*)count, offset,
+                     tile_sum, n_cnt, n_rows);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_totals_kernel, dim3(1), dim3(256), 0, st, tile_sum, tiles, offset, n_cnt);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_add_kernel, dim3((unsigned)tiles), dim3(256), 0, st, offset, (const int32_t*)tile_sum,
+                     n_cnt);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(position_kernel, dim3(grid_for(n_slots, 256)), dim3(256), 0, st, idx, (const int32_t*)offset,
+                     pos, token0, n_slots, S, S_kv, (int)topk);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_rows(const float* stage, const int32_t* offset, float* acc, void* out_bf16, int accumulate,
+                              int64_t n_rows, int64_t D, hipStream_t st) {
+  if (D == 512)
+    hipLaunchKernelGGL(reduce_rows_kernel<512>, dim3((unsigned)n_rows), dim3(256), 0, st, (const f32x4*)stage,
+                       offset, (f32x4*)acc, (uint2*)out_bf16, accumulate);
+  else if (D == 64)
+    hipLaunchKernelGGL(reduce_rows_kernel<64>, dim3((unsigned)n_rows), dim3(256), 0, st, (const f32x4*)stage,
+                       offset, (f32x4*)acc, (uint2*)out_bf16, accumulate);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace smqa

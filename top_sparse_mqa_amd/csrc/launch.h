@@ -26,17 +26,36 @@ struct BwdMainArgs {
   const float* lse;
   const float* delta;
   void* dq;
-  float* dkv_accum;
+  float* dkv_accum;       // atomic mode: pre-zeroed fp32 accumulator [B,S_kv,D]
+  const int32_t* pos;     // staging mode: staging row of each slot of the chunk (-1 if masked)
+  float* stage;           // staging mode: contribution rows; nullptr selects atomic mode
   int64_t B, S, S_kv, H, D, topk;
   float sm_scale;
+  int64_t token0;         // first token of the chunk (dKV kernel)
+  int64_t n_chunk;        // tokens in the chunk (dKV kernel)
 };
+
+// Heads handled by one backward workgroup, and workgroups per token.
+inline int bwd_heads_per_wg(int64_t H) { return H >= 64 ? 64 : (int)H; }
+inline int bwd_hblocks(int64_t H) { return (int)(H / bwd_heads_per_wg(H)); }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_preprocess(const void* o, const void* d_o, float* delta, int64_t rows, int64_t D,
                                  hipStream_t st);
 hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t st);
-// which: 1 = dQ kernel, 2 = dKV scatter kernel, 3 = both.
+// which: 1 = dQ kernel (all tokens), 2 = dKV kernel (chunk; atomic or staging mode), 3 = both.
 hipError_t launch_bwd_main(const BwdMainArgs& a, int which, hipStream_t st);
+// Staging-row assignment for the tokens [token0, token0 + n_chunk): clears count, ranks every valid
+// slot within its kv row, scans the counts into offset[0..n_rows], and turns ranks into rows (pos).
+hipError_t launch_dkv_prepare(const int32_t* idx, int32_t* count, int32_t* offset, int32_t* tile_sum, int32_t* pos,
+                              int64_t B, int64_t S, int64_t S_kv, int64_t topk, int n_hblk, int64_t token0,
+                              int64_t n_chunk, hipStream_t st);
+int64_t scan_tiles(int64_t n);
+// Number of rank counters (and scanned offsets, minus the final total) for n_rows kv rows.
+int64_t rank_counters(int64_t n_rows);
+// Per kv row: sum of its staging segment (+ acc if accumulate); writes acc (fp32) and/or out (bf16).
+hipError_t launch_reduce_rows(const float* stage, const int32_t* offset, float* acc, void* out_bf16,
+                              int accumulate, int64_t n_rows, int64_t D, hipStream_t st);
 hipError_t launch_bwd_postprocess(const float* acc, void* dkv, int64_t n, hipStream_t st);
 
 }  // namespace smqa
