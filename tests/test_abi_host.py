@@ -81,12 +81,13 @@ def test_workspace_bytes(lib):
     n_cnt = 16 * B * S_kv  # sixteen rank counters per kv row
     fixed = r256((n_cnt + 4) * 4) + r256((n_cnt + 1) * 4) + r256(((n_cnt + 4095) // 4096) * 4)
     full = lib.sparse_mqa_bwd_workspace_bytes(B, S, S_kv, H, D, K)
-    assert full == r256(B * S * H * 4) + fixed + r256(B * S * K * 4) + r256(B * S * K * D * 4) + 512
+    # staging: one row per slot plus one spare row per token (masked slots' stores land there)
+    assert full == r256(B * S * H * 4) + fixed + r256(B * S * K * 4) + r256(B * S * (K + 1) * D * 4) + 512
     low = lib.sparse_mqa_bwd_workspace_min_bytes(B, S, S_kv, H, D, K)
-    assert low == r256(B * S * H * 4) + fixed + r256(B * S_kv * D * 4) + r256(K * 4) + r256(K * D * 4) + 512
-    # H = 128 runs two 64-head workgroups per token: two staging rows per valid slot
+    assert low == r256(B * S * H * 4) + fixed + r256(B * S_kv * D * 4) + r256(K * 4) + r256((K + 1) * D * 4) + 512
+    # H = 128 runs two 64-head workgroups per token: two staging rows per slot (and two spare rows)
     assert (lib.sparse_mqa_bwd_workspace_bytes(1, 8, 16, 128, 512, 4)
-            - lib.sparse_mqa_bwd_workspace_bytes(1, 8, 16, 64, 512, 4)) == r256(8 * 4 * 2 * 512 * 4) - r256(8 * 4 * 512 * 4) + r256(8 * 128 * 4) - r256(8 * 64 * 4)
+            - lib.sparse_mqa_bwd_workspace_bytes(1, 8, 16, 64, 512, 4)) == r256(8 * 5 * 2 * 512 * 4) - r256(8 * 5 * 512 * 4) + r256(8 * 128 * 4) - r256(8 * 64 * 4)
     assert lib.sparse_mqa_bwd_workspace_bytes(0, 1, 1, 16, 64, 1) == 0
     assert lib.sparse_mqa_bwd_workspace_min_bytes(1, 1, 1, 48, 512, 1) == 0
 

@@ -23,6 +23,9 @@ HIPCC_FLAGS = [
     "-fPIC",
     # packed fp32 VALU ops are kept out of the generated code on purpose
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the accumulator-register form made the register allocator
+    # shuttle operands and accumulators between the two register files inside the hot loops
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -122,8 +122,10 @@ size_t fixed_dkv_bytes(int64_t B, int64_t S_kv) {
          round256((size_t)smqa::scan_tiles(n_cnt) * 4);
 }
 
+// Per token: its slots' positions, one staging row per slot and head block, and one spare row per
+// head block that takes the stores of the token's masked slots.
 size_t per_token_dkv_bytes(int64_t H, int64_t D, int64_t topk) {
-  return (size_t)topk * 4 + (size_t)topk * smqa::bwd_hblocks(H) * D * 4;
+  return (size_t)topk * 4 + (size_t)(topk + 1) * smqa::bwd_hblocks(H) * D * 4;
 }
 
 // Lay out the dKV part of the workspace starting at `base`; false if `bytes` cannot hold even one
@@ -139,8 +141,10 @@ bool plan_dkv(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t 
   p->tiles = o;
   o += round256((size_t)smqa::scan_tiles(n_cnt) * 4);
   const size_t per_tok = per_token_dkv_bytes(H, D, topk);
+  // staging row indices are 32-bit
+  const int64_t max_chunk = (int64_t)(INT32_MAX / ((topk + 1) * smqa::bwd_hblocks(H)));
   // one pass over all tokens if it fits, else token chunks with an fp32 running sum
-  if (o + per_tok * tokens + 512 <= bytes) {
+  if (o + per_tok * tokens + 512 <= bytes && tokens <= max_chunk) {
     p->chunk = tokens;
     p->use_acc = false;
     p->acc = 0;
@@ -151,11 +155,12 @@ bool plan_dkv(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t 
     if (o + per_tok + 512 > bytes) return false;
     p->chunk = (int64_t)((bytes - o - 512) / per_tok);
     if (p->chunk > tokens) p->chunk = tokens;
+    if (p->chunk > max_chunk) p->chunk = max_chunk;
   }
   p->pos = o;
   o += round256((size_t)p->chunk * topk * 4);
   p->stage = o;
-  o += round256((size_t)p->chunk * topk * smqa::bwd_hblocks(H) * D * 4);
+  o += round256((size_t)p->chunk * (topk + 1) * smqa::bwd_hblocks(H) * D * 4);
   p->end = o;
   return o <= bytes;
 }
@@ -210,13 +215,13 @@ extern "C" {
 size_t sparse_mqa_bwd_workspace_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk) {
   if (!sizes_ok(B, S, S_kv, H, D, topk)) return 0;
   return delta_bytes(B, S, H) + fixed_dkv_bytes(B, S_kv) + round256((size_t)(B * S) * topk * 4) +
-         round256((size_t)(B * S) * topk * smqa::bwd_hblocks(H) * D * 4) + 512;
+         round256((size_t)(B * S) * (topk + 1) * smqa::bwd_hblocks(H) * D * 4) + 512;
 }
 
 size_t sparse_mqa_bwd_workspace_min_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk) {
   if (!sizes_ok(B, S, S_kv, H, D, topk)) return 0;
   return delta_bytes(B, S, H) + fixed_dkv_bytes(B, S_kv) + round256((size_t)(B * S_kv) * D * 4) +
-         round256((size_t)topk * 4) + round256((size_t)topk * smqa::bwd_hblocks(H) * D * 4) + 512;
+         round256((size_t)topk * 4) + round256((size_t)(topk + 1) * smqa::bwd_hblocks(H) * D * 4) + 512;
 }
 
 int sparse_mqa_bwd_preprocess(const void* o, const void* d_o, float* delta, int64_t B, int64_t S, int64_t H,

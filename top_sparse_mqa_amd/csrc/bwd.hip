@@ -5,7 +5,8 @@
 //   bwd_dq       per token: S^T, dP^T, P, dS, dQ^T += K^T dS^T      (bf16 MFMA 16x16x32)
 //   bwd_dkv      per token: S^T, dP^T, P, dS, then dKV rows of the block
 //                = (sm_scale dS)^T Q + P^T dO over all heads          (bf16 MFMA 32x32x16)
-//                and a fp32 atomic add of each valid row into the accumulator. P and
+//                and either a plain store of each valid row into its staging row (segmented
+//                scatter-add, below) or a fp32 atomic add into the accumulator. P and
 //                sm_scale*dS enter this product as hi + lo bf16 pairs (two MFMAs each): a
 //                kv row sums thousands of heavily cancelling terms, and single-bf16
 //                coefficients leave errors of several percent of the result there.
@@ -80,45 +81,96 @@ struct BwdCommon {
   static constexpr int TB = T * ROWB;
   static constexpr int RPI = 1024 / ROWB;
   static constexpr int NINSTR = T / RPI;
+  static constexpr int KS = D / 32;              // k-steps of the score products
+  static constexpr int KSJ = KS < 4 ? KS : 4;    // distinct per-lane score-fragment offsets
+  static constexpr int NDQ = D / 16;             // 16-wide d tiles of dQ
+  static constexpr int DQJ = NDQ < 8 ? NDQ : 8;  // distinct per-lane dQ-fragment offsets
 };
 
+// Tile rows are gathered with direct-to-LDS loads. With 1 KiB rows (D = 512) one instruction
+// moves one row: its kv row index is read from the index lane into a scalar register and the lane
+// offset carries the row's chunk swizzle; smaller rows take several rows per instruction.
 template <int D, int NW>
-__device__ __forceinline__ void bwd_issue_tile(const char* kv_b, int32_t my_idx, uint64_t mask, char* tile,
-                                               int lane, int w) {
+__device__ __forceinline__ void bwd_issue_tile(const char* kv_b, int64_t S_kv, int32_t my_idx, uint64_t mask,
+                                               char* tile, int lane, int wu) {
   using C = BwdCommon<D, NW>;
-  for (int ins = w; ins < C::NINSTR; ins += NW) {
-    const int r = ins * C::RPI + lane / C::CPR;
-    const int p = lane % C::CPR;
-    const int c = p ^ (bwd_swz(r) & (C::CPR - 1));
-    const int32_t ri = __shfl(my_idx, r);
-    const bool v = (mask >> r) & 1ull;
-    const char* src = v ? kv_b + (int64_t)ri * C::ROWB + c * 16 : (const char*)g_zero_row_bwd + c * 16;
-    dma16(src, tile + ins * 1024);
-  }
-}
-
-// S^T and dP^T of one 32-slot block for this wave's 16 heads: C layout lane l holds head
-// (l & 15) and slots 16 mt + 4 (l>>4) + r.
-template <int D>
-__device__ __forceinline__ void bwd_scores(const char* tile, const bf16x8* qb, const bf16x8* dob, int lane,
-                                           f32x4* sacc, f32x4* dpacc) {
-  const int g = lane >> 4;
+  if constexpr (C::RPI == 1) {
+    // kv rows through a buffer resource (row offset in the scalar offset), masked rows from the
+    // zero row through a second one
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv_b, (int)(S_kv * C::ROWB));
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(g_zero_row_bwd, C::ROWB);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
-  for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-    for (int r = 0; r < 4; r++) { sacc[mt][r] = 0.f; dpacc[mt][r] = 0.f; }
-#pragma unroll
-  for (int ks = 0; ks < D / 32; ks++) {
-#pragma unroll
-    for (int mt = 0; mt < 2; mt++) {
-      const bf16x8 a = lds_load16(tile + bwd_off<D>(16 * mt + (lane & 15), 4 * ks + g));
-      sacc[mt] = mfma16(a, qb[ks], sacc[mt]);
-      dpacc[mt] = mfma16(a, dob[ks], dpacc[mt]);
+    for (int i = 0; i < C::T / NW; i++) {
+      const int r = wu + NW * i;
+      const int32_t ri = __builtin_amdgcn_readlane(my_idx, r);
+      const uint32_t voff = (uint32_t)((ln ^ (bwd_swz(r) & (C::CPR - 1))) << 4);
+      if ((mask >> r) & 1ull) dma16_buf(rk, voff, (uint32_t)ri * C::ROWB, tile + r * C::ROWB);
+      else dma16_buf(rz, voff, 0, tile + r * C::ROWB);
+    }
+  } else {
+    for (int ins = wu; ins < C::NINSTR; ins += NW) {
+      const int r = ins * C::RPI + lane / C::CPR;
+      const int p = lane % C::CPR;
+      const int c = p ^ (bwd_swz(r) & (C::CPR - 1));
+      const int32_t ri = __shfl(my_idx, r);
+      const bool v = (mask >> r) & 1ull;
+      const char* src = v ? kv_b + (int64_t)ri * C::ROWB + c * 16 : (const char*)g_zero_row_bwd + c * 16;
+      dma16(src, tile + ins * 1024);
     }
   }
 }
 
+// Per-lane byte offsets of the score A fragments inside a tile: fragment (ks, mt) = rows
+// 16 mt + (lane & 15), chunk 4 ks + (lane >> 4). The swizzle only touches the low four chunk
+// bits, so fragments 4 k-steps apart differ by 256 bytes and mt by 16 rows (instruction offsets).
+template <int D>
+__device__ __forceinline__ void bwd_score_offsets(int lane, int* sc_off) {
+  using C = BwdCommon<D, 1>;
+  const int row = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < C::KSJ; j++) sc_off[j] = row * C::ROWB + (((4 * j + g) ^ (bwd_swz(row) & (C::CPR - 1))) << 4);
+}
+
+// S^T and dP^T of one 32-slot block for this wave's 16 heads (C layout: lane l holds head
+// (l & 15) and slots 16 mt + 4 (l>>4) + r). Fragment i is (ks, mt) = (i / 2, i % 2). PF fragment
+// reads run ahead of the MFMAs that use them; every stage is fenced so the scheduler cannot pull
+// a read down to its use, which would expose the full LDS latency on each MFMA.
+template <int D, int PF>
+__device__ __forceinline__ void bwd_scores(const char* tile, const int* sc_off, const bf16x8* qb,
+                                           const bf16x8* dob, f32x4* sacc, f32x4* dpacc) {
+  using C = BwdCommon<D, 1>;
+  constexpr int NF = 2 * C::KS;
+  constexpr int PFE = PF < NF ? PF : NF;  // reads in flight
+  constexpr int NB = PFE + 1;
+  auto frag = [&](int i) {
+    const int ks = i >> 1, mt = i & 1;
+    return lds_load16(tile + sc_off[ks % C::KSJ] + 256 * (ks / C::KSJ) + mt * 16 * C::ROWB);
+  };
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) { sacc[mt][r] = 0.f; dpacc[mt][r] = 0.f; }
+  bf16x8 fr[NB];
+#pragma unroll
+  for (int i = 0; i < PFE; i++) fr[i] = frag(i);
+#pragma unroll
+  for (int i = 0; i < NF; i++) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + PFE < NF) fr[(i + PFE) % NB] = frag(i + PFE);
+    const int ks = i >> 1, mt = i & 1;
+    sacc[mt] = mfma16(fr[i % NB], qb[ks], sacc[mt]);
+    dpacc[mt] = mfma16(fr[i % NB], dob[ks], dpacc[mt]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---------------------------------------------------------------------------------------------
+// The two tile buffers are distinct LDS arrays and the block loop is unrolled by two, so every
+// read names the buffer it reads at compile time. The compiler can then tell a read of one buffer
+// from the gather in flight into the other; with a single array it makes each transposing read
+// wait for all outstanding gathers.
 template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64)
 bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ dout,
@@ -127,9 +179,13 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
               int n_hblk, int n_tokens) {
   using C = BwdCommon<D, NW>;
   constexpr int T = C::T;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::TB];
+  constexpr int PF = 6;
+  constexpr int PFQ = C::NDQ < 6 ? C::NDQ : 6, NBQ = PFQ + 1;  // dQ fragment reads in flight
+  __shared__ __attribute__((aligned(16))) char tile0[C::TB];
+  __shared__ __attribute__((aligned(16))) char tile1[C::TB];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int g = lane >> 4;
   const int item = blockIdx.x;
   const int64_t token = (int64_t)n_tokens - 1 - item / n_hblk;
@@ -137,23 +193,39 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
   const int64_t b = token / S;
   const int head = hblk * 16 * NW + 16 * w + (lane & 15);
 
-  bf16x8 qb[D / 32], dob[D / 32];
+  bf16x8 qb[C::KS], dob[C::KS];
   {
     const int64_t off = (token * H + head) * (int64_t)D + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ks++) {
+    for (int ks = 0; ks < C::KS; ks++) {
       qb[ks] = load_bf16x8(q + off + 32 * ks);
       dob[ks] = load_bf16x8(dout + off + 32 * ks);
+    }
+    // after all loads are issued: pinning waits for the value
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ks++) {
+      keep_in_agpr(qb[ks]);
+      keep_in_agpr(dob[ks]);
     }
   }
   const float lse_h = lse[token * H + head];
   const float delta_h = delta[token * H + head];
 
-  f32x4 dqacc[D / 16];
+  f32x4 dqacc[C::NDQ];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; dt++)
+  for (int dt = 0; dt < C::NDQ; dt++)
 #pragma unroll
     for (int r = 0; r < 4; r++) dqacc[dt][r] = 0.f;
+
+  int sc_off[C::KSJ];
+  bwd_score_offsets<D>(lane, sc_off);
+  // dQ^T A fragments (16 d x 32 slots, read transposed): lane rows t0 and t0 + 16 of the tile,
+  // d = 16 dt + 4 (lane & 3) -> chunk 2 dt + ((lane & 3) >> 1), byte 8 (lane & 1) of the chunk.
+  const int t0 = 4 * g + ((lane & 15) >> 2);
+  int dq_off[C::DQJ];
+#pragma unroll
+  for (int j = 0; j < C::DQJ; j++)
+    dq_off[j] = t0 * C::ROWB + (((2 * j + ((lane & 3) >> 1)) ^ (bwd_swz(t0) & (C::CPR - 1))) << 4) + 8 * (lane & 1);
 
   const int nblk = (topk + T - 1) / T;
   const int32_t* idx_tok = idx + token * (int64_t)topk;
@@ -165,27 +237,38 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
 
   int32_t idx_cur = load_idx(0);
   uint64_t mask_cur = __ballot(slot_in_range(idx_cur, S_kv));
-  if (mask_cur) bwd_issue_tile<D, NW>(kv_b, idx_cur, mask_cur, smem, lane, w);
+  if (mask_cur) bwd_issue_tile<D, NW>(kv_b, S_kv, idx_cur, mask_cur, tile0, lane, wu);
   int32_t idx_nxt = nblk > 1 ? load_idx(1) : -1;
 
-  for (int blk = 0; blk < nblk; blk++) {
-    const int buf = blk & 1;
+  auto block = [&](auto buf_tag, int blk) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    char* tile = BUF ? tile1 : tile0;
+    char* other = BUF ? tile0 : tile1;
     wait_all_mem();
     __syncthreads();
     uint64_t mask_nxt = 0;
     if (blk + 1 < nblk) {
       mask_nxt = __ballot(slot_in_range(idx_nxt, S_kv));
-      if (mask_nxt) bwd_issue_tile<D, NW>(kv_b, idx_nxt, mask_nxt, smem + (buf ^ 1) * C::TB, lane, w);
+      if (mask_nxt) bwd_issue_tile<D, NW>(kv_b, S_kv, idx_nxt, mask_nxt, other, lane, wu);
     }
     idx_cur = idx_nxt;
     idx_nxt = blk + 2 < nblk ? load_idx(blk + 2) : -1;
     const uint64_t mask = mask_cur;
     mask_cur = mask_nxt;
-    if (mask == 0) continue;
+    if (mask == 0) return;
 
-    const char* tile = smem + buf * C::TB;
     f32x4 sacc[2], dpacc[2];
-    bwd_scores<D>(tile, qb, dob, lane, sacc, dpacc);
+    bwd_scores<D, PF>(tile, sc_off, qb, dob, sacc, dpacc);
+
+    auto dfrag = [&](int dt) {
+      const char* p = tile + dq_off[dt % C::DQJ] + 256 * (dt / C::DQJ);
+      return join_tr(lds_load_tr(p), lds_load_tr(p + 16 * C::ROWB));
+    };
+    // the first dQ fragments are read while the softmax below runs
+    bf16x8 fq[NBQ];
+#pragma unroll
+    for (int i = 0; i < PFQ; i++) fq[i] = dfrag(i);
+
     // dS as the B operand of dQ^T = K^T dS^T: element e <-> slot 4g + e (e < 4), 16 + 4g + e - 4.
     bf16x8 dsb;
 #pragma unroll
@@ -196,21 +279,23 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
         const float p = ((mask >> t) & 1ull) ? fast_exp2(sacc[mt][r] * scale_log2 - lse_h) : 0.f;
         dsb[4 * mt + r] = (__bf16)(p * (dpacc[mt][r] - delta_h));
       }
-    const int t0 = 4 * g + ((lane & 15) >> 2);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; dt++) {
-      const int d = 16 * dt + 4 * (lane & 3);
-      const int hoff = (d & 4) ? 8 : 0;
-      const s16x4 lo = lds_load_tr(tile + bwd_off<D>(t0, d >> 3) + hoff);
-      const s16x4 hi = lds_load_tr(tile + bwd_off<D>(t0 + 16, d >> 3) + hoff);
-      dqacc[dt] = mfma16(join_tr(lo, hi), dsb, dqacc[dt]);
+    for (int dt = 0; dt < C::NDQ; dt++) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (dt + PFQ < C::NDQ) fq[(dt + PFQ) % NBQ] = dfrag(dt + PFQ);
+      dqacc[dt] = mfma16(fq[dt % NBQ], dsb, dqacc[dt]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int blk = 0; blk < nblk; blk += 2) {
+    block(IntTag<0>{}, blk);
+    if (blk + 1 < nblk) block(IntTag<1>{}, blk + 1);
   }
 
   // dQ^T C layout: lane holds head (lane & 15), d = 16 dt + 4 g + r.
   uint16_t* dqrow = dq + (token * H + head) * (int64_t)D;
 #pragma unroll
-  for (int dt = 0; dt < D / 16; dt++)
+  for (int dt = 0; dt < C::NDQ; dt++)
     *(uint2*)(dqrow + 16 * dt + 4 * g) = pack4_bf16(dqacc[dt][0] * sm_scale, dqacc[dt][1] * sm_scale,
                                                     dqacc[dt][2] * sm_scale, dqacc[dt][3] * sm_scale);
 }
@@ -225,19 +310,22 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
                int token0, int n_tokens) {
   using C = BwdCommon<D, NW>;
   constexpr int T = C::T;
+  constexpr int PF = 6;
   constexpr int HB = 16 * NW;   // heads of this workgroup
   constexpr int DW = D / NW;    // d-columns of dKV owned by one wave
-  constexpr int NDT = DW / 32;
-  constexpr int KS = HB / 16;   // 16-head k-steps of the dKV product
-  static_assert(NDT >= 1, "each wave needs at least one 32-wide d tile");
+  constexpr int NDT = DW / 32;  // 32-wide d tiles of one wave
+  constexpr int DG = NDT < 4 ? NDT : 4;  // d tiles accumulated together
+  constexpr int KH = HB / 16;   // 16-head k-steps of the dKV product
+  static_assert(NDT >= 1 && NDT % DG == 0, "each wave needs whole groups of 32-wide d tiles");
   constexpr int SB = HB * T * 2;  // bytes of one [HB][T] bf16 buffer
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::TB + 4 * SB];
-  char* dsbuf = smem + 2 * C::TB;  // hi parts
-  char* pbuf = dsbuf + SB;
-  char* dslo = pbuf + SB;          // lo parts: x - float(bf16(x)), rounded to bf16
-  char* plo = dslo + SB;
+  __shared__ __attribute__((aligned(16))) char tile0[C::TB];
+  __shared__ __attribute__((aligned(16))) char tile1[C::TB];
+  // P / sm_scale*dS as hi and lo bf16 parts (lo = x - float(bf16(x)), rounded): buffers
+  // 0 = dS hi, 1 = dS lo, 2 = P hi, 3 = P lo, each [head][slot].
+  __shared__ __attribute__((aligned(16))) char pds[4 * SB];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int g = lane >> 4, kg = lane >> 5;
   const int item = blockIdx.x;
   const int64_t ctok = (int64_t)n_tokens - 1 - item / n_hblk;  // token within the chunk
@@ -251,42 +339,69 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
 
   // (1) Q and dO with heads along k, as B operands of dKV = (sm_scale dS)^T Q + P^T dO:
   // lane l holds d = w*DW + 32 dt + (l & 31) and heads 16 ks + 8 kg .. +7, read with transposing
-  // LDS loads from a row-major [HB][D] staging copy (the tile buffers are free at this point).
-  static_assert(HB * D * 2 <= 2 * C::TB, "staging copy must fit the tile buffers");
-  bf16x8 qv[NDT][KS], dov[NDT][KS];
+  // LDS loads from a row-major [HB][D] staging copy held in the two tile buffers (heads
+  // 0 .. HH-1 in tile0, the rest in tile1; the buffers are free at this point).
+  constexpr int HH = C::TB / (D * 2);  // heads per tile buffer
+  static_assert(HB <= 2 * HH && HH % 16 == 0, "staging copy must fit the tile buffers");
+  bf16x8 qv[NDT][KH], dov[NDT][KH];
   {
     const int64_t base = (token * H + (int64_t)hblk * HB) * D;
     for (int pass = 0; pass < 2; pass++) {
       const uint16_t* src = (pass == 0 ? q : dout) + base;
-      for (int i = threadIdx.x; i < HB * D / 8; i += NW * 64)
-        *(uint4*)(smem + 16 * i) = *(const uint4*)(src + 8 * i);
+      for (int i = threadIdx.x; i < HB * D / 8; i += NW * 64) {
+        const int h = i / (D / 8);
+        char* dst = (h < HH ? tile0 + 16 * i : tile1 + 16 * (i - HH * (D / 8)));
+        *(uint4*)dst = *(const uint4*)(src + 8 * i);
+      }
       __syncthreads();
 #pragma unroll
       for (int dt = 0; dt < NDT; dt++)
 #pragma unroll
-        for (int ks = 0; ks < KS; ks++) {
-          const int h0 = 16 * ks + 8 * kg + ((lane & 15) >> 2);
+        for (int ks = 0; ks < KH; ks++) {
+          const int hb0 = 16 * ks;  // first head of the k-step: all 16 sit in one buffer
+          const char* sb = hb0 < HH ? tile0 : tile1;
+          const int h0 = hb0 % HH + 8 * kg + ((lane & 15) >> 2);
           const int d = w * DW + 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-          const s16x4 lo = lds_load_tr(smem + (h0 * D + d) * 2);
-          const s16x4 hi = lds_load_tr(smem + ((h0 + 4) * D + d) * 2);
+          const s16x4 lo = lds_load_tr(sb + (h0 * D + d) * 2);
+          const s16x4 hi = lds_load_tr(sb + ((h0 + 4) * D + d) * 2);
           if (pass == 0) qv[dt][ks] = join_tr(lo, hi);
           else dov[dt][ks] = join_tr(lo, hi);
         }
       __syncthreads();
     }
+#pragma unroll
+    for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+      for (int ks = 0; ks < KH; ks++) {
+        keep_in_agpr(qv[dt][ks]);
+        keep_in_agpr(dov[dt][ks]);
+      }
   }
   // (2) Q and dO with d along k, as B operands of S^T and dP^T (this wave's 16 heads).
-  bf16x8 qb[D / 32], dob[D / 32];
+  bf16x8 qb[C::KS], dob[C::KS];
   {
     const int64_t off = (token * H + head) * (int64_t)D + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ks++) {
+    for (int ks = 0; ks < C::KS; ks++) {
       qb[ks] = load_bf16x8(q + off + 32 * ks);
       dob[ks] = load_bf16x8(dout + off + 32 * ks);
+    }
+    // after all loads are issued: pinning waits for the value
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ks++) {
+      keep_in_agpr(qb[ks]);
+      keep_in_agpr(dob[ks]);
     }
   }
   const float lse_h = lse[token * H + head];
   const float delta_h = delta[token * H + head];
+
+  int sc_off[C::KSJ];
+  bwd_score_offsets<D>(lane, sc_off);
+  // P/dS writes: head hrow, slots 16 mt + 4 g .. +3 (8 bytes). Reads (A operand of dKV): lane l
+  // gets slot (l & 31) and heads 16 ks + 8 kg .. +7 from two transposing reads 4 heads apart.
+  const int pw_off = (hrow * T + 4 * g) * 2;
+  const int pr_off = ((8 * kg + ((lane & 15) >> 2)) * T + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
   const int nblk = (topk + T - 1) / T;
   const int32_t* idx_tok = idx + token * (int64_t)topk;
@@ -305,17 +420,21 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
   int32_t pos_nxt = nblk > 1 ? load_pos(1) : -1;
   int32_t idx_cur = load_idx(0);
   uint64_t mask_cur = __ballot(slot_in_range(idx_cur, S_kv));
-  if (mask_cur) bwd_issue_tile<D, NW>(kv_b, idx_cur, mask_cur, smem, lane, w);
+  if (mask_cur) bwd_issue_tile<D, NW>(kv_b, S_kv, idx_cur, mask_cur, tile0, lane, wu);
   int32_t idx_nxt = nblk > 1 ? load_idx(1) : -1;
+  wait_all_mem();
 
-  for (int blk = 0; blk < nblk; blk++) {
-    const int buf = blk & 1;
-    wait_all_mem();
-    __syncthreads();  // tile ready; dsbuf / pbuf of the previous block fully consumed
+  // Each wave waits for its own part of tile blk + 1 right before it stores the rows of tile blk,
+  // so the barrier at the top of the next block finds the tile complete without draining stores.
+  auto block = [&](auto buf_tag, int blk) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    const char* tile = BUF ? tile1 : tile0;
+    char* other = BUF ? tile0 : tile1;
+    __syncthreads();  // tile blk complete; the P/dS buffers of the previous block fully consumed
     uint64_t mask_nxt = 0;
     if (blk + 1 < nblk) {
       mask_nxt = __ballot(slot_in_range(idx_nxt, S_kv));
-      if (mask_nxt) bwd_issue_tile<D, NW>(kv_b, idx_nxt, mask_nxt, smem + (buf ^ 1) * C::TB, lane, w);
+      if (mask_nxt) bwd_issue_tile<D, NW>(kv_b, S_kv, idx_nxt, mask_nxt, other, lane, wu);
     }
     const int32_t idx_this = idx_cur;
     idx_cur = idx_nxt;
@@ -325,77 +444,103 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
     pos_nxt = blk + 2 < nblk ? load_pos(blk + 2) : -1;
     const uint64_t mask = mask_cur;
     mask_cur = mask_nxt;
-    if (mask == 0) continue;
+    if (mask == 0) {
+      wait_all_mem();
+      return;
+    }
 
-    const char* tile = smem + buf * C::TB;
     f32x4 sacc[2], dpacc[2];
-    bwd_scores<D>(tile, qb, dob, lane, sacc, dpacc);
-    // P and sm_scale*dS, stored [head][slot] in bf16 (four consecutive slots per lane).
+    bwd_scores<D, PF>(tile, sc_off, qb, dob, sacc, dpacc);
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) {
-      float p[4], ds[4];
+      float p[4], ds[4], plr[4], dslr[4];
 #pragma unroll
       for (int r = 0; r < 4; r++) {
         const int t = 16 * mt + 4 * g + r;
         p[r] = ((mask >> t) & 1ull) ? fast_exp2(sacc[mt][r] * scale_log2 - lse_h) : 0.f;
         ds[r] = sm_scale * p[r] * (dpacc[mt][r] - delta_h);
-      }
-      float plr[4], dslr[4];
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
         plr[r] = p[r] - (float)(__bf16)p[r];
         dslr[r] = ds[r] - (float)(__bf16)ds[r];
       }
-      const int off = (hrow * T + 16 * mt + 4 * g) * 2;
-      *(uint2*)(pbuf + off) = pack4_bf16(p[0], p[1], p[2], p[3]);
-      *(uint2*)(dsbuf + off) = pack4_bf16(ds[0], ds[1], ds[2], ds[3]);
-      *(uint2*)(plo + off) = pack4_bf16(plr[0], plr[1], plr[2], plr[3]);
-      *(uint2*)(dslo + off) = pack4_bf16(dslr[0], dslr[1], dslr[2], dslr[3]);
+      char* wp = pds + pw_off + 32 * mt;
+      *(uint2*)(wp) = pack4_bf16(ds[0], ds[1], ds[2], ds[3]);
+      *(uint2*)(wp + SB) = pack4_bf16(dslr[0], dslr[1], dslr[2], dslr[3]);
+      *(uint2*)(wp + 2 * SB) = pack4_bf16(p[0], p[1], p[2], p[3]);
+      *(uint2*)(wp + 3 * SB) = pack4_bf16(plr[0], plr[1], plr[2], plr[3]);
     }
     __syncthreads();
 
-    // dKV rows of the block for this wave's d-range. A operand = [slot][head] via transposing
-    // reads of the [head][slot] buffers: lane l holds slot (l & 31), heads 16 ks + 8 kg .. +7.
-    // destination row of each C row: the kv row (atomic mode) or the staging row (staging mode)
-    const int32_t dst_this = stage ? pos_this + hblk : idx_this;
+    // dKV[slot, d] for this wave's d-range, DG tiles of 32 d at a time:
+    //   dS_hi^T Q + dS_lo^T Q + P_hi^T dO + P_lo^T dO, k over the block's heads.
+    // C layout: lane holds d = w*DW + 32 dt + (lane & 31), slots 8 (r>>2) + 4 kg + (r & 3); each
+    // store instruction then writes two whole 128-byte row segments.
+    // staging mode: masked slots store into this workgroup's spare row (after all staging rows of
+    // the chunk), so the stores need no per-slot branches
+    const int32_t spare = (n_tokens * topk + (int32_t)ctok) * n_hblk + hblk;
+    const int32_t dst_this = stage ? (slot_in_range(idx_this, S_kv) ? pos_this + hblk : spare) : idx_this;
     int32_t rowi[16];
 #pragma unroll
     for (int r = 0; r < 16; r++) rowi[r] = __shfl(dst_this, 8 * (r >> 2) + 4 * kg + (r & 3));
-    const int hl = 8 * kg + ((lane & 15) >> 2);
-    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    float* outb = (stage ? stage : acc_b) + w * DW + (lane & 31);
+    auto afrag = [&](int ks, int m) {
+      const char* p = pds + m * SB + pr_off + ks * 16 * T * 2;
+      return join_tr(lds_load_tr(p), lds_load_tr(p + 4 * T * 2));
+    };
 #pragma unroll
-    for (int dt = 0; dt < NDT; dt++) {
-      f32x16 c;
+    for (int dg = 0; dg < NDT / DG; dg++) {
+      f32x16 c[DG];
 #pragma unroll
-      for (int r = 0; r < 16; r++) c[r] = 0.f;
+      for (int i = 0; i < DG; i++)
 #pragma unroll
-      for (int ks = 0; ks < KS; ks++) {
-        const int o0 = (16 * ks + hl) * T * 2 + tcol * 2, o1 = o0 + 4 * T * 2;
-        const bf16x8 ads = join_tr(lds_load_tr(dsbuf + o0), lds_load_tr(dsbuf + o1));
-        const bf16x8 adl = join_tr(lds_load_tr(dslo + o0), lds_load_tr(dslo + o1));
-        const bf16x8 aph = join_tr(lds_load_tr(pbuf + o0), lds_load_tr(pbuf + o1));
-        const bf16x8 apl = join_tr(lds_load_tr(plo + o0), lds_load_tr(plo + o1));
-        c = mfma32(ads, qv[dt][ks], c);
-        c = mfma32(adl, qv[dt][ks], c);
-        c = mfma32(aph, dov[dt][ks], c);
-        c = mfma32(apl, dov[dt][ks], c);
+        for (int r = 0; r < 16; r++) c[i][r] = 0.f;
+      bf16x8 acur[4], anxt[4];
+#pragma unroll
+      for (int m = 0; m < 4; m++) acur[m] = afrag(0, m);
+#pragma unroll
+      for (int ks = 0; ks < KH; ks++) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + 1 < KH) {
+#pragma unroll
+          for (int m = 0; m < 4; m++) anxt[m] = afrag(ks + 1, m);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+#pragma unroll
+          for (int i = 0; i < DG; i++) {
+            const int dt = dg * DG + i;
+            c[i] = mfma32(acur[m], m < 2 ? qv[dt][ks] : dov[dt][ks], c[i]);
+          }
+        if (ks + 1 < KH) {
+#pragma unroll
+          for (int m = 0; m < 4; m++) acur[m] = anxt[m];
+        }
       }
-      // C layout: lane holds d = w*DW + 32 dt + (lane & 31), slots 8 (r>>2) + 4 kg + (r&3).
-      const int d = w * DW + 32 * dt + (lane & 31);
+      __builtin_amdgcn_sched_barrier(0);
+      if (dg == NDT / DG - 1) wait_all_mem();  // this wave's part of tile blk + 1
       if (stage) {
+        // one row address per slot, the DG d tiles at instruction offsets
 #pragma unroll
         for (int r = 0; r < 16; r++) {
-          const int t = 8 * (r >> 2) + 4 * kg + (r & 3);
-          if ((mask >> t) & 1ull) __builtin_nontemporal_store(c[r], stage + (int64_t)rowi[r] * D + d);
+          float* p = outb + (int64_t)rowi[r] * D + 32 * dg * DG;
+#pragma unroll
+          for (int i = 0; i < DG; i++) __builtin_nontemporal_store(c[i][r], p + 32 * i);
         }
       } else {
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const int t = 8 * (r >> 2) + 4 * kg + (r & 3);
-          if ((mask >> t) & 1ull) unsafeAtomicAdd(acc_b + (int64_t)rowi[r] * D + d, c[r]);
+          if ((mask >> t) & 1ull) {
+            float* p = outb + (int64_t)rowi[r] * D + 32 * dg * DG;
+#pragma unroll
+            for (int i = 0; i < DG; i++) unsafeAtomicAdd(p + 32 * i, c[i][r]);
+          }
         }
       }
     }
+  };
+  for (int blk = 0; blk < nblk; blk += 2) {
+    block(IntTag<0>{}, blk);
+    if (blk + 1 < nblk) block(IntTag<1>{}, blk + 1);
   }
 }
 

@@ -49,8 +49,23 @@ __device__ __forceinline__ bf16x8 join_tr(s16x4 lo, s16x4 hi) {
 __device__ __forceinline__ void dma16(const void* gsrc, char* lds_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (SMQA_LDS void*)(SMQA_LDS char*)lds_base, 16, 0, 0);
 }
+// Buffer resource over [base, base + bytes) for raw (unswizzled, stride 0) buffer loads.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+// 16-byte global -> LDS copy through a buffer resource (buffer_load_dwordx4 ... lds): lane l reads
+// rsrc + soff + voff and lands at lds_base + 16*l. Unlike the global_ form this is not a FLAT
+// instruction, so the compiler keeps exact LDS wait counts for reads issued while it is in flight.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, char* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SMQA_LDS void*)(SMQA_LDS char*)lds_base, 16, voff, soff, 0, 0);
+}
 // Wait for all outstanding memory operations of this wave (including LDS DMA).
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Pins a long-lived MFMA operand to the accumulator register file (an MFMA reads its A and B
+// operands from there directly), leaving the vector registers to accumulators and in-flight
+// fragments.
+__device__ __forceinline__ void keep_in_agpr(bf16x8& v) { asm volatile("" : "+a"(v)); }
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *(const uint4*)p);
@@ -66,6 +81,12 @@ __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) 
   v[0] = (__bf16)a; v[1] = (__bf16)b; v[2] = (__bf16)c; v[3] = (__bf16)d;
   return __builtin_bit_cast(uint2, v);
 }
+
+// Compile-time integer tag, used to instantiate a loop body once per LDS buffer.
+template <int V>
+struct IntTag {
+  static constexpr int value = V;
+};
 
 __device__ __forceinline__ float wave_max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 
