@@ -110,7 +110,7 @@ int sparse_mqa_fwd(const void* q, const void* kv, const float* attn_sink, const 
 namespace {
 
 struct DkvPlan {
-  size_t count, offset, tiles, acc, pos, stage;  // byte offsets into the workspace
+  size_t count, offset, tiles, acc, pos, stage, stage_exp;  // byte offsets into the workspace
   int64_t chunk;                                  // tokens per chunk
   bool use_acc;                                   // a separate fp32 accumulator in the workspace
   size_t end;                                     // bytes used
@@ -122,10 +122,12 @@ size_t fixed_dkv_bytes(int64_t B, int64_t S_kv) {
          round256((size_t)smqa::scan_tiles(n_cnt) * 4);
 }
 
+// Bytes of one staging row: D fp16 values and D/16 int8 exponents (one per 16 values).
+size_t stage_row_bytes(int64_t D) { return (size_t)D * 2 + (size_t)D / 16; }
 // Per token: its slots' positions, one staging row per slot and head block, and one spare row per
 // head block that takes the stores of the token's masked slots.
 size_t per_token_dkv_bytes(int64_t H, int64_t D, int64_t topk) {
-  return (size_t)topk * 4 + (size_t)(topk + 1) * smqa::bwd_hblocks(H) * D * 4;
+  return (size_t)topk * 4 + (size_t)(topk + 1) * smqa::bwd_hblocks(H) * stage_row_bytes(D);
 }
 
 // Lay out the dKV part of the workspace starting at `base`; false if `bytes` cannot hold even one
@@ -159,8 +161,11 @@ bool plan_dkv(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t 
   }
   p->pos = o;
   o += round256((size_t)p->chunk * topk * 4);
+  const size_t rows = (size_t)p->chunk * (topk + 1) * smqa::bwd_hblocks(H);
   p->stage = o;
-  o += round256((size_t)p->chunk * (topk + 1) * smqa::bwd_hblocks(H) * D * 4);
+  o += round256(rows * D * 2);
+  p->stage_exp = o;
+  o += round256(rows * (D / 16));
   p->end = o;
   return o <= bytes;
 }
@@ -180,19 +185,20 @@ int run_dkv(const void* q, const void* kv, const void* d_o, const int32_t* idx, 
   int32_t* offset = (int32_t*)(ws + p.offset);
   int32_t* tiles = (int32_t*)(ws + p.tiles);
   int32_t* pos = (int32_t*)(ws + p.pos);
-  float* stage = (float*)(ws + p.stage);
+  uint16_t* stage = (uint16_t*)(ws + p.stage);
+  int8_t* stage_exp = (int8_t*)(ws + p.stage_exp);
   float* acc = dkv_fp32 ? (float*)dkv : (p.use_acc ? (float*)(ws + p.acc) : nullptr);
   for (int64_t t0 = 0; t0 < tokens; t0 += p.chunk) {
     const int64_t n = (tokens - t0) < p.chunk ? (tokens - t0) : p.chunk;
     if (smqa::launch_dkv_prepare(idx, count, offset, tiles, pos, B, S, S_kv, topk, smqa::bwd_hblocks(H), t0, n, st) !=
         hipSuccess)
       return SMQA_ERR_HIP;
-    smqa::BwdMainArgs a{q, kv, d_o, idx, lse, delta, nullptr, nullptr, pos, stage, B, S, S_kv, H, D, topk, scale,
-                        t0, n};
+    smqa::BwdMainArgs a{q, kv, d_o, idx, lse, delta, nullptr, nullptr, pos, stage, stage_exp, B, S, S_kv, H, D,
+                        topk, scale, t0, n};
     if (smqa::launch_bwd_main(a, 2, st) != hipSuccess) return SMQA_ERR_HIP;
     const bool last = t0 + n >= tokens;
     void* out16 = (!dkv_fp32 && last) ? dkv : nullptr;
-    if (smqa::launch_reduce_rows(stage, offset, acc, out16, t0 > 0 ? 1 : 0, n_rows, D, st) != hipSuccess)
+    if (smqa::launch_reduce_rows(stage, stage_exp, offset, acc, out16, t0 > 0 ? 1 : 0, n_rows, D, st) != hipSuccess)
       return SMQA_ERR_HIP;
   }
   return SMQA_OK;
@@ -215,13 +221,15 @@ extern "C" {
 size_t sparse_mqa_bwd_workspace_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk) {
   if (!sizes_ok(B, S, S_kv, H, D, topk)) return 0;
   return delta_bytes(B, S, H) + fixed_dkv_bytes(B, S_kv) + round256((size_t)(B * S) * topk * 4) +
-         round256((size_t)(B * S) * (topk + 1) * smqa::bwd_hblocks(H) * D * 4) + 512;
+         round256((size_t)(B * S) * (topk + 1) * smqa::bwd_hblocks(H) * D * 2) +
+         round256((size_t)(B * S) * (topk + 1) * smqa::bwd_hblocks(H) * (D / 16)) + 512;
 }
 
 size_t sparse_mqa_bwd_workspace_min_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk) {
   if (!sizes_ok(B, S, S_kv, H, D, topk)) return 0;
   return delta_bytes(B, S, H) + fixed_dkv_bytes(B, S_kv) + round256((size_t)(B * S_kv) * D * 4) +
-         round256((size_t)topk * 4) + round256((size_t)(topk + 1) * smqa::bwd_hblocks(H) * D * 4) + 512;
+         round256((size_t)topk * 4) + round256((size_t)(topk + 1) * smqa::bwd_hblocks(H) * D * 2) +
+         round256((size_t)(topk + 1) * smqa::bwd_hblocks(H) * (D / 16)) + 512;
 }
 
 int sparse_mqa_bwd_preprocess(const void* o, const void* d_o, float* delta, int64_t B, int64_t S, int64_t H,
@@ -252,7 +260,7 @@ int sparse_mqa_bwd_dq(const void* q, const void* kv, const void* d_o, const int3
                       {lse, count({B, S, H}) * 4}, {delta, count({B, S, H}) * 4}};
   for (const Span& s : ins)
     if (overlap(sdq, s)) return SMQA_ERR_ALIAS;
-  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, nullptr, nullptr, nullptr, B, S, S_kv, H, D, topk,
+  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, nullptr, nullptr, nullptr, nullptr, B, S, S_kv, H, D, topk,
                       scale, 0, B * S};
   return smqa::launch_bwd_main(a, 1, (hipStream_t)stream) == hipSuccess ? SMQA_OK : SMQA_ERR_HIP;
 }
@@ -295,7 +303,7 @@ int sparse_mqa_bwd_main(const void* q, const void* kv, const void* d_o, const in
   for (const Span& s : ins)
     if (overlap(sdq, s) || overlap(sacc, s)) return SMQA_ERR_ALIAS;
   if (overlap(sdq, sacc)) return SMQA_ERR_ALIAS;
-  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, dkv_accum, nullptr, nullptr, B, S, S_kv, H, D, topk,
+  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, dkv_accum, nullptr, nullptr, nullptr, B, S, S_kv, H, D, topk,
                       scale, 0, B * S};
   return smqa::launch_bwd_main(a, 3, (hipStream_t)stream) == hipSuccess ? SMQA_OK : SMQA_ERR_HIP;
 }
@@ -341,7 +349,7 @@ int sparse_mqa_bwd(const void* q, const void* kv, const float* attn_sink, const 
   if ((st = run_dkv(q, kv, d_o, topk_idxs, lse, delta, dkv, dkv_fp32, (char*)workspace, p, B, S, S_kv, H, D, topk,
                     scale, hs)))
     return st;
-  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, nullptr, nullptr, nullptr, B, S, S_kv, H, D, topk,
+  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, nullptr, nullptr, nullptr, nullptr, B, S, S_kv, H, D, topk,
                       scale, 0, B * S};
   return smqa::launch_bwd_main(a, 1, hs) == hipSuccess ? SMQA_OK : SMQA_ERR_HIP;
 }

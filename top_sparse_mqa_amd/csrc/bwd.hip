@@ -32,6 +32,23 @@ __device__ __forceinline__ int bwd_off(int row, int chunk) {
   return row * (D * 2) + ((chunk ^ (bwd_swz(row) & (D / 8 - 1))) << 4);
 }
 
+// Staging rows hold D fp16 values and D/16 int8 exponents: value = fp16 * 2^e, one e per 16
+// consecutive values (the exponent of their largest magnitude, so the fp16 parts lie in (-1, 1)).
+// This halves the traffic of the staged scatter-add against fp32 rows; a value keeps 11 significant
+// bits relative to its group maximum. One lane stores 4 values; the 16-value group is a hardware
+// quad of lanes (all 64 lanes must execute this), whose first lane also stores the exponent.
+template <int D>
+__device__ __forceinline__ void stage_store4(uint16_t* stage, int8_t* stage_exp, int32_t row, int d, f32x4 v, int lane) {
+  const float m = quad_max(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+  int e = (m > 0.f && m <= 3.4028235e38f) ? __builtin_amdgcn_frexp_expf(m) : 0;  // m < 2^e
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  f16x4 h;
+#pragma unroll
+  for (int k = 0; k < 4; k++) h[k] = (_Float16)__builtin_amdgcn_ldexpf(v[k], -e);
+  __builtin_nontemporal_store(__builtin_bit_cast(i32x2, h), (i32x2*)(stage + (int64_t)row * D + d));
+  if ((lane & 3) == 0) stage_exp[(int64_t)row * (D / 16) + (d >> 4)] = (int8_t)e;
+}
+
 // ---------------------------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256)
@@ -136,10 +153,11 @@ __device__ __forceinline__ void bwd_score_offsets(int lane, int* sc_off) {
 // S^T and dP^T of one 32-slot block for this wave's 16 heads (C layout: lane l holds head
 // (l & 15) and slots 16 mt + 4 (l>>4) + r). Fragment i is (ks, mt) = (i / 2, i % 2). PF fragment
 // reads run ahead of the MFMAs that use them; every stage is fenced so the scheduler cannot pull
-// a read down to its use, which would expose the full LDS latency on each MFMA.
-template <int D, int PF>
+// a read down to its use, which would expose the full LDS latency on each MFMA. stage_hook(i)
+// runs inside stage i (the dKV kernel issues the previous block's stores there).
+template <int D, int PF, typename Hook>
 __device__ __forceinline__ void bwd_scores(const char* tile, const int* sc_off, const bf16x8* qb,
-                                           const bf16x8* dob, f32x4* sacc, f32x4* dpacc) {
+                                           const bf16x8* dob, f32x4* sacc, f32x4* dpacc, Hook&& stage_hook) {
   using C = BwdCommon<D, 1>;
   constexpr int NF = 2 * C::KS;
   constexpr int PFE = PF < NF ? PF : NF;  // reads in flight
@@ -162,6 +180,7 @@ __device__ __forceinline__ void bwd_scores(const char* tile, const int* sc_off, 
     const int ks = i >> 1, mt = i & 1;
     sacc[mt] = mfma16(fr[i % NB], qb[ks], sacc[mt]);
     dpacc[mt] = mfma16(fr[i % NB], dob[ks], dpacc[mt]);
+    stage_hook(i);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -258,7 +277,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
     if (mask == 0) return;
 
     f32x4 sacc[2], dpacc[2];
-    bwd_scores<D, PF>(tile, sc_off, qb, dob, sacc, dpacc);
+    bwd_scores<D, PF>(tile, sc_off, qb, dob, sacc, dpacc, [](int) {});
 
     auto dfrag = [&](int dt) {
       const char* p = tile + dq_off[dt % C::DQJ] + 256 * (dt / C::DQJ);
@@ -305,9 +324,9 @@ template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64)
 bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ dout,
                const int32_t* __restrict__ idx, const float* __restrict__ lse, const float* __restrict__ delta,
-               float* __restrict__ dkv_acc, const int32_t* __restrict__ pos, float* __restrict__ stage,
-               int S, int64_t S_kv, int H, int topk, float sm_scale, float scale_log2, int n_hblk,
-               int token0, int n_tokens) {
+               float* __restrict__ dkv_acc, const int32_t* __restrict__ pos, uint16_t* __restrict__ stage,
+               int8_t* __restrict__ stage_exp, int S, int64_t S_kv, int H, int topk, float sm_scale,
+               float scale_log2, int n_hblk, int token0, int n_tokens) {
   using C = BwdCommon<D, NW>;
   constexpr int T = C::T;
   constexpr int PF = 6;
@@ -323,6 +342,20 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
   // P / sm_scale*dS as hi and lo bf16 parts (lo = x - float(bf16(x)), rounded): buffers
   // 0 = dS hi, 1 = dS lo, 2 = P hi, 3 = P lo, each [head][slot].
   __shared__ __attribute__((aligned(16))) char pds[4 * SB];
+  // Staging-store transpose: each wave writes its [32 slots][DG*32 d] fp32 tile here and reads it
+  // back as whole row segments, so each 16-byte store covers DG*128 contiguous bytes of a row.
+  // The row pitch is padded by 32 bytes: the two half-waves of a column write (slots 4 apart) then
+  // fall on disjoint banks.
+  constexpr int OP = DG * 128 + 32;
+  __shared__ __attribute__((aligned(16))) char obuf[NW][T * OP];
+  // read-back geometry of the transpose: RPS slot rows of LPR lanes per instruction
+  constexpr int LPR = DG * 8, RPS = 64 / LPR, NI = T / RPS;
+  // With one d group per wave the stores of a block are deferred: the block leaves its rows in
+  // obuf (and their staging row indices in obdst) and the next block issues them from inside its
+  // score loop, one every other stage. A wave issues in order, so stores issued in one burst
+  // would stall its MFMAs behind the memory pipeline.
+  constexpr bool DEFER = (NDT == DG);
+  __shared__ int32_t obdst[NW][T];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -424,13 +457,51 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
   int32_t idx_nxt = nblk > 1 ? load_idx(1) : -1;
   wait_all_mem();
 
+  // Deferred staging stores (stage mode, one d group): row k of the previous block's transpose
+  // buffer goes to staging row obdst[k * RPS + lane / LPR]. Reads of row k run in score stage 2k,
+  // its store in stage 2k + 7 (a ring of four rows in flight); the rest are flushed after the loop.
+  bool pending = false;
+  const int dlane = w * DW + 4 * (lane % LPR);  // first d of this lane's 4 values
+  f32x4 dv[4];
+  int32_t dd[4];
+  auto dread = [&](int k) {
+    dv[k & 3] = *(const f32x4*)(obuf[w] + (k * RPS + lane / LPR) * OP + 16 * (lane % LPR));
+    dd[k & 3] = obdst[w][k * RPS + lane / LPR];
+  };
+  auto dstore = [&](int k) { stage_store4<D>(stage, stage_exp, dd[k & 3], dlane, dv[k & 3], lane); };
+  constexpr int NFS = 2 * C::KS;  // score stages
+  auto store_hook = [&](int i) {
+    if constexpr (DEFER) {
+      if (!pending) return;
+      if ((i & 1) == 0 && i / 2 < NI) dread(i / 2);
+      if ((i & 1) == 1 && i >= 7 && (i - 7) / 2 < NI) dstore((i - 7) / 2);
+    }
+  };
+  // issues whatever the hook did not: reads for rows with 2k >= NFS, stores for rows with 2k+7 >= NFS
+  auto flush_pending = [&](bool after_scores) {
+    if constexpr (DEFER) {
+      if (!pending) return;
+#pragma unroll
+      for (int k = 0; k < NI; k++) {
+        const bool read_done = after_scores && 2 * k < NFS;
+        const bool store_done = after_scores && 2 * k + 7 < NFS;
+        if (store_done) continue;
+        if (!read_done) dread(k);
+        dstore(k);
+      }
+      pending = false;
+    }
+  };
+
   // Each wave waits for its own part of tile blk + 1 right before it stores the rows of tile blk,
   // so the barrier at the top of the next block finds the tile complete without draining stores.
   auto block = [&](auto buf_tag, int blk) {
     constexpr int BUF = decltype(buf_tag)::value;
     const char* tile = BUF ? tile1 : tile0;
     char* other = BUF ? tile0 : tile1;
-    __syncthreads();  // tile blk complete; the P/dS buffers of the previous block fully consumed
+    // tile blk complete (each wave waited for its part before its previous stores); the P/dS
+    // buffers of the previous block fully consumed. The stores themselves stay in flight.
+    lds_barrier();
     uint64_t mask_nxt = 0;
     if (blk + 1 < nblk) {
       mask_nxt = __ballot(slot_in_range(idx_nxt, S_kv));
@@ -450,7 +521,8 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
     }
 
     f32x4 sacc[2], dpacc[2];
-    bwd_scores<D, PF>(tile, sc_off, qb, dob, sacc, dpacc);
+    bwd_scores<D, PF>(tile, sc_off, qb, dob, sacc, dpacc, store_hook);
+    flush_pending(true);
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) {
       float p[4], ds[4], plr[4], dslr[4];
@@ -468,20 +540,27 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
       *(uint2*)(wp + 2 * SB) = pack4_bf16(p[0], p[1], p[2], p[3]);
       *(uint2*)(wp + 3 * SB) = pack4_bf16(plr[0], plr[1], plr[2], plr[3]);
     }
-    __syncthreads();
+    lds_barrier();  // P/dS visible to all waves; the next tile's gather stays in flight
 
     // dKV[slot, d] for this wave's d-range, DG tiles of 32 d at a time:
     //   dS_hi^T Q + dS_lo^T Q + P_hi^T dO + P_lo^T dO, k over the block's heads.
-    // C layout: lane holds d = w*DW + 32 dt + (lane & 31), slots 8 (r>>2) + 4 kg + (r & 3); each
-    // store instruction then writes two whole 128-byte row segments.
+    // C layout: lane holds d = w*DW + 32 dt + (lane & 31), slots 8 (r>>2) + 4 kg + (r & 3).
     // staging mode: masked slots store into this workgroup's spare row (after all staging rows of
     // the chunk), so the stores need no per-slot branches
     const int32_t spare = (n_tokens * topk + (int32_t)ctok) * n_hblk + hblk;
     const int32_t dst_this = stage ? (slot_in_range(idx_this, S_kv) ? pos_this + hblk : spare) : idx_this;
     int32_t rowi[16];
+    if (stage && DEFER) {
+      // no per-lane rows needed: they go to obdst below
+    } else if (stage) {
 #pragma unroll
-    for (int r = 0; r < 16; r++) rowi[r] = __shfl(dst_this, 8 * (r >> 2) + 4 * kg + (r & 3));
-    float* outb = (stage ? stage : acc_b) + w * DW + (lane & 31);
+      for (int n = 0; n < NI; n++) rowi[n] = __shfl(dst_this, n * RPS + lane / LPR);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; r++) rowi[r] = __shfl(dst_this, 8 * (r >> 2) + 4 * kg + (r & 3));
+    }
+    float* outb = stage ? nullptr : acc_b + w * DW + (lane & 31);  // atomic mode only
+    char* ob = obuf[w];
     auto afrag = [&](int ks, int m) {
       const char* p = pds + m * SB + pr_off + ks * 16 * T * 2;
       return join_tr(lds_load_tr(p), lds_load_tr(p + 4 * T * 2));
@@ -516,16 +595,31 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (dg == NDT / DG - 1) wait_all_mem();  // this wave's part of tile blk + 1
       if (stage) {
-        // one row address per slot, the DG d tiles at instruction offsets
+        // column writes into this wave's transpose buffer (slot row t, d column 32 i + lane & 31)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          float* p = outb + (int64_t)rowi[r] * D + 32 * dg * DG;
+        for (int i = 0; i < DG; i++)
 #pragma unroll
-          for (int i = 0; i < DG; i++) __builtin_nontemporal_store(c[i][r], p + 32 * i);
+          for (int r = 0; r < 16; r++) {
+            const int t = 8 * (r >> 2) + 4 * kg + (r & 3);
+            *(float*)(ob + t * OP + (32 * i + (lane & 31)) * 4) = c[i][r];
+          }
+        if constexpr (DEFER) {
+          if (lane < T) obdst[w][lane] = dst_this;
+          wait_all_mem();  // this wave's part of tile blk + 1
+          pending = true;
+          continue;
+        }
+        if (dg == NDT / DG - 1) wait_all_mem();  // this wave's part of tile blk + 1
+        // row reads: lane covers 4 consecutive d of slot row n*RPS + lane/LPR
+        const int d0 = w * DW + 32 * dg * DG + 4 * (lane % LPR);
+#pragma unroll
+        for (int n = 0; n < NI; n++) {
+          const f32x4 v = *(const f32x4*)(ob + (n * RPS + lane / LPR) * OP + 16 * (lane % LPR));
+          stage_store4<D>(stage, stage_exp, rowi[n], d0, v, lane);
         }
       } else {
+        if (dg == NDT / DG - 1) wait_all_mem();  // this wave's part of tile blk + 1
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const int t = 8 * (r >> 2) + 4 * kg + (r & 3);
@@ -542,6 +636,7 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
     block(IntTag<0>{}, blk);
     if (blk + 1 < nblk) block(IntTag<1>{}, blk + 1);
   }
+  flush_pending(false);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -662,33 +757,60 @@ scan_add_kernel(int32_t* __restrict__ out, const int32_t* __restrict__ tile_sum,
 // the running accumulator (earlier token chunks), then write fp32 and/or bf16 output.
 template <int D>
 __global__ void __launch_bounds__(256)
-reduce_rows_kernel(const f32x4* __restrict__ stage, const int32_t* __restrict__ offset,
-                   f32x4* __restrict__ acc, uint2* __restrict__ out_bf16, int accumulate) {
+reduce_rows_kernel(const uint16_t* __restrict__ stage, const int8_t* __restrict__ stage_exp,
+                   const int32_t* __restrict__ offset, f32x4* __restrict__ acc, uint4* __restrict__ out_bf16,
+                   int accumulate) {
   // offset is indexed by (row, sub): the row's segment is [offset[row*RANK_SUB], offset[(row+1)*RANK_SUB]).
-  constexpr int F4 = D / 4;         // 16-byte pieces per row
-  constexpr int NG = 256 / F4;      // thread groups, each taking every NG-th contribution
-  static_assert(NG >= 1 && 256 % F4 == 0, "row width");
-  __shared__ f32x4 part[NG][F4];
+  // Thread c of a group takes values 8c .. 8c+7 of every NG-th staging row of the segment.
+  constexpr int F8 = D / 8;         // 16-byte pieces of fp16 per row
+  constexpr int NG = 256 / F8;      // thread groups
+  static_assert(NG >= 1 && 256 % F8 == 0, "row width");
+  __shared__ f32x4 part[NG][F8][2];
   const int64_t row = blockIdx.x;
-  const int g = threadIdx.x / F4, c = threadIdx.x % F4;
+  const int g = threadIdx.x / F8, c = threadIdx.x % F8;
   const int32_t beg = offset[row * RANK_SUB], end = offset[(row + 1) * RANK_SUB];
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, s2 = s0, s3 = s0;
+  f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
+  auto add = [&](const i32x4& raw, int e) {
+    const f16x8 h = __builtin_bit_cast(f16x8, raw);
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      lo[k] += __builtin_amdgcn_ldexpf((float)h[k], e);
+      hi[k] += __builtin_amdgcn_ldexpf((float)h[4 + k], e);
+    }
+  };
+  auto ld = [&](int32_t i) { return __builtin_nontemporal_load((const i32x4*)(stage + (int64_t)i * D) + c); };
+  auto lde = [&](int32_t i) { return (int)stage_exp[(int64_t)i * (D / 16) + (c >> 1)]; };
   int32_t i = beg + g;
   for (; i + 3 * NG < end; i += 4 * NG) {
-    s0 += __builtin_nontemporal_load(stage + (int64_t)i * F4 + c);
-    s1 += __builtin_nontemporal_load(stage + (int64_t)(i + NG) * F4 + c);
-    s2 += __builtin_nontemporal_load(stage + (int64_t)(i + 2 * NG) * F4 + c);
-    s3 += __builtin_nontemporal_load(stage + (int64_t)(i + 3 * NG) * F4 + c);
+    const i32x4 r0 = ld(i), r1 = ld(i + NG), r2 = ld(i + 2 * NG), r3 = ld(i + 3 * NG);
+    const int e0 = lde(i), e1 = lde(i + NG), e2 = lde(i + 2 * NG), e3 = lde(i + 3 * NG);
+    add(r0, e0);
+    add(r1, e1);
+    add(r2, e2);
+    add(r3, e3);
   }
-  for (; i < end; i += NG) s0 += __builtin_nontemporal_load(stage + (int64_t)i * F4 + c);
-  part[g][c] = (s0 + s1) + (s2 + s3);
+  for (; i < end; i += NG) add(ld(i), lde(i));
+  part[g][c][0] = lo;
+  part[g][c][1] = hi;
   __syncthreads();
   if (g == 0) {
-    f32x4 t = part[0][c];
-    for (int k = 1; k < NG; k++) t += part[k][c];
-    if (accumulate) t += acc[row * F4 + c];
-    if (acc) acc[row * F4 + c] = t;
-    if (out_bf16) out_bf16[row * F4 + c] = pack4_bf16(t[0], t[1], t[2], t[3]);
+    f32x4 t0 = part[0][c][0], t1 = part[0][c][1];
+    for (int k = 1; k < NG; k++) {
+      t0 += part[k][c][0];
+      t1 += part[k][c][1];
+    }
+    if (accumulate) {
+      t0 += acc[row * (D / 4) + 2 * c];
+      t1 += acc[row * (D / 4) + 2 * c + 1];
+    }
+    if (acc) {
+      acc[row * (D / 4) + 2 * c] = t0;
+      acc[row * (D / 4) + 2 * c + 1] = t1;
+    }
+    if (out_bf16) {
+      const uint2 a = pack4_bf16(t0[0], t0[1], t0[2], t0[3]), b = pack4_bf16(t1[0], t1[1], t1[2], t1[3]);
+      out_bf16[row * F8 + c] = make_uint4(a.x, a.y, b.x, b.y);
+    }
   }
 }
 
@@ -739,8 +861,8 @@ static hipError_t launch_bwd_main_t(const BwdMainArgs& a, int which, hipStream_t
   if (!(which & 2)) return hipSuccess;
   hipLaunchKernelGGL((bwd_dkv_kernel<D, NW>), dim3((unsigned)(a.n_chunk * n_hblk)), dim3(NW * 64), 0, st,
                      (const uint16_t*)a.q, (const uint16_t*)a.kv, (const uint16_t*)a.d_o, a.idx, a.lse, a.delta,
-                     a.dkv_accum, a.pos, a.stage, (int)a.S, a.S_kv, (int)a.H, (int)a.topk, a.sm_scale, sl2, n_hblk,
-                     (int)a.token0, (int)a.n_chunk);
+                     a.dkv_accum, a.pos, a.stage, a.stage_exp, (int)a.S, a.S_kv, (int)a.H, (int)a.topk, a.sm_scale,
+                     sl2, n_hblk, (int)a.token0, (int)a.n_chunk);
   return hipGetLastError();
 }
 
@@ -791,14 +913,14 @@ hipError_t launch_dkv_prepare(const int32_t* idx, int32_t* count, int32_t* offse
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_rows(const float* stage, const int32_t* offset, float* acc, void* out_bf16, int accumulate,
-                              int64_t n_rows, int64_t D, hipStream_t st) {
+hipError_t launch_reduce_rows(const uint16_t* stage, const int8_t* stage_exp, const int32_t* offset, float* acc,
+                              void* out_bf16, int accumulate, int64_t n_rows, int64_t D, hipStream_t st) {
   if (D == 512)
-    hipLaunchKernelGGL(reduce_rows_kernel<512>, dim3((unsigned)n_rows), dim3(256), 0, st, (const f32x4*)stage,
-                       offset, (f32x4*)acc, (uint2*)out_bf16, accumulate);
+    hipLaunchKernelGGL(reduce_rows_kernel<512>, dim3((unsigned)n_rows), dim3(256), 0, st, stage, stage_exp, offset,
+                       (f32x4*)acc, (uint4*)out_bf16, accumulate);
   else if (D == 64)
-    hipLaunchKernelGGL(reduce_rows_kernel<64>, dim3((unsigned)n_rows), dim3(256), 0, st, (const f32x4*)stage,
-                       offset, (f32x4*)acc, (uint2*)out_bf16, accumulate);
+    hipLaunchKernelGGL(reduce_rows_kernel<64>, dim3((unsigned)n_rows), dim3(256), 0, st, stage, stage_exp, offset,
+                       (f32x4*)acc, (uint4*)out_bf16, accumulate);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -59,6 +59,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, char* lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SMQA_LDS void*)(SMQA_LDS char*)lds_base, 16, voff, soff, 0, 0);
 }
+// Workgroup barrier that publishes this wave's LDS writes only. __syncthreads() also waits for
+// every outstanding global access, including tile gathers still in flight for a later block; this
+// waits for the LDS counter alone, and the empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 // Wait for all outstanding memory operations of this wave (including LDS DMA).
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -80,6 +90,18 @@ __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) 
   bf16x4 v;
   v[0] = (__bf16)a; v[1] = (__bf16)b; v[2] = (__bf16)c; v[3] = (__bf16)d;
   return __builtin_bit_cast(uint2, v);
+}
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Maximum over the four lanes of a hardware quad (DPP quad permutations, no LDS traffic).
+__device__ __forceinline__ float quad_max(float m) {
+  m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0xB1, 0xF, 0xF, true)));
+  m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0x4E, 0xF, 0xF, true)));
+  return m;
 }
 
 // Compile-time integer tag, used to instantiate a loop body once per LDS buffer.

@@ -37,9 +37,17 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
   constexpr int RPI = 1024 / ROWB;
   constexpr int NINSTR = T / RPI;
   constexpr int XB = 2 * 16 * 64 * 4;  // one wave's partial S^T: 2 tiles x 16 regs x 64 lanes fp32
-  __shared__ __attribute__((aligned(16))) char smem[2 * TB + NW * XB];
-  char* tiles = smem;
-  char* xbuf = smem + 2 * TB;
+  constexpr int KS = DH / 16;          // k-steps of the S^T product
+  constexpr int NDT = DH / 32;         // 32-wide d tiles of O^T
+  constexpr int PFS = 4;               // S fragment reads in flight
+  constexpr int NFV = 4 * NDT;         // V fragments per block
+  constexpr int PFV = NFV < 4 ? NFV : 4;  // V fragment reads in flight
+  // The two tile buffers are distinct LDS arrays and the block loop is unrolled by two, so every
+  // read names its buffer at compile time and is not made to wait for the gather in flight into
+  // the other one.
+  __shared__ __attribute__((aligned(16))) char tile0[TB];
+  __shared__ __attribute__((aligned(16))) char tile1[TB];
+  __shared__ __attribute__((aligned(16))) char xbuf[NW * XB];
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -54,20 +62,22 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
 
   // Q for this wave's half of D, as the B operand of S^T = K Q^T:
   // lane holds head (lane & 31), d = half*DH + 16 ks + 8 kg .. +7.
-  bf16x8 qb[DH / 16];
+  bf16x8 qb[KS];
   {
     const uint16_t* qrow = q + (token * H + (head_ok ? head : 0)) * (int64_t)D + half * DH + 8 * kg;
 #pragma unroll
-    for (int ks = 0; ks < DH / 16; ks++) qb[ks] = head_ok ? load_bf16x8(qrow + 16 * ks) : zero_bf16x8();
+    for (int ks = 0; ks < KS; ks++) qb[ks] = head_ok ? load_bf16x8(qrow + 16 * ks) : zero_bf16x8();
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) keep_in_agpr(qb[ks]);
   }
   const float sink2 = head_ok ? sink[head] * kLog2e : 0.f;
   float m_run = sink2;
   // The sink's share of the denominator is carried by the kg == 0 lane of each head.
   float l_run = (kg == 0 && sink2 != -INFINITY) ? 1.f : 0.f;
 
-  f32x16 oacc[DH / 32];
+  f32x16 oacc[NDT];
 #pragma unroll
-  for (int dt = 0; dt < DH / 32; dt++)
+  for (int dt = 0; dt < NDT; dt++)
 #pragma unroll
     for (int r = 0; r < 16; r++) oacc[dt][r] = 0.f;
 
@@ -80,21 +90,23 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
     return t < topk ? idx_tok[t] : -1;
   };
   const int wu = __builtin_amdgcn_readfirstlane(w);  // wave index as a scalar
-  auto issue_tile = [&](int32_t my_idx, uint64_t mask, int buf) {
-    char* tile = tiles + buf * TB;
+  auto issue_tile = [&](int32_t my_idx, uint64_t mask, char* tile) {
     if constexpr (RPI == 1) {
-      // One kv row per instruction: row index and validity are wave-uniform (scalar registers).
+      // One kv row per instruction, through a buffer resource: row index and validity are
+      // wave-uniform, the row offset goes in the scalar offset; masked rows read the zero row.
       // The lane id is passed through an empty asm so the per-row lane offsets are computed
-      // here (two VALU ops each) instead of being hoisted out of the block loop, where they
-      // would hold 16 registers for the whole kernel.
+      // here instead of being hoisted out of the block loop into 16 live registers.
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv_b, (int)(S_kv * ROWB));
+      const __amdgpu_buffer_rsrc_t rz = make_rsrc(g_zero_row, ROWB);
       int ln = lane;
       asm volatile("" : "+v"(ln));
 #pragma unroll
       for (int i = 0; i < NINSTR / NW; i++) {
         const int r = wu + NW * i;
         const int32_t ri = __builtin_amdgcn_readlane(my_idx, r);
-        const char* row = ((mask >> r) & 1ull) ? kv_b + (int64_t)ri * ROWB : (const char*)g_zero_row;
-        dma16(row + (uint32_t)((ln ^ (fwd_swz(r) & (CPR - 1))) << 4), tile + r * ROWB);
+        const uint32_t voff = (uint32_t)((ln ^ (fwd_swz(r) & (CPR - 1))) << 4);
+        if ((mask >> r) & 1ull) dma16_buf(rk, voff, (uint32_t)ri * ROWB, tile + r * ROWB);
+        else dma16_buf(rz, voff, 0, tile + r * ROWB);
       }
     } else {
       for (int ins = wu; ins < NINSTR; ins += NW) {
@@ -112,7 +124,7 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
   // Per-lane parts of the LDS addresses, fixed for the whole kernel. The XOR swizzle only touches
   // the low four chunk bits, so chunks 16 apart differ by 256 bytes (an instruction offset).
   // S^T reads: row (lane & 31) (+32 for the second tile), chunk half*DH/8 + 2 ks + kg.
-  constexpr int KSJ = (DH / 16) < 8 ? (DH / 16) : 8;
+  constexpr int KSJ = KS < 8 ? KS : 8;
   const int arow = lane & 31;
   int qk_off[KSJ];
 #pragma unroll
@@ -122,7 +134,7 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
   const int t0 = 4 * kg + ((lane & 15) >> 2);
   const int c0 = (half * DH + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) >> 3;
   const int hoff = (lane & 1) ? 8 : 0;
-  constexpr int NK = (DH / 32) < 4 ? (DH / 32) : 4;
+  constexpr int NK = NDT < 4 ? NDT : 4;
   int pv_off[2][NK];
 #pragma unroll
   for (int a = 0; a < 2; a++)
@@ -134,37 +146,50 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
 
   int32_t idx_cur = load_idx(0);
   uint64_t mask_cur = __ballot(slot_in_range(idx_cur, S_kv));
-  if (mask_cur) issue_tile(idx_cur, mask_cur, 0);
+  if (mask_cur) issue_tile(idx_cur, mask_cur, tile0);
   int32_t idx_nxt = nblk > 1 ? load_idx(1) : -1;
 
-  for (int blk = 0; blk < nblk; blk++) {
-    const int buf = blk & 1;
+  auto block = [&](auto buf_tag, int blk) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    const char* tile = BUF ? tile1 : tile0;
+    char* other = BUF ? tile0 : tile1;
     wait_all_mem();
     __syncthreads();  // tile blk is in LDS; every wave is done with block blk-1
     uint64_t mask_nxt = 0;
     if (blk + 1 < nblk) {
       mask_nxt = __ballot(slot_in_range(idx_nxt, S_kv));
-      if (mask_nxt) issue_tile(idx_nxt, mask_nxt, buf ^ 1);
+      if (mask_nxt) issue_tile(idx_nxt, mask_nxt, other);
     }
     idx_cur = idx_nxt;
     idx_nxt = blk + 2 < nblk ? load_idx(blk + 2) : -1;
     const uint64_t mask = mask_cur;
     mask_cur = mask_nxt;
-    if (mask == 0) continue;
+    if (mask == 0) return;
 
-    const char* tile = tiles + buf * TB;
-    // ---- partial S^T over this wave's half of D, for all 64 slots (two 32-slot tiles)
+    // ---- partial S^T over this wave's half of D, for all 64 slots (two 32-slot tiles).
+    // Fragment i = (ks, mt) = (i / 2, i % 2); PFS reads run ahead of their MFMAs, every stage
+    // fenced so the scheduler keeps that distance.
     f32x16 sacc[2];
 #pragma unroll
     for (int mt = 0; mt < 2; mt++)
 #pragma unroll
       for (int r = 0; r < 16; r++) sacc[mt][r] = 0.f;
+    {
+      constexpr int NF = 2 * KS, NB = PFS + 1;
+      auto sfrag = [&](int i) {
+        const int ks = i >> 1, mt = i & 1;
+        return lds_load16(tile + qk_off[ks % KSJ] + 256 * (ks / KSJ) + 32 * mt * ROWB);
+      };
+      bf16x8 fr[NB];
 #pragma unroll
-    for (int ks = 0; ks < DH / 16; ks++) {
-      const int off = qk_off[ks % KSJ] + 256 * (ks / KSJ);
+      for (int i = 0; i < PFS; i++) fr[i] = sfrag(i);
 #pragma unroll
-      for (int mt = 0; mt < 2; mt++)
-        sacc[mt] = mfma32(lds_load16(tile + off + 32 * mt * ROWB), qb[ks], sacc[mt]);
+      for (int i = 0; i < NF; i++) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + PFS < NF) fr[(i + PFS) % NB] = sfrag(i + PFS);
+        sacc[i & 1] = mfma32(fr[i % NB], qb[i >> 1], sacc[i & 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // ---- swap partial sums with the other half of the head group
 #pragma unroll
@@ -173,8 +198,19 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
       for (int r4 = 0; r4 < 4; r4++)
         xmine[(mt * 4 + r4) * 64 + lane] = make_float4(sacc[mt][4 * r4], sacc[mt][4 * r4 + 1],
                                                        sacc[mt][4 * r4 + 2], sacc[mt][4 * r4 + 3]);
-    __syncthreads();
-    float s2[2][16];
+    lds_barrier();  // partial sums visible; the next tile's gather stays in flight
+    // the first V fragments are read while the softmax below runs
+    constexpr int NBV = PFV + 1;
+    auto vfrag = [&](int i) {
+      // i = (k-step kk = (mt, j), d tile dt); k-step kk covers slots 16 kk .. 16 kk + 15
+      const int kk = i / NDT, dt = i % NDT;
+      const int imm = 16 * kk * ROWB + 256 * (dt / NK);
+      return join_tr(lds_load_tr(tile + pv_off[0][dt % NK] + imm), lds_load_tr(tile + pv_off[1][dt % NK] + imm));
+    };
+    bf16x8 fv[NBV];
+#pragma unroll
+    for (int i = 0; i < PFV; i++) fv[i] = vfrag(i);
+
     float bmax = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; mt++)
@@ -187,8 +223,8 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
           const int r = 4 * r4 + i;
           const int t = 32 * mt + 8 * r4 + 4 * kg + i;
           const float v = (sacc[mt][r] + ov[i]) * scale_log2;
-          s2[mt][r] = ((mask >> t) & 1ull) ? v : -INFINITY;
-          bmax = fmaxf(bmax, s2[mt][r]);
+          sacc[mt][r] = ((mask >> t) & 1ull) ? v : -INFINITY;
+          bmax = fmaxf(bmax, sacc[mt][r]);
         }
       }
     bmax = wave_max_xor32(bmax);  // block max of this head over the 64 slots
@@ -205,14 +241,14 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
     for (int mt = 0; mt < 2; mt++)
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        const float p = fast_exp2(s2[mt][r] - m_new);
+        const float p = fast_exp2(sacc[mt][r] - m_new);
         psum += p;
         pb[mt][r >> 3][r & 7] = (__bf16)p;
       }
     l_run = l_run * alpha + psum;
     if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int dt = 0; dt < DH / 32; dt++)
+      for (int dt = 0; dt < NDT; dt++)
 #pragma unroll
         for (int r = 0; r < 16; r++) oacc[dt][r] *= alpha;
     }
@@ -221,18 +257,17 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
     // k-order of step (mt, j): element e <-> slot 32 mt + 16 j + 8 (e>>2) + 4 kg + (e&3), the
     // C-layout order of S^T, so P needs no shuffle.
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-      for (int j = 0; j < 2; j++) {
-        const int rowb = (32 * mt + 16 * j) * ROWB;
-#pragma unroll
-        for (int dt = 0; dt < DH / 32; dt++) {
-          const int imm = rowb + 256 * (dt / NK);
-          const s16x4 lo = lds_load_tr(tile + pv_off[0][dt % NK] + imm);
-          const s16x4 hi = lds_load_tr(tile + pv_off[1][dt % NK] + imm);
-          oacc[dt] = mfma32(join_tr(lo, hi), pb[mt][j], oacc[dt]);
-        }
-      }
+    for (int i = 0; i < NFV; i++) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + PFV < NFV) fv[(i + PFV) % NBV] = vfrag(i + PFV);
+      const int kk = i / NDT, dt = i % NDT;
+      oacc[dt] = mfma32(fv[i % NBV], pb[kk >> 1][kk & 1], oacc[dt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int blk = 0; blk < nblk; blk += 2) {
+    block(IntTag<0>{}, blk);
+    if (blk + 1 < nblk) block(IntTag<1>{}, blk + 1);
   }
 
   // ---- epilogue: normalise, store O (bf16) and LSE (log2)
@@ -241,7 +276,7 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
   if (head_ok) {
     uint16_t* orow = out + (token * H + head) * (int64_t)D;
 #pragma unroll
-    for (int dt = 0; dt < DH / 32; dt++)
+    for (int dt = 0; dt < NDT; dt++)
 #pragma unroll
       for (int r4 = 0; r4 < 4; r4++) {
         const int d = half * DH + 32 * dt + 8 * r4 + 4 * kg;

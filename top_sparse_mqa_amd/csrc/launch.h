@@ -28,7 +28,8 @@ struct BwdMainArgs {
   void* dq;
   float* dkv_accum;       // atomic mode: pre-zeroed fp32 accumulator [B,S_kv,D]
   const int32_t* pos;     // staging mode: staging row of each slot of the chunk (-1 if masked)
-  float* stage;           // staging mode: contribution rows; nullptr selects atomic mode
+  uint16_t* stage;        // staging mode: contribution rows (fp16); nullptr selects atomic mode
+  int8_t* stage_exp;      // staging mode: one power-of-two exponent per 16 values of a row
   int64_t B, S, S_kv, H, D, topk;
   float sm_scale;
   int64_t token0;         // first token of the chunk (dKV kernel)
@@ -54,8 +55,8 @@ int64_t scan_tiles(int64_t n);
 // Number of rank counters (and scanned offsets, minus the final total) for n_rows kv rows.
 int64_t rank_counters(int64_t n_rows);
 // Per kv row: sum of its staging segment (+ acc if accumulate); writes acc (fp32) and/or out (bf16).
-hipError_t launch_reduce_rows(const float* stage, const int32_t* offset, float* acc, void* out_bf16,
-                              int accumulate, int64_t n_rows, int64_t D, hipStream_t st);
+hipError_t launch_reduce_rows(const uint16_t* stage, const int8_t* stage_exp, const int32_t* offset, float* acc,
+                              void* out_bf16, int accumulate, int64_t n_rows, int64_t D, hipStream_t st);
 hipError_t launch_bwd_postprocess(const float* acc, void* dkv, int64_t n, hipStream_t st);
 
 }  // namespace smqa
