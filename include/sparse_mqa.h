@@ -71,7 +71,7 @@ int sparse_mqa_fwd(const void* q, const void* kv, const float* attn_sink, const 
  * [B,S,H] fp32 (sparse_mqa_bwd only), per-row counters and offsets, and the staging rows of the
  * segmented dKV scatter-add (one row per valid (token, slot) pair and 64-head block, and one spare
  * row per token and head block that absorbs the stores of masked slots; a row is D fp16 values
- * with one power-of-two exponent per 16 values, summed in fp32).
+ * with one power-of-two exponent per segment of up to 128 values, summed in fp32).
  * sparse_mqa_bwd_workspace_bytes is the size for one pass over all tokens (an upper bound that
  * assumes every slot valid); any size >= sparse_mqa_bwd_workspace_min_bytes also works, and the
  * tokens are then processed in chunks with an fp32 running sum. Both return 0 for invalid sizes. */

@@ -82,9 +82,9 @@ def test_workspace_bytes(lib):
     fixed = r256((n_cnt + 4) * 4) + r256((n_cnt + 1) * 4) + r256(((n_cnt + 4095) // 4096) * 4)
     full = lib.sparse_mqa_bwd_workspace_bytes(B, S, S_kv, H, D, K)
     # staging: one row per slot plus one spare row per token (masked slots' stores land there); a
-    # row is D fp16 values plus one int8 exponent per 16 values, in two planes
+    # row is D fp16 values plus one int8 exponent per 128-value segment, in two planes
     def stage(rows):
-        return r256(rows * D * 2) + r256(rows * D // 16)
+        return r256(rows * D * 2) + r256(rows * (D // 128))
     assert full == r256(B * S * H * 4) + fixed + r256(B * S * K * 4) + stage(B * S * (K + 1)) + 512
     low = lib.sparse_mqa_bwd_workspace_min_bytes(B, S, S_kv, H, D, K)
     assert low == r256(B * S * H * 4) + fixed + r256(B * S_kv * D * 4) + r256(K * 4) + stage(K + 1) + 512
@@ -109,9 +109,9 @@ def test_bwd_validation(lib):
     assert bwd(lib, wsb=100) == WORKSPACE
     low = lib.sparse_mqa_bwd_workspace_min_bytes(1, 8, 16, 64, 512, 4)
     # the minimum passes validation (the launch then fails without a GPU); one token's staging
-    # (positions + 5 rows of 512 fp16 values and 32 exponents) less does not
+    # (positions + 5 rows of 512 fp16 values and 4 exponents) less does not
     assert bwd(lib, wsb=low, ws=0x7A000000) not in (WORKSPACE, ALIAS, ALIGN, NULL)
-    assert bwd(lib, wsb=low - (4 * 4 + 5 * (1024 + 32)), ws=0x7A000000) == WORKSPACE
+    assert bwd(lib, wsb=low - (4 * 4 + 5 * (1024 + 4)), ws=0x7A000000) == WORKSPACE
     assert bwd(lib, ws=G + 4) == ALIGN
     assert bwd(lib, dq=A) == ALIAS
     assert bwd(lib, dkv=0x71000000 + 64) == ALIAS

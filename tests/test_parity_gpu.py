@@ -170,7 +170,8 @@ def test_dkv_paths_agree(gpu_lib):
     one = smqa.bwd_dkv(*args)
     lib = smqa.load_library()
     low = lib.sparse_mqa_bwd_workspace_min_bytes(w.B, w.S, w.S_kv, w.H, w.D, w.topk)
-    per_tok = w.topk * 4 + (w.topk + 1) * (w.D * 2 + w.D // 16)  # positions, staging rows, spare row
+    # positions, staging rows (fp16 + one exponent per 128 values) and the spare row
+    per_tok = w.topk * 4 + (w.topk + 1) * (w.D * 2 + max(1, w.D // 128))
     for fp32 in (False, True):
         ws = torch.empty(low + 37 * per_tok, dtype=torch.uint8, device="cuda")  # 38 tokens per chunk
         chunked = smqa.bwd_dkv(*args, dkv_fp32=fp32, workspace=ws)

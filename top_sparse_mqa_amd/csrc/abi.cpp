@@ -122,12 +122,12 @@ size_t fixed_dkv_bytes(int64_t B, int64_t S_kv) {
          round256((size_t)smqa::scan_tiles(n_cnt) * 4);
 }
 
-// Bytes of one staging row: D fp16 values and D/16 int8 exponents (one per 16 values).
-size_t stage_row_bytes(int64_t D) { return (size_t)D * 2 + (size_t)D / 16; }
+// Bytes of one staging row: D fp16 values and one int8 exponent per segment.
+size_t stage_row_bytes(int64_t H, int64_t D) { return (size_t)D * 2 + (size_t)smqa::stage_segments(H, D); }
 // Per token: its slots' positions, one staging row per slot and head block, and one spare row per
 // head block that takes the stores of the token's masked slots.
 size_t per_token_dkv_bytes(int64_t H, int64_t D, int64_t topk) {
-  return (size_t)topk * 4 + (size_t)(topk + 1) * smqa::bwd_hblocks(H) * stage_row_bytes(D);
+  return (size_t)topk * 4 + (size_t)(topk + 1) * smqa::bwd_hblocks(H) * stage_row_bytes(H, D);
 }
 
 // Lay out the dKV part of the workspace starting at `base`; false if `bytes` cannot hold even one
@@ -165,7 +165,7 @@ bool plan_dkv(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t 
   p->stage = o;
   o += round256(rows * D * 2);
   p->stage_exp = o;
-  o += round256(rows * (D / 16));
+  o += round256(rows * smqa::stage_segments(H, D));
   p->end = o;
   return o <= bytes;
 }
@@ -198,7 +198,8 @@ int run_dkv(const void* q, const void* kv, const void* d_o, const int32_t* idx, 
     if (smqa::launch_bwd_main(a, 2, st) != hipSuccess) return SMQA_ERR_HIP;
     const bool last = t0 + n >= tokens;
     void* out16 = (!dkv_fp32 && last) ? dkv : nullptr;
-    if (smqa::launch_reduce_rows(stage, stage_exp, offset, acc, out16, t0 > 0 ? 1 : 0, n_rows, D, st) != hipSuccess)
+    if (smqa::launch_reduce_rows(stage, stage_exp, smqa::stage_segments(H, D), offset, acc, out16, t0 > 0 ? 1 : 0,
+                                 n_rows, D, st) != hipSuccess)
       return SMQA_ERR_HIP;
   }
   return SMQA_OK;
@@ -222,14 +223,14 @@ size_t sparse_mqa_bwd_workspace_bytes(int64_t B, int64_t S, int64_t S_kv, int64_
   if (!sizes_ok(B, S, S_kv, H, D, topk)) return 0;
   return delta_bytes(B, S, H) + fixed_dkv_bytes(B, S_kv) + round256((size_t)(B * S) * topk * 4) +
          round256((size_t)(B * S) * (topk + 1) * smqa::bwd_hblocks(H) * D * 2) +
-         round256((size_t)(B * S) * (topk + 1) * smqa::bwd_hblocks(H) * (D / 16)) + 512;
+         round256((size_t)(B * S) * (topk + 1) * smqa::bwd_hblocks(H) * smqa::stage_segments(H, D)) + 512;
 }
 
 size_t sparse_mqa_bwd_workspace_min_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk) {
   if (!sizes_ok(B, S, S_kv, H, D, topk)) return 0;
   return delta_bytes(B, S, H) + fixed_dkv_bytes(B, S_kv) + round256((size_t)(B * S_kv) * D * 4) +
          round256((size_t)topk * 4) + round256((size_t)(topk + 1) * smqa::bwd_hblocks(H) * D * 2) +
-         round256((size_t)(topk + 1) * smqa::bwd_hblocks(H) * (D / 16)) + 512;
+         round256((size_t)(topk + 1) * smqa::bwd_hblocks(H) * smqa::stage_segments(H, D)) + 512;
 }
 
 int sparse_mqa_bwd_preprocess(const void* o, const void* d_o, float* delta, int64_t B, int64_t S, int64_t H,

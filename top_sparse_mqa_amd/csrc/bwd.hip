@@ -32,21 +32,23 @@ __device__ __forceinline__ int bwd_off(int row, int chunk) {
   return row * (D * 2) + ((chunk ^ (bwd_swz(row) & (D / 8 - 1))) << 4);
 }
 
-// Staging rows hold D fp16 values and D/16 int8 exponents: value = fp16 * 2^e, one e per 16
-// consecutive values (the exponent of their largest magnitude, so the fp16 parts lie in (-1, 1)).
-// This halves the traffic of the staged scatter-add against fp32 rows; a value keeps 11 significant
-// bits relative to its group maximum. One lane stores 4 values; the 16-value group is a hardware
-// quad of lanes (all 64 lanes must execute this), whose first lane also stores the exponent.
-template <int D>
-__device__ __forceinline__ void stage_store4(uint16_t* stage, int8_t* stage_exp, int32_t row, int d, f32x4 v, int lane) {
-  const float m = quad_max(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
-  int e = (m > 0.f && m <= 3.4028235e38f) ? __builtin_amdgcn_frexp_expf(m) : 0;  // m < 2^e
-  e = e < -127 ? -127 : (e > 127 ? 127 : e);
-  f16x4 h;
+// Staging rows hold D fp16 values plus one int8 exponent per segment of SEG values: value =
+// fp16 * 2^e. A wave stores segment-wide pieces of 32 rows at once (its d-range of one block) and
+// picks one exponent for all of them: 0 while the largest magnitude m lies in [2^-10, 2^14) --
+// there fp16 keeps 11 significant bits down to m / 16 and smaller values err by at most 2^-25 --
+// else the one that brings m to [2^13, 2^14). This halves the traffic of the staged scatter-add
+// against fp32 rows.
+__device__ __forceinline__ int stage_exponent(float m) {
+  if (!(m > 0.f && m <= 3.4028235e38f)) return 0;  // zero, inf or NaN: stored as is
+  if (m >= 0.0009765625f && m < 16384.f) return 0;
+  int e = __builtin_amdgcn_frexp_expf(m) - 14;      // m < 2^(e + 14)
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+// Maximum over the wave.
+__device__ __forceinline__ float wave_max(float m) {
 #pragma unroll
-  for (int k = 0; k < 4; k++) h[k] = (_Float16)__builtin_amdgcn_ldexpf(v[k], -e);
-  __builtin_nontemporal_store(__builtin_bit_cast(i32x2, h), (i32x2*)(stage + (int64_t)row * D + d));
-  if ((lane & 3) == 0) stage_exp[(int64_t)row * (D / 16) + (d >> 4)] = (int8_t)e;
+  for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  return m;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -289,13 +291,15 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
     for (int i = 0; i < PFQ; i++) fq[i] = dfrag(i);
 
     // dS as the B operand of dQ^T = K^T dS^T: element e <-> slot 4g + e (e < 4), 16 + 4g + e - 4.
+    // validity of this lane's slots 4g + r (bit r) and 16 + 4g + r (bit 16 + r); extracting the
+    // lane's bits with one variable shift keeps the compiler from hoisting per-slot 64-bit masks
+    const uint32_t vb = (uint32_t)(mask >> (4 * g));
     bf16x8 dsb;
 #pragma unroll
     for (int mt = 0; mt < 2; mt++)
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        const int t = 16 * mt + 4 * g + r;
-        const float p = ((mask >> t) & 1ull) ? fast_exp2(sacc[mt][r] * scale_log2 - lse_h) : 0.f;
+        const float p = ((vb >> (16 * mt + r)) & 1u) ? fast_exp2(sacc[mt][r] * scale_log2 - lse_h) : 0.f;
         dsb[4 * mt + r] = (__bf16)(p * (dpacc[mt][r] - delta_h));
       }
 #pragma unroll
@@ -346,10 +350,14 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
   // back as whole row segments, so each 16-byte store covers DG*128 contiguous bytes of a row.
   // The row pitch is padded by 32 bytes: the two half-waves of a column write (slots 4 apart) then
   // fall on disjoint banks.
-  constexpr int OP = DG * 128 + 32;
+  // The transpose holds fp16 (the staging format); the row pitch is padded by 16 bytes so the two
+  // half-waves of a column write (slots 4 apart) fall on disjoint banks.
+  constexpr int SEGW = DG * 32;         // d values per wave group = one staging exponent segment
+  constexpr int NSEG = D / SEGW;        // exponents per staging row
+  constexpr int OP = SEGW * 2 + 16;
   __shared__ __attribute__((aligned(16))) char obuf[NW][T * OP];
-  // read-back geometry of the transpose: RPS slot rows of LPR lanes per instruction
-  constexpr int LPR = DG * 8, RPS = 64 / LPR, NI = T / RPS;
+  // read-back geometry of the transpose: RPS slot rows of LPR lanes (16 bytes each) per instruction
+  constexpr int LPR = SEGW / 8, RPS = 64 / LPR, NI = T / RPS;
   // With one d group per wave the stores of a block are deferred: the block leaves its rows in
   // obuf (and their staging row indices in obdst) and the next block issues them from inside its
   // score loop, one every other stage. A wave issues in order, so stores issued in one burst
@@ -458,33 +466,48 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
   wait_all_mem();
 
   // Deferred staging stores (stage mode, one d group): row k of the previous block's transpose
-  // buffer goes to staging row obdst[k * RPS + lane / LPR]. Reads of row k run in score stage 2k,
-  // its store in stage 2k + 7 (a ring of four rows in flight); the rest are flushed after the loop.
+  // buffer goes to staging row obdst[k * RPS + lane / LPR]. Row k is read in score stage 2k and
+  // stored in stage 2k + 1 (more rows in flight push this kernel past its registers); the segment
+  // exponents of the 32 rows go out in stage 1; the rest is flushed after the loop.
   bool pending = false;
-  const int dlane = w * DW + 4 * (lane % LPR);  // first d of this lane's 4 values
-  f32x4 dv[4];
-  int32_t dd[4];
+  int pending_e = 0;
+  const int dlane = w * DW + 8 * (lane % LPR);  // first d of this lane's 8 values
+  i32x4 dv[1];
+  int32_t dd[1];
+  int32_t ddx = 0;
   auto dread = [&](int k) {
-    dv[k & 3] = *(const f32x4*)(obuf[w] + (k * RPS + lane / LPR) * OP + 16 * (lane % LPR));
-    dd[k & 3] = obdst[w][k * RPS + lane / LPR];
+    dv[0] = *(const i32x4*)(obuf[w] + (k * RPS + lane / LPR) * OP + 16 * (lane % LPR));
+    dd[0] = obdst[w][k * RPS + lane / LPR];
   };
-  auto dstore = [&](int k) { stage_store4<D>(stage, stage_exp, dd[k & 3], dlane, dv[k & 3], lane); };
+  auto dstore = [&](int k) {
+    __builtin_nontemporal_store(dv[0], (i32x4*)(stage + (int64_t)dd[0] * D + dlane));
+  };
+  auto eread = [&]() { ddx = obdst[w][lane & 31]; };
+  auto estore = [&]() {
+    if (lane < T) stage_exp[(int64_t)ddx * NSEG + w * (DW / SEGW)] = (int8_t)pending_e;
+  };
   constexpr int NFS = 2 * C::KS;  // score stages
   auto store_hook = [&](int i) {
     if constexpr (DEFER) {
       if (!pending) return;
+      if (i == 0) eread();
+      if (i == 1) estore();
       if ((i & 1) == 0 && i / 2 < NI) dread(i / 2);
-      if ((i & 1) == 1 && i >= 7 && (i - 7) / 2 < NI) dstore((i - 7) / 2);
+      if ((i & 1) == 1 && (i - 1) / 2 < NI) dstore((i - 1) / 2);
     }
   };
-  // issues whatever the hook did not: reads for rows with 2k >= NFS, stores for rows with 2k+7 >= NFS
+  // issues whatever the hook did not
   auto flush_pending = [&](bool after_scores) {
     if constexpr (DEFER) {
       if (!pending) return;
+      if (!(after_scores && NFS > 1)) {
+        eread();
+        estore();
+      }
 #pragma unroll
       for (int k = 0; k < NI; k++) {
         const bool read_done = after_scores && 2 * k < NFS;
-        const bool store_done = after_scores && 2 * k + 7 < NFS;
+        const bool store_done = after_scores && 2 * k + 1 < NFS;
         if (store_done) continue;
         if (!read_done) dread(k);
         dstore(k);
@@ -523,13 +546,14 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
     f32x4 sacc[2], dpacc[2];
     bwd_scores<D, PF>(tile, sc_off, qb, dob, sacc, dpacc, store_hook);
     flush_pending(true);
+    // validity of this lane's slots 4g + r (bit r) and 16 + 4g + r (bit 16 + r), one variable shift
+    const uint32_t vb = (uint32_t)(mask >> (4 * g));
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) {
       float p[4], ds[4], plr[4], dslr[4];
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        const int t = 16 * mt + 4 * g + r;
-        p[r] = ((mask >> t) & 1ull) ? fast_exp2(sacc[mt][r] * scale_log2 - lse_h) : 0.f;
+        p[r] = ((vb >> (16 * mt + r)) & 1u) ? fast_exp2(sacc[mt][r] * scale_log2 - lse_h) : 0.f;
         ds[r] = sm_scale * p[r] * (dpacc[mt][r] - delta_h);
         plr[r] = p[r] - (float)(__bf16)p[r];
         dslr[r] = ds[r] - (float)(__bf16)ds[r];
@@ -596,34 +620,50 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
       }
       __builtin_amdgcn_sched_barrier(0);
       if (stage) {
-        // column writes into this wave's transpose buffer (slot row t, d column 32 i + lane & 31)
+        // one exponent for this wave's 32 rows of the group, then fp16 column writes into this
+        // wave's transpose buffer (slot row t, d column 32 i + lane & 31)
+        float m = 0.f;
+#pragma unroll
+        for (int i = 0; i < DG; i++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) m = fmaxf(m, fabsf(c[i][r]));
+        const int e = stage_exponent(wave_max(m));
+        if (e != 0) {
+#pragma unroll
+          for (int i = 0; i < DG; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) c[i][r] = __builtin_amdgcn_ldexpf(c[i][r], -e);
+        }
 #pragma unroll
         for (int i = 0; i < DG; i++)
 #pragma unroll
           for (int r = 0; r < 16; r++) {
             const int t = 8 * (r >> 2) + 4 * kg + (r & 3);
-            *(float*)(ob + t * OP + (32 * i + (lane & 31)) * 4) = c[i][r];
+            *(_Float16*)(ob + t * OP + (32 * i + (lane & 31)) * 2) = (_Float16)c[i][r];
           }
         if constexpr (DEFER) {
           if (lane < T) obdst[w][lane] = dst_this;
           wait_all_mem();  // this wave's part of tile blk + 1
           pending = true;
+          pending_e = e;
           continue;
         }
         if (dg == NDT / DG - 1) wait_all_mem();  // this wave's part of tile blk + 1
-        // row reads: lane covers 4 consecutive d of slot row n*RPS + lane/LPR
-        const int d0 = w * DW + 32 * dg * DG + 4 * (lane % LPR);
+        // row reads: lane covers 8 consecutive d of slot row n*RPS + lane/LPR
+        const int d0 = w * DW + SEGW * dg + 8 * (lane % LPR);
 #pragma unroll
         for (int n = 0; n < NI; n++) {
-          const f32x4 v = *(const f32x4*)(ob + (n * RPS + lane / LPR) * OP + 16 * (lane % LPR));
-          stage_store4<D>(stage, stage_exp, rowi[n], d0, v, lane);
+          const i32x4 v = *(const i32x4*)(ob + (n * RPS + lane / LPR) * OP + 16 * (lane % LPR));
+          __builtin_nontemporal_store(v, (i32x4*)(stage + (int64_t)rowi[n] * D + d0));
         }
+        // the group's exponent for its 32 rows (row indices as the lanes below 32 hold them)
+        if (lane < T) stage_exp[(int64_t)dst_this * NSEG + (w * DW + SEGW * dg) / SEGW] = (int8_t)e;
       } else {
         if (dg == NDT / DG - 1) wait_all_mem();  // this wave's part of tile blk + 1
+        const uint32_t vk = (uint32_t)(mask >> (4 * kg));  // bit 8 (r>>2) + (r&3): slot of C row r
 #pragma unroll
         for (int r = 0; r < 16; r++) {
-          const int t = 8 * (r >> 2) + 4 * kg + (r & 3);
-          if ((mask >> t) & 1ull) {
+          if ((vk >> (8 * (r >> 2) + (r & 3))) & 1u) {
             float* p = outb + (int64_t)rowi[r] * D + 32 * dg * DG;
 #pragma unroll
             for (int i = 0; i < DG; i++) unsafeAtomicAdd(p + 32 * i, c[i][r]);
@@ -757,7 +797,7 @@ scan_add_kernel(int32_t* __restrict__ out, const int32_t* __restrict__ tile_sum,
 // the running accumulator (earlier token chunks), then write fp32 and/or bf16 output.
 template <int D>
 __global__ void __launch_bounds__(256)
-reduce_rows_kernel(const uint16_t* __restrict__ stage, const int8_t* __restrict__ stage_exp,
+reduce_rows_kernel(const uint16_t* __restrict__ stage, const int8_t* __restrict__ stage_exp, int nseg,
                    const int32_t* __restrict__ offset, f32x4* __restrict__ acc, uint4* __restrict__ out_bf16,
                    int accumulate) {
   // offset is indexed by (row, sub): the row's segment is [offset[row*RANK_SUB], offset[(row+1)*RANK_SUB]).
@@ -779,7 +819,8 @@ reduce_rows_kernel(const uint16_t* __restrict__ stage, const int8_t* __restrict_
     }
   };
   auto ld = [&](int32_t i) { return __builtin_nontemporal_load((const i32x4*)(stage + (int64_t)i * D) + c); };
-  auto lde = [&](int32_t i) { return (int)stage_exp[(int64_t)i * (D / 16) + (c >> 1)]; };
+  const int seg = 8 * c * nseg / D;  // exponent segment of this thread's 8 values
+  auto lde = [&](int32_t i) { return (int)stage_exp[(int64_t)i * nseg + seg]; };
   int32_t i = beg + g;
   for (; i + 3 * NG < end; i += 4 * NG) {
     const i32x4 r0 = ld(i), r1 = ld(i + NG), r2 = ld(i + 2 * NG), r3 = ld(i + 3 * NG);
@@ -913,14 +954,14 @@ hipError_t launch_dkv_prepare(const int32_t* idx, int32_t* count, int32_t* offse
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_rows(const uint16_t* stage, const int8_t* stage_exp, const int32_t* offset, float* acc,
-                              void* out_bf16, int accumulate, int64_t n_rows, int64_t D, hipStream_t st) {
+hipError_t launch_reduce_rows(const uint16_t* stage, const int8_t* stage_exp, int nseg, const int32_t* offset,
+                              float* acc, void* out_bf16, int accumulate, int64_t n_rows, int64_t D, hipStream_t st) {
   if (D == 512)
-    hipLaunchKernelGGL(reduce_rows_kernel<512>, dim3((unsigned)n_rows), dim3(256), 0, st, stage, stage_exp, offset,
-                       (f32x4*)acc, (uint4*)out_bf16, accumulate);
+    hipLaunchKernelGGL(reduce_rows_kernel<512>, dim3((unsigned)n_rows), dim3(256), 0, st, stage, stage_exp, nseg,
+                       offset, (f32x4*)acc, (uint4*)out_bf16, accumulate);
   else if (D == 64)
-    hipLaunchKernelGGL(reduce_rows_kernel<64>, dim3((unsigned)n_rows), dim3(256), 0, st, stage, stage_exp, offset,
-                       (f32x4*)acc, (uint4*)out_bf16, accumulate);
+    hipLaunchKernelGGL(reduce_rows_kernel<64>, dim3((unsigned)n_rows), dim3(256), 0, st, stage, stage_exp, nseg,
+                       offset, (f32x4*)acc, (uint4*)out_bf16, accumulate);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

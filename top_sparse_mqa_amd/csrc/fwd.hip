@@ -212,6 +212,9 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
     for (int i = 0; i < PFV; i++) fv[i] = vfrag(i);
 
     float bmax = -INFINITY;
+    // validity of this lane's slots, bit 32 mt + 8 r4 + i for C element (mt, 4 r4 + i); one
+    // variable shift keeps the compiler from hoisting per-slot 64-bit masks out of the loop
+    const uint64_t vb = mask >> (4 * kg);
 #pragma unroll
     for (int mt = 0; mt < 2; mt++)
 #pragma unroll
@@ -221,9 +224,8 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const int r = 4 * r4 + i;
-          const int t = 32 * mt + 8 * r4 + 4 * kg + i;
           const float v = (sacc[mt][r] + ov[i]) * scale_log2;
-          sacc[mt][r] = ((mask >> t) & 1ull) ? v : -INFINITY;
+          sacc[mt][r] = ((vb >> (32 * mt + 8 * r4 + i)) & 1ull) ? v : -INFINITY;
           bmax = fmaxf(bmax, sacc[mt][r]);
         }
       }

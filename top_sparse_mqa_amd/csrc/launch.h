@@ -29,7 +29,7 @@ struct BwdMainArgs {
   float* dkv_accum;       // atomic mode: pre-zeroed fp32 accumulator [B,S_kv,D]
   const int32_t* pos;     // staging mode: staging row of each slot of the chunk (-1 if masked)
   uint16_t* stage;        // staging mode: contribution rows (fp16); nullptr selects atomic mode
-  int8_t* stage_exp;      // staging mode: one power-of-two exponent per 16 values of a row
+  int8_t* stage_exp;      // staging mode: one power-of-two exponent per row segment (stage_segments)
   int64_t B, S, S_kv, H, D, topk;
   float sm_scale;
   int64_t token0;         // first token of the chunk (dKV kernel)
@@ -39,6 +39,11 @@ struct BwdMainArgs {
 // Heads handled by one backward workgroup, and workgroups per token.
 inline int bwd_heads_per_wg(int64_t H) { return H >= 64 ? 64 : (int)H; }
 inline int bwd_hblocks(int64_t H) { return (int)(H / bwd_heads_per_wg(H)); }
+// Exponent segments per staging row: one per min(128, d-range of a backward wave) values.
+inline int stage_segments(int64_t H, int64_t D) {
+  const int64_t dw = D / (bwd_heads_per_wg(H) / 16);
+  return (int)(D / (dw < 128 ? dw : 128));
+}
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_preprocess(const void* o, const void* d_o, float* delta, int64_t rows, int64_t D,
@@ -55,8 +60,8 @@ int64_t scan_tiles(int64_t n);
 // Number of rank counters (and scanned offsets, minus the final total) for n_rows kv rows.
 int64_t rank_counters(int64_t n_rows);
 // Per kv row: sum of its staging segment (+ acc if accumulate); writes acc (fp32) and/or out (bf16).
-hipError_t launch_reduce_rows(const uint16_t* stage, const int8_t* stage_exp, const int32_t* offset, float* acc,
-                              void* out_bf16, int accumulate, int64_t n_rows, int64_t D, hipStream_t st);
+hipError_t launch_reduce_rows(const uint16_t* stage, const int8_t* stage_exp, int nseg, const int32_t* offset,
+                              float* acc, void* out_bf16, int accumulate, int64_t n_rows, int64_t D, hipStream_t st);
 hipError_t launch_bwd_postprocess(const float* acc, void* dkv, int64_t n, hipStream_t st);
 
 }  // namespace smqa
