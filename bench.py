@@ -9,9 +9,18 @@ reduction that also emits the bf16 dKV). Inputs are resident in HBM before timin
 Prints one JSON line. `value` is the step's algorithmic TFLOP/s: (4 + 10) * H * D flops per valid
 (token, slot) pair (forward 4HD: QK^T and PV; backward 10HD: score recompute, dP, dQ, dKV) divided
 by the measured step time. Per-kernel times come from HIP events recorded on the stream the
-kernels run on.
+kernels run on; the dKV stage runs as its three library steps (prepare, partials, reduce) so the
+partials kernel is timed alone.
+
+`roofline` is for the longest single-kernel step, with its own algorithmic flops per valid pair
+(forward 4HD; dQ kernel 6HD: S and dP recompute, dQ; dKV partials kernel 8HD: S and dP recompute,
+dS^T Q and P^T dO). `traffic` is that kernel's HBM bytes per launch from the rocprofv3 FETCH_SIZE
+and WRITE_SIZE summary under profiles/, scaled by the same counters' reading for a copy of known
+size, and null once the kernel source differs from the one the counters were taken on.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                  [--calibration-copy]
+  python bench.py --summarize-pmc FETCH.csv WRITE.csv --out profiles/hbm_traffic_<workload>.md
 """
 from __future__ import annotations
 
@@ -27,7 +36,16 @@ import torch
 METRIC = "sparse-MQA fwd/bwd TFLOP/s and % bf16 MFMA peak @ H=64 D=512 topk=2048"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
-KERNELS = ("fwd", "bwd_preprocess", "bwd_dq", "bwd_dkv")
+KERNELS = ("fwd", "bwd_preprocess", "bwd_dq", "bwd_dkv_prepare", "bwd_dkv_partials", "bwd_dkv_reduce")
+# single-kernel steps: rocprofv3 kernel name prefix, source files, algorithmic flops per valid pair / (H*D)
+SINGLE = {
+    "fwd": ("smqa::fwd_kernel", ("fwd.hip", "device_common.h"), 4),
+    "bwd_dq": ("smqa::bwd_dq_kernel", ("bwd.hip", "device_common.h"), 6),
+    "bwd_dkv_partials": ("smqa::bwd_dkv_kernel", ("bwd.hip", "device_common.h"), 8),
+}
+CALIB_BYTES = 1 << 30        # the calibration copy reads and writes this many bytes
+CALIB_KERNEL = "MulFunctor"  # part of the name of the kernel torch.mul(src, 1.0, out=dst) runs
+REPO = os.path.dirname(os.path.abspath(__file__))
 
 
 def parse():
@@ -37,6 +55,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="causal_h64_d512_k2048")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibration-copy", action="store_true",
+                   help="run one 1 GiB copy kernel before the warmup (reference for the HBM byte counters)")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="write the HBM traffic summary from two rocprofv3 --pmc counter_collection.csv files")
+    p.add_argument("--out", help="output file of --summarize-pmc")
     return p.parse_args()
 
 
@@ -58,7 +81,8 @@ class Step:
         self.delta = torch.empty((B, S, H), dtype=torch.float32, device=dev)
         self.dq = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev)
         self.dkv = torch.empty((B, S_kv, D), dtype=torch.bfloat16, device=dev)
-        self.ws_bytes = smqa.bwd_workspace_bytes(B, S, S_kv, H, D, w.topk)
+        # one pass over all tokens (the dKV steps need it)
+        self.ws_bytes = self.lib.sparse_mqa_bwd_workspace_bytes(B, S, S_kv, H, D, w.topk)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
         self.stream = torch.cuda.current_stream()
         self.events = []  # one {kernel: (start, end)} per timed step
@@ -78,9 +102,13 @@ class Step:
             "bwd_preprocess": lambda: L.sparse_mqa_bwd_preprocess(p(self.o), p(self.do), p(self.delta), B, S, H, D, h),
             "bwd_dq": lambda: L.sparse_mqa_bwd_dq(p(self.q), p(self.kv), p(self.do), p(self.idx), p(self.lse),
                                                   p(self.delta), p(self.dq), B, S, S_kv, H, D, K, self.nan, h),
-            "bwd_dkv": lambda: L.sparse_mqa_bwd_dkv(p(self.q), p(self.kv), p(self.do), p(self.idx), p(self.lse),
-                                                    p(self.delta), p(self.dkv), 0, p(self.ws), self.ws_bytes,
-                                                    B, S, S_kv, H, D, K, self.nan, h),
+            "bwd_dkv_prepare": lambda: L.sparse_mqa_bwd_dkv_prepare(p(self.idx), p(self.ws), self.ws_bytes,
+                                                                    B, S, S_kv, H, D, K, h),
+            "bwd_dkv_partials": lambda: L.sparse_mqa_bwd_dkv_partials(
+                p(self.q), p(self.kv), p(self.do), p(self.idx), p(self.lse), p(self.delta), p(self.ws),
+                self.ws_bytes, B, S, S_kv, H, D, K, self.nan, h),
+            "bwd_dkv_reduce": lambda: L.sparse_mqa_bwd_dkv_reduce(p(self.dkv), 0, p(self.ws), self.ws_bytes,
+                                                                  B, S, S_kv, H, D, K, h),
         }
         ev = {}
         for k in KERNELS:
@@ -99,14 +127,95 @@ class Step:
         return {k: sum(e[k][0].elapsed_time(e[k][1]) for e in self.events) / n for k in KERNELS}
 
 
+def source_sha256(files) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(REPO, "top_sparse_mqa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, out_path: str, workload: str) -> None:
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel from two rocprofv3 --pmc runs,
+    scaled by the same counters' reading for the calibration copy (CALIB_BYTES read and written)."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: statistics.mean(v) for k, v in vals.items()}
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    calib = [k for k in fetch if CALIB_KERNEL in k]
+    if not calib:
+        raise SystemExit("no calibration copy kernel in the counter files (run with --calibration-copy)")
+    f_scale = CALIB_BYTES / (fetch[calib[0]] * 1024.0)
+    w_scale = CALIB_BYTES / (write[calib[0]] * 1024.0)
+    kernels = {}
+    for step, (prefix, files, _) in SINGLE.items():
+        names = [k for k in fetch if k.startswith("void " + prefix) or k.startswith(prefix)]
+        if not names:
+            continue
+        k = names[0]
+        kernels[step] = {"kernel": k.split("(")[0].replace("void ", ""),
+                         "fetch_bytes": round(fetch[k] * 1024.0 * f_scale),
+                         "write_bytes": round(write.get(k, 0.0) * 1024.0 * w_scale),
+                         "source_sha256": source_sha256(files)}
+    summary = {"workload": workload, "calibration": {"bytes": CALIB_BYTES, "fetch_KiB": fetch[calib[0]],
+                                                     "write_KiB": write[calib[0]], "fetch_scale": f_scale,
+                                                     "write_scale": w_scale},
+               "kernels": kernels}
+    lines = [f"# HBM traffic per launch: {workload}", "",
+             "rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), two separate runs, averaged per kernel,",
+             f"each scaled by the same counter's reading for a copy kernel that reads and writes {CALIB_BYTES} bytes.",
+             "", "Commands (from the repository root on one MI355X; `<out>` an output directory):", "", "```",
+             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/fetch -o pmc -- python bench.py --workload "
+             f"{workload} --steps 2 --warmup 1 --no-cpu-baseline --calibration-copy",
+             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/write -o pmc -- python bench.py --workload "
+             f"{workload} --steps 2 --warmup 1 --no-cpu-baseline --calibration-copy",
+             "python bench.py --summarize-pmc <out>/fetch/pmc_counter_collection.csv "
+             f"<out>/write/pmc_counter_collection.csv --workload {workload} --out <this file>", "```", "",
+             "| step | kernel | fetch (GB) | write (GB) |", "|---|---|---|---|"]
+    for step, k in kernels.items():
+        lines.append(f"| {step} | `{k['kernel']}` | {k['fetch_bytes'] / 1e9:.3f} | {k['write_bytes'] / 1e9:.3f} |")
+    lines += ["", f"Calibration: copy read {fetch[calib[0]]:.0f} KiB and wrote {write[calib[0]]:.0f} KiB for "
+              f"{CALIB_BYTES // 1024} KiB each (scales {f_scale:.4f}, {w_scale:.4f}).", "",
+              "Machine-readable (bench.py reads this block):", "", "```json", json.dumps(summary, indent=1), "```"]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def traffic_for(step: str, workload: str):
+    """HBM bytes per launch of a single-kernel step from the committed summary, or None when there
+    is none for this workload or the kernel source changed since the counters were taken."""
+    path = os.path.join(REPO, "profiles", f"hbm_traffic_{workload}.md")
+    if step not in SINGLE or not os.path.exists(path):
+        return None
+    text = open(path).read()
+    try:
+        block = text.split("```json", 1)[1].split("```", 1)[0]
+        k = json.loads(block)["kernels"][step]
+    except (IndexError, KeyError, ValueError):
+        return None
+    if k["source_sha256"] != source_sha256(SINGLE[step][1]):
+        return None
+    return k["fetch_bytes"] + k["write_bytes"]
+
+
 def cpu_baseline(x, w, valid_per_token):
     """The oracle as it stands, on a bounded sample of the same workload (about 10 s of CPU work at
-    the headline shape): forward and dQ for the last 2048 tokens, dKV for the first 512 kv rows."""
+    the headline shape): forward and dQ for all tokens (at most 4096), dKV for the first 1536 kv rows."""
     import oracle
 
-    n_tok = min(2048, w.B * w.S)
+    n_tok = min(4096, w.B * w.S)
     toks = list(range(w.B * w.S - n_tok, w.B * w.S))
-    rows = list(range(0, min(512, w.B * w.S_kv)))
+    rows = list(range(0, min(1536, w.B * w.S_kv)))
     t0 = time.perf_counter()
     o, lse = oracle.fwd(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], tokens=toks)
     O = torch.zeros(w.B * w.S, w.H, w.D, dtype=torch.bfloat16)
@@ -137,9 +246,14 @@ def cpu_baseline(x, w, valid_per_token):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        if not args.out:
+            raise SystemExit("--summarize-pmc needs --out")
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.out, args.workload)
+        return
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}); multi-GPU runs are not part of "
-              "this build", file=sys.stderr)
+        print(f"bench.py measures one GPU (got --gpus {args.gpus}): the kernels run on a single device and "
+              "no multi-GPU path exists", file=sys.stderr)
         sys.exit(2)
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     import top_sparse_mqa_amd as smqa
@@ -153,6 +267,12 @@ def main():
     valid = ((x["topk_idxs"] >= 0) & (x["topk_idxs"] < w.S_kv)).sum(-1).view(-1)
     n_valid = int(valid.sum())
     step = Step(smqa, w, x)
+    if args.calibration_copy:
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step.run(timed=False)
     torch.cuda.synchronize()
@@ -172,12 +292,11 @@ def main():
     HD = w.H * w.D
     fl_fwd = 4 * HD * n_valid
     fl_bwd = 10 * HD * n_valid
-    fl_kernel = {"fwd": fl_fwd, "bwd_dq": 6 * HD * n_valid, "bwd_dkv": 4 * HD * n_valid}
     ms_fwd = ms["fwd"]
     ms_bwd = sum(ms[k] for k in KERNELS if k.startswith("bwd"))
     tflops = (fl_fwd + fl_bwd) / (ms_step * 1e-3) / 1e12
-    dom = max(("fwd", "bwd_dq", "bwd_dkv"), key=lambda k: ms[k])
-    ach = fl_kernel[dom] / (ms[dom] * 1e-3) / 1e12
+    dom = max(SINGLE, key=lambda k: ms[k])
+    ach = SINGLE[dom][2] * HD * n_valid / (ms[dom] * 1e-3) / 1e12
     out = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -209,10 +328,12 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic_for(dom, args.workload),
         },
     }
-    out["dkv_scatter_payload_TBps"] = round(n_valid * w.D * 4 / (ms["bwd_dkv"] * 1e-3) / 1e12, 3)
+    # staged dKV rows written by the partials kernel: D fp16 values per valid pair and head block
+    out["dkv_staging_write_TBps"] = round(n_valid * (w.H // min(w.H, 64)) * 2 * w.D / (ms["bwd_dkv_partials"] * 1e-3)
+                                          / 1e12, 3)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, w, valid)
     print(json.dumps(out), flush=True)

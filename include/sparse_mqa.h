@@ -108,6 +108,25 @@ int sparse_mqa_bwd_dkv(const void* q, const void* kv, const void* d_o, const int
                        size_t workspace_bytes, int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D,
                        int64_t topk, float sm_scale, void* stream);
 
+/* The three steps of sparse_mqa_bwd_dkv for a single pass, for callers that schedule or time them
+ * separately (bwd page, bwd factory: the dKV scatter-add). They need a workspace that holds every
+ * token (at least sparse_mqa_bwd_workspace_bytes minus Delta's bytes; SMQA_ERR_WORKSPACE otherwise)
+ * and must be enqueued in this order on one stream with the same workspace and sizes:
+ *   prepare   ranks each valid slot within its kv row and assigns its staging row;
+ *   partials  computes every valid slot's dKV contribution row into the staging rows;
+ *   reduce    sums each kv row's staging rows and writes dkv (bf16, or fp32 if dkv_fp32). */
+int sparse_mqa_bwd_dkv_prepare(const int32_t* topk_idxs, void* workspace, size_t workspace_bytes,
+                               int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk,
+                               void* stream);
+int sparse_mqa_bwd_dkv_partials(const void* q, const void* kv, const void* d_o,
+                                const int32_t* topk_idxs, const float* lse, const float* delta,
+                                void* workspace, size_t workspace_bytes, int64_t B, int64_t S,
+                                int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale,
+                                void* stream);
+int sparse_mqa_bwd_dkv_reduce(void* dkv, int dkv_fp32, void* workspace, size_t workspace_bytes,
+                              int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk,
+                              void* stream);
+
 /* Stage, workspace-free variant of the main backward: writes dq and adds every valid slot's dKV
  * contribution into dkv_accum [B,S_kv,D] fp32 with fp32 atomic adds. dkv_accum must be zeroed by
  * the caller first; rows no slot references are untouched. Slower than the staged path on MI355X

@@ -135,3 +135,27 @@ def test_stage_validation(lib):
     assert lib.sparse_mqa_bwd_postprocess(None, A, 1, 16, 512, None) == NULL
     assert lib.sparse_mqa_bwd_postprocess(A, Bp, 1, 16, 12, None) == SHAPE
     assert lib.sparse_mqa_bwd_postprocess(A, A + 16, 1, 16, 512, None) == ALIAS
+
+
+def test_dkv_step_validation(lib):
+    """The separately enqueued dKV steps need a one-pass workspace and valid arguments."""
+    B, S, S_kv, H, D, K = 1, 8, 16, 64, 512, 4
+    full = lib.sparse_mqa_bwd_workspace_bytes(B, S, S_kv, H, D, K)
+    dims = (B, S, S_kv, H, D, K)
+    assert lib.sparse_mqa_bwd_dkv_prepare(None, G, full, *dims, None) == NULL
+    assert lib.sparse_mqa_bwd_dkv_prepare(Dp, None, full, *dims, None) == WORKSPACE
+    assert lib.sparse_mqa_bwd_dkv_prepare(Dp, G + 8, full, *dims, None) == ALIGN
+    # a workspace that only allows token chunks is refused (the steps are one pass)
+    low = lib.sparse_mqa_bwd_workspace_min_bytes(*dims)
+    assert lib.sparse_mqa_bwd_dkv_prepare(Dp, G, low, *dims, None) == WORKSPACE
+    assert lib.sparse_mqa_bwd_dkv_prepare(Dp, Dp, full, *dims, None) == ALIAS
+    assert lib.sparse_mqa_bwd_dkv_prepare(Dp, G, full, 1, 8, 16, 48, 512, 4, None) == UNSUP
+    assert lib.sparse_mqa_bwd_dkv_partials(A, Bp, C, Dp, E, None, G, full, *dims, NAN, None) == NULL
+    assert lib.sparse_mqa_bwd_dkv_partials(A, Bp, C, Dp, E, F_ + 2, G, full, *dims, NAN, None) == ALIGN
+    assert lib.sparse_mqa_bwd_dkv_partials(A, Bp, C, Dp, E, F_, G, low, *dims, NAN, None) == WORKSPACE
+    assert lib.sparse_mqa_bwd_dkv_partials(A, Bp, C, Dp, E, F_, A, full, *dims, NAN, None) == ALIAS
+    assert lib.sparse_mqa_bwd_dkv_partials(A, Bp, C, Dp, E, F_, G, full, *dims, -math.inf, None) == ARG
+    assert lib.sparse_mqa_bwd_dkv_reduce(None, 0, G, full, *dims, None) == NULL
+    assert lib.sparse_mqa_bwd_dkv_reduce(A + 8, 0, G, full, *dims, None) == ALIGN
+    assert lib.sparse_mqa_bwd_dkv_reduce(A, 0, G, 100, *dims, None) == WORKSPACE
+    assert lib.sparse_mqa_bwd_dkv_reduce(G + 256, 1, G, full, *dims, None) == ALIAS

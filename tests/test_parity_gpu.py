@@ -182,6 +182,15 @@ def test_dkv_paths_agree(gpu_lib):
     torch.cuda.synchronize()
     check_bf16("dKV one pass", one.view(-1, w.D), dkv_ref)
     check_bf16("dKV atomic", acc.view(-1, w.D), dkv_ref)
+    # the three separately enqueued steps run the same kernels; a row's staging order comes from
+    # int atomics, so the summation order (and the last bits) may differ from the one-call stage
+    steps = smqa.DkvSteps(*args)
+    steps.prepare()
+    steps.partials()
+    split = steps.reduce()
+    torch.cuda.synchronize()
+    check_bf16("dKV steps", split.view(-1, w.D), dkv_ref)
+    check_bf16("dKV steps vs one call", split.view(-1, w.D), one.float().view(-1, w.D))
 
 
 def test_non_default_stream(gpu_lib):

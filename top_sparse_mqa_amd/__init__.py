@@ -6,6 +6,7 @@ libsparse_mqa.so (include/sparse_mqa.h); this package is the Python binding.
 from .binding import (  # noqa: F401
     EXPORTED,
     LIB_PATH,
+    DkvSteps,
     SparseMQAError,
     bwd_dkv,
     bwd_dq,

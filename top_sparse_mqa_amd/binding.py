@@ -32,6 +32,9 @@ _SIGS = {
     "sparse_mqa_bwd_dq": [_c_void_p] * 7 + [_i64] * 6 + [ctypes.c_float, _c_void_p],
     "sparse_mqa_bwd_dkv": [_c_void_p] * 7 + [ctypes.c_int, _c_void_p, ctypes.c_size_t] + [_i64] * 6
     + [ctypes.c_float, _c_void_p],
+    "sparse_mqa_bwd_dkv_prepare": [_c_void_p] * 2 + [ctypes.c_size_t] + [_i64] * 6 + [_c_void_p],
+    "sparse_mqa_bwd_dkv_partials": [_c_void_p] * 7 + [ctypes.c_size_t] + [_i64] * 6 + [ctypes.c_float, _c_void_p],
+    "sparse_mqa_bwd_dkv_reduce": [_c_void_p, ctypes.c_int, _c_void_p, ctypes.c_size_t] + [_i64] * 6 + [_c_void_p],
     "sparse_mqa_bwd_postprocess": [_c_void_p] * 2 + [_i64] * 3 + [_c_void_p],
     "sparse_mqa_status_string": [ctypes.c_int],
 }
@@ -265,6 +268,46 @@ def bwd_dkv(q: torch.Tensor, kv: torch.Tensor, do: torch.Tensor, topk_idxs: torc
         _ptr(q), _ptr(kv), _ptr(do), _ptr(idx), _ptr(lse), _ptr(delta), _ptr(dkv), 1 if dkv_fp32 else 0,
         _ptr(workspace), workspace.numel(), B, S, S_kv, H, D, topk, _scale_arg(sm_scale), _stream()))
     return dkv
+
+
+class DkvSteps:
+    """The three steps of a single-pass dKV stage (prepare, partials, reduce) over one workspace,
+    for callers that time or schedule them separately; together they equal bwd_dkv."""
+
+    def __init__(self, q: torch.Tensor, kv: torch.Tensor, do: torch.Tensor, topk_idxs: torch.Tensor,
+                 lse: torch.Tensor, delta: torch.Tensor, sm_scale: Optional[float] = None, dkv_fp32: bool = False):
+        self.idx = _main_stage_args(q, kv, do, topk_idxs, lse, delta)
+        self.q, self.kv, self.do, self.lse, self.delta = q, kv, do, lse, delta
+        self.B, self.S, self.H, self.D = q.shape
+        self.S_kv, self.topk = kv.shape[1], self.idx.shape[2]
+        lib = load_library()
+        full = lib.sparse_mqa_bwd_workspace_bytes(self.B, self.S, self.S_kv, self.H, self.D, self.topk)
+        if full == 0:
+            raise ValueError("invalid sizes for the backward workspace")
+        # sparse_mqa_bwd_workspace_bytes includes Delta's part, which these steps do not use
+        self.workspace = torch.empty(full, dtype=torch.uint8, device=q.device)
+        self.scale = _scale_arg(sm_scale)
+        self.dkv_fp32 = dkv_fp32
+        self.dkv = torch.empty((self.B, self.S_kv, self.D), dtype=torch.float32 if dkv_fp32 else torch.bfloat16,
+                               device=q.device)
+
+    def _dims(self):
+        return (self.B, self.S, self.S_kv, self.H, self.D, self.topk)
+
+    def prepare(self) -> None:
+        _check("sparse_mqa_bwd_dkv_prepare", load_library().sparse_mqa_bwd_dkv_prepare(
+            _ptr(self.idx), _ptr(self.workspace), self.workspace.numel(), *self._dims(), _stream()))
+
+    def partials(self) -> None:
+        _check("sparse_mqa_bwd_dkv_partials", load_library().sparse_mqa_bwd_dkv_partials(
+            _ptr(self.q), _ptr(self.kv), _ptr(self.do), _ptr(self.idx), _ptr(self.lse), _ptr(self.delta),
+            _ptr(self.workspace), self.workspace.numel(), *self._dims(), self.scale, _stream()))
+
+    def reduce(self) -> torch.Tensor:
+        _check("sparse_mqa_bwd_dkv_reduce", load_library().sparse_mqa_bwd_dkv_reduce(
+            _ptr(self.dkv), 1 if self.dkv_fp32 else 0, _ptr(self.workspace), self.workspace.numel(), *self._dims(),
+            _stream()))
+        return self.dkv
 
 
 def bwd_postprocess(dkv_accum: torch.Tensor) -> torch.Tensor:

@@ -289,6 +289,79 @@ int sparse_mqa_bwd_dkv(const void* q, const void* kv, const void* d_o, const int
                  (hipStream_t)stream);
 }
 
+// The three steps of a single-pass staged dKV, for callers that schedule or time them separately.
+// They need a workspace that holds every token (sparse_mqa_bwd_workspace_bytes minus Delta's part)
+// and must run in order on one stream with the same workspace and sizes.
+static int single_pass_plan(void* workspace, size_t workspace_bytes, int64_t B, int64_t S, int64_t S_kv, int64_t H,
+                            int64_t D, int64_t topk, int dkv_fp32, DkvPlan* p) {
+  if (!workspace) return SMQA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return SMQA_ERR_ALIGN;
+  if (!plan_dkv(B, S, S_kv, H, D, topk, dkv_fp32 != 0, 0, workspace_bytes, p) || p->chunk != B * S)
+    return SMQA_ERR_WORKSPACE;
+  return SMQA_OK;
+}
+
+int sparse_mqa_bwd_dkv_prepare(const int32_t* topk_idxs, void* workspace, size_t workspace_bytes, int64_t B,
+                               int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, void* stream) {
+  int st = check_shapes(B, S, S_kv, H, D, topk);
+  if (st) return st;
+  if (!topk_idxs) return SMQA_ERR_NULL;
+  if (!aligned4(topk_idxs)) return SMQA_ERR_ALIGN;
+  DkvPlan p;
+  if ((st = single_pass_plan(workspace, workspace_bytes, B, S, S_kv, H, D, topk, 0, &p))) return st;
+  if (overlap(Span{workspace, (int64_t)p.end}, Span{topk_idxs, count({B, S, topk}) * 4})) return SMQA_ERR_ALIAS;
+  char* ws = (char*)workspace;
+  if (smqa::launch_dkv_prepare(topk_idxs, (int32_t*)(ws + p.count), (int32_t*)(ws + p.offset),
+                               (int32_t*)(ws + p.tiles), (int32_t*)(ws + p.pos), B, S, S_kv, topk,
+                               smqa::bwd_hblocks(H), 0, B * S, (hipStream_t)stream) != hipSuccess)
+    return SMQA_ERR_HIP;
+  return SMQA_OK;
+}
+
+int sparse_mqa_bwd_dkv_partials(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs,
+                                const float* lse, const float* delta, void* workspace, size_t workspace_bytes,
+                                int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk,
+                                float sm_scale, void* stream) {
+  float scale;
+  int st = check_bwd_inputs(q, kv, d_o, topk_idxs, lse, B, S, S_kv, H, D, topk, sm_scale, &scale);
+  if (st) return st;
+  if (!delta) return SMQA_ERR_NULL;
+  if (!aligned4(delta)) return SMQA_ERR_ALIGN;
+  DkvPlan p;
+  if ((st = single_pass_plan(workspace, workspace_bytes, B, S, S_kv, H, D, topk, 0, &p))) return st;
+  const int64_t qb = count({B, S, H, D}) * 2;
+  const Span sws{workspace, (int64_t)p.end};
+  const Span ins[] = {{q, qb}, {kv, count({B, S_kv, D}) * 2}, {d_o, qb}, {topk_idxs, count({B, S, topk}) * 4},
+                      {lse, count({B, S, H}) * 4}, {delta, count({B, S, H}) * 4}};
+  for (const Span& s : ins)
+    if (overlap(sws, s)) return SMQA_ERR_ALIAS;
+  char* ws = (char*)workspace;
+  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, nullptr, nullptr, (const int32_t*)(ws + p.pos),
+                      (uint16_t*)(ws + p.stage), (int8_t*)(ws + p.stage_exp), B, S, S_kv, H, D, topk, scale, 0,
+                      B * S};
+  if (smqa::launch_bwd_main(a, 2, (hipStream_t)stream) != hipSuccess) return SMQA_ERR_HIP;
+  return SMQA_OK;
+}
+
+int sparse_mqa_bwd_dkv_reduce(void* dkv, int dkv_fp32, void* workspace, size_t workspace_bytes, int64_t B,
+                              int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, void* stream) {
+  int st = check_shapes(B, S, S_kv, H, D, topk);
+  if (st) return st;
+  if (!dkv) return SMQA_ERR_NULL;
+  if (!aligned16(dkv)) return SMQA_ERR_ALIGN;
+  DkvPlan p;
+  if ((st = single_pass_plan(workspace, workspace_bytes, B, S, S_kv, H, D, topk, dkv_fp32, &p))) return st;
+  if (overlap(Span{workspace, (int64_t)p.end}, Span{dkv, count({B, S_kv, D}) * (dkv_fp32 ? 4 : 2)}))
+    return SMQA_ERR_ALIAS;
+  char* ws = (char*)workspace;
+  if (smqa::launch_reduce_rows((const uint16_t*)(ws + p.stage), (const int8_t*)(ws + p.stage_exp),
+                               smqa::stage_segments(H, D), (const int32_t*)(ws + p.offset),
+                               dkv_fp32 ? (float*)dkv : nullptr, dkv_fp32 ? nullptr : dkv, 0, B * S_kv, D,
+                               (hipStream_t)stream) != hipSuccess)
+    return SMQA_ERR_HIP;
+  return SMQA_OK;
+}
+
 int sparse_mqa_bwd_main(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs,
                         const float* lse, const float* delta, void* dq, float* dkv_accum, int64_t B, int64_t S,
                         int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale, void* stream) {
