@@ -3,13 +3,14 @@
 //   preprocess   Delta[b,s,h] = <O, dO> in fp32                       (HBM stream)
 //   fill_zero    clears the fp32 dKV accumulator (a kernel, so the sequence is graph-safe)
 //   bwd_dq       per token: S^T, dP^T, P, dS, dQ^T += K^T dS^T      (bf16 MFMA 16x16x32)
-//   bwd_dkv      per token: S^T, dP^T, P, dS, then dKV rows of the block
-//                = (sm_scale dS)^T Q + P^T dO over all heads          (bf16 MFMA 32x32x16)
+//   bwd_dkv      per token: S^T, dP^T, P, dS, then dKV^T for the block's slots
+//                = Q^T (sm_scale dS) + dO^T P over all heads            (MFMA 32x32x16)
 //                and either a plain store of each valid row into its staging row (segmented
-//                scatter-add, below) or a fp32 atomic add into the accumulator. P and
-//                sm_scale*dS enter this product as hi + lo bf16 pairs (two MFMAs each): a
-//                kv row sums thousands of heavily cancelling terms, and single-bf16
-//                coefficients leave errors of several percent of the result there.
+//                scatter-add, below) or a fp32 atomic add into the accumulator. A kv row sums
+//                thousands of heavily cancelling terms, and 8-bit-mantissa coefficients leave
+//                errors of several percent of the result there: sm_scale*dS enters as a hi + lo
+//                bf16 pair (two MFMAs) and P as fp16, against dO converted to fp16 under a
+//                per-token power-of-two scale (one f16 MFMA).
 //   postprocess  fp32 accumulator -> bf16 (round to nearest even)
 // dQ and dKV run as two kernels: the per-token state both need (Q and dO in two layouts plus
 // the dQ accumulator) does not fit one workgroup's registers at H = 64, D = 512.
@@ -21,34 +22,32 @@ namespace smqa {
 
 __device__ __attribute__((aligned(16))) uint4 g_zero_row_bwd[64];
 
-// Tile swizzle for the backward: 16 consecutive rows at one chunk and 8 consecutive rows at two
-// adjacent chunks (the footprint of a transposing read over 32 lanes) both avoid bank conflicts.
+// Tile swizzle for the backward (16-byte chunk c of row r sits at c ^ bwd_swz(r)): a GF(2)-linear
+// map of the row's low four bits under which both tile reads are free of LDS bank conflicts on
+// gfx950 -- the score read (rows lane & 15 at one chunk per 16-lane group, 16-byte reads) and the
+// dQ transposing read (rows 4 (lane >> 4) + ((lane & 15) >> 2) at two adjacent chunks). Chosen by
+// measuring the bank-conflict counter over candidate maps; simpler maps such as
+// ((r & 7) << 1) | (r >> 3) leave the score read 2-way conflicted.
 __device__ __forceinline__ int bwd_swz(int row) {
   const int r = row & 15;
-  return ((r & 7) << 1) | (r >> 3);
-}
-template <int D>
-__device__ __forceinline__ int bwd_off(int row, int chunk) {
-  return row * (D * 2) + ((chunk ^ (bwd_swz(row) & (D / 8 - 1))) << 4);
+  return ((r & 1) << 2) ^ (r & 10) ^ (((r >> 2) & 1) * 9);
 }
 
 // Staging rows hold D fp16 values plus one int8 exponent per segment of SEG values: value =
-// fp16 * 2^e. A wave stores segment-wide pieces of 32 rows at once (its d-range of one block) and
-// picks one exponent for all of them: 0 while the largest magnitude m lies in [2^-10, 2^14) --
-// there fp16 keeps 11 significant bits down to m / 16 and smaller values err by at most 2^-25 --
-// else the one that brings m to [2^13, 2^14). This halves the traffic of the staged scatter-add
-// against fp32 rows.
+// fp16 * 2^e. Each row segment picks its own exponent: 0 while its largest magnitude m lies in
+// [2^-10, 2^14) -- there fp16 keeps 11 significant bits down to m / 16 and smaller values err by
+// at most 2^-25 -- else the one that brings m to [2^13, 2^14). This halves the traffic of the
+// staged scatter-add against fp32 rows.
 __device__ __forceinline__ int stage_exponent(float m) {
   if (!(m > 0.f && m <= 3.4028235e38f)) return 0;  // zero, inf or NaN: stored as is
   if (m >= 0.0009765625f && m < 16384.f) return 0;
   int e = __builtin_amdgcn_frexp_expf(m) - 14;      // m < 2^(e + 14)
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
-// Maximum over the wave.
-__device__ __forceinline__ float wave_max(float m) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-  return m;
+// Maximum of lanes l and l ^ 32 (one cross-half lane swap).
+__device__ __forceinline__ float half_swap_max(float m) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(m, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -108,38 +107,47 @@ struct BwdCommon {
 
 // Tile rows are gathered with direct-to-LDS loads. With 1 KiB rows (D = 512) one instruction
 // moves one row: its kv row index is read from the index lane into a scalar register and the lane
-// offset carries the row's chunk swizzle; smaller rows take several rows per instruction.
+// offset carries the row's chunk swizzle; smaller rows take several rows per instruction. A wave
+// issues its share of a tile as NP instructions.
 template <int D, int NW>
-__device__ __forceinline__ void bwd_issue_tile(const char* kv_b, int64_t S_kv, int32_t my_idx, uint64_t mask,
-                                               char* tile, int lane, int wu) {
+struct BwdGather {
   using C = BwdCommon<D, NW>;
-  if constexpr (C::RPI == 1) {
-    // kv rows through a buffer resource (row offset in the scalar offset), masked rows from the
-    // zero row through a second one
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv_b, (int)(S_kv * C::ROWB));
-    const __amdgpu_buffer_rsrc_t rz = make_rsrc(g_zero_row_bwd, C::ROWB);
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-#pragma unroll
-    for (int i = 0; i < C::T / NW; i++) {
-      const int r = wu + NW * i;
+  static constexpr int NP = C::RPI == 1 ? C::T / NW : (C::NINSTR + NW - 1) / NW;
+  const char* kv_b;
+  __amdgpu_buffer_rsrc_t rk, rz;  // kv rows of this batch; the zero row (masked slots)
+
+  __device__ __forceinline__ BwdGather(const char* kv_b_, int64_t S_kv)
+      : kv_b(kv_b_), rk(make_rsrc(kv_b_, (int)(S_kv * C::ROWB))), rz(make_rsrc(g_zero_row_bwd, C::ROWB)) {}
+
+  // part k of this wave's share of the tile whose slots' indices sit in my_idx (lane t = slot t)
+  __device__ __forceinline__ void part(int k, int32_t my_idx, uint64_t mask, char* tile, int lane, int wu) const {
+    if constexpr (C::RPI == 1) {
+      const int r = wu + NW * k;
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
       const int32_t ri = __builtin_amdgcn_readlane(my_idx, r);
       const uint32_t voff = (uint32_t)((ln ^ (bwd_swz(r) & (C::CPR - 1))) << 4);
-      if ((mask >> r) & 1ull) dma16_buf(rk, voff, (uint32_t)ri * C::ROWB, tile + r * C::ROWB);
-      else dma16_buf(rz, voff, 0, tile + r * C::ROWB);
-    }
-  } else {
-    for (int ins = wu; ins < C::NINSTR; ins += NW) {
-      const int r = ins * C::RPI + lane / C::CPR;
-      const int p = lane % C::CPR;
-      const int c = p ^ (bwd_swz(r) & (C::CPR - 1));
-      const int32_t ri = __shfl(my_idx, r);
+      // branch-free: the row's resource and offset are selected (scalar selects)
       const bool v = (mask >> r) & 1ull;
-      const char* src = v ? kv_b + (int64_t)ri * C::ROWB + c * 16 : (const char*)g_zero_row_bwd + c * 16;
-      dma16(src, tile + ins * 1024);
+      dma16_buf(v ? rk : rz, voff, v ? (uint32_t)ri * C::ROWB : 0u, tile + r * C::ROWB);
+    } else {
+      const int ins = wu + NW * k;
+      if (NP * NW == C::NINSTR || ins < C::NINSTR) {
+        const int r = ins * C::RPI + lane / C::CPR;
+        const int p = lane % C::CPR;
+        const int c = p ^ (bwd_swz(r) & (C::CPR - 1));
+        const int32_t ri = __shfl(my_idx, r);
+        const bool v = (mask >> r) & 1ull;
+        const char* src = v ? kv_b + (int64_t)ri * C::ROWB + c * 16 : (const char*)g_zero_row_bwd + c * 16;
+        dma16(src, tile + ins * 1024);
+      }
     }
   }
-}
+  __device__ __forceinline__ void all(int32_t my_idx, uint64_t mask, char* tile, int lane, int wu) const {
+#pragma unroll
+    for (int k = 0; k < NP; k++) part(k, my_idx, mask, tile, lane, wu);
+  }
+};
 
 // Per-lane byte offsets of the score A fragments inside a tile: fragment (ks, mt) = rows
 // 16 mt + (lane & 15), chunk 4 ks + (lane >> 4). The swizzle only touches the low four chunk
@@ -175,15 +183,15 @@ __device__ __forceinline__ void bwd_scores(const char* tile, const int* sc_off, 
   bf16x8 fr[NB];
 #pragma unroll
   for (int i = 0; i < PFE; i++) fr[i] = frag(i);
-#pragma unroll
-  for (int i = 0; i < NF; i++) {
+  static_for<NF>([&](auto it) {
+    constexpr int i = decltype(it)::value;
     __builtin_amdgcn_sched_barrier(0);
-    if (i + PFE < NF) fr[(i + PFE) % NB] = frag(i + PFE);
-    const int ks = i >> 1, mt = i & 1;
+    if constexpr (i + PFE < NF) fr[(i + PFE) % NB] = frag(i + PFE);
+    constexpr int ks = i >> 1, mt = i & 1;
     sacc[mt] = mfma16(fr[i % NB], qb[ks], sacc[mt]);
     dpacc[mt] = mfma16(fr[i % NB], dob[ks], dpacc[mt]);
-    stage_hook(i);
-  }
+    stage_hook(it);
+  });
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -250,7 +258,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
 
   const int nblk = (topk + T - 1) / T;
   const int32_t* idx_tok = idx + token * (int64_t)topk;
-  const char* kv_b = (const char*)(kv + b * S_kv * D);
+  using G = BwdGather<D, NW>;
+  const G gather((const char*)(kv + b * S_kv * D), S_kv);
   auto load_idx = [&](int blk) -> int32_t {
     const int t = blk * T + lane;
     return (lane < T && t < topk) ? idx_tok[t] : -1;
@@ -258,7 +267,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
 
   int32_t idx_cur = load_idx(0);
   uint64_t mask_cur = __ballot(slot_in_range(idx_cur, S_kv));
-  if (mask_cur) bwd_issue_tile<D, NW>(kv_b, S_kv, idx_cur, mask_cur, tile0, lane, wu);
+  if (mask_cur) gather.all(idx_cur, mask_cur, tile0, lane, wu);
   int32_t idx_nxt = nblk > 1 ? load_idx(1) : -1;
 
   auto block = [&](auto buf_tag, int blk) {
@@ -267,10 +276,12 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
     char* other = BUF ? tile0 : tile1;
     wait_all_mem();
     __syncthreads();
+    // the next tile's gather goes out at once: spread over the score loop (one part every few
+    // stages) it measured slower in this kernel
     uint64_t mask_nxt = 0;
     if (blk + 1 < nblk) {
       mask_nxt = __ballot(slot_in_range(idx_nxt, S_kv));
-      if (mask_nxt) bwd_issue_tile<D, NW>(kv_b, S_kv, idx_nxt, mask_nxt, other, lane, wu);
+      if (mask_nxt) gather.all(idx_nxt, mask_nxt, other, lane, wu);
     }
     idx_cur = idx_nxt;
     idx_nxt = blk + 2 < nblk ? load_idx(blk + 2) : -1;
@@ -324,7 +335,9 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
 }
 
 // ---------------------------------------------------------------------------------------------
-template <int D, int NW>
+// STAGED: every valid slot's dKV row goes to its staging row (pos, stage, stage_exp); otherwise it
+// is added into the fp32 accumulator dkv_acc with fp32 atomics (the workspace-free variant).
+template <int D, int NW, bool STAGED>
 __global__ void __launch_bounds__(NW * 64)
 bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ dout,
                const int32_t* __restrict__ idx, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -332,6 +345,7 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
                int8_t* __restrict__ stage_exp, int S, int64_t S_kv, int H, int topk, float sm_scale,
                float scale_log2, int n_hblk, int token0, int n_tokens) {
   using C = BwdCommon<D, NW>;
+  using G = BwdGather<D, NW>;
   constexpr int T = C::T;
   constexpr int PF = 6;
   constexpr int HB = 16 * NW;   // heads of this workgroup
@@ -339,30 +353,34 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
   constexpr int NDT = DW / 32;  // 32-wide d tiles of one wave
   constexpr int DG = NDT < 4 ? NDT : 4;  // d tiles accumulated together
   constexpr int KH = HB / 16;   // 16-head k-steps of the dKV product
+  constexpr int NFS = 2 * C::KS;  // score stages
   static_assert(NDT >= 1 && NDT % DG == 0, "each wave needs whole groups of 32-wide d tiles");
   constexpr int SB = HB * T * 2;  // bytes of one [HB][T] bf16 buffer
   __shared__ __attribute__((aligned(16))) char tile0[C::TB];
   __shared__ __attribute__((aligned(16))) char tile1[C::TB];
-  // P / sm_scale*dS as hi and lo bf16 parts (lo = x - float(bf16(x)), rounded): buffers
-  // 0 = dS hi, 1 = dS lo, 2 = P hi, 3 = P lo, each [head][slot].
-  __shared__ __attribute__((aligned(16))) char pds[4 * SB];
-  // Staging-store transpose: each wave writes its [32 slots][DG*32 d] fp32 tile here and reads it
-  // back as whole row segments, so each 16-byte store covers DG*128 contiguous bytes of a row.
-  // The row pitch is padded by 32 bytes: the two half-waves of a column write (slots 4 apart) then
-  // fall on disjoint banks.
-  // The transpose holds fp16 (the staging format); the row pitch is padded by 16 bytes so the two
-  // half-waves of a column write (slots 4 apart) fall on disjoint banks.
+  // B operands of the dKV product, each [head][slot]: 0 = hi and 1 = lo bf16 parts of
+  // sm_scale * dS * 2^-so (lo = x - float(bf16(x)), rounded), 2 = P as fp16.
+  __shared__ __attribute__((aligned(16))) char pds[3 * SB];
+  __shared__ float red[NW];
+  // Staging-store transpose. The dKV^T accumulator gives each lane one slot row and runs of four
+  // consecutive d; they go to this wave's [32 slots][SEGW d] fp16 buffer as 8-byte writes and come
+  // back as 16-byte pieces of whole row segments, so one store instruction covers LPR * 16
+  // contiguous bytes of each of RPS rows. Rows are unpadded and their 16-byte chunks XOR-swizzled
+  // by the row's low bits (obuf_chunk): the read-back is conflict-free and the writes (32 rows at
+  // one column) 2-way. (A padded pitch that makes the writes conflict-free too leaves the rows
+  // 8-byte aligned, and the compiler then makes every read-back wait for the gathers in flight.)
   constexpr int SEGW = DG * 32;         // d values per wave group = one staging exponent segment
   constexpr int NSEG = D / SEGW;        // exponents per staging row
-  constexpr int OP = SEGW * 2 + 16;
+  constexpr int OP = SEGW * 2;
   __shared__ __attribute__((aligned(16))) char obuf[NW][T * OP];
   // read-back geometry of the transpose: RPS slot rows of LPR lanes (16 bytes each) per instruction
   constexpr int LPR = SEGW / 8, RPS = 64 / LPR, NI = T / RPS;
+  auto obuf_chunk = [](int row, int chunk) { return ((chunk ^ (row & (LPR - 1))) << 4); };
   // With one d group per wave the stores of a block are deferred: the block leaves its rows in
   // obuf (and their staging row indices in obdst) and the next block issues them from inside its
   // score loop, one every other stage. A wave issues in order, so stores issued in one burst
   // would stall its MFMAs behind the memory pipeline.
-  constexpr bool DEFER = (NDT == DG);
+  constexpr bool DEFER = STAGED && (NDT == DG);
   __shared__ int32_t obdst[NW][T];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -374,27 +392,31 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
   const int hblk = item % n_hblk;
   const int64_t b = token / S;
   const int hrow = 16 * w + (lane & 15);          // head within the workgroup's block
-  // staging mode: every valid slot owns n_hblk consecutive staging rows from pos[]
-  const int32_t* pos_tok = stage ? pos + ctok * (int64_t)topk : nullptr;
+  // staged: every valid slot owns n_hblk consecutive staging rows from pos[]
+  const int32_t* pos_tok = STAGED ? pos + ctok * (int64_t)topk : nullptr;
   const int head = hblk * HB + hrow;
 
-  // (1) Q and dO with heads along k, as B operands of dKV = (sm_scale dS)^T Q + P^T dO:
+  // (1) Q and dO with heads along k, as A operands of dKV^T = Q^T (sm_scale dS) + dO^T P:
   // lane l holds d = w*DW + 32 dt + (l & 31) and heads 16 ks + 8 kg .. +7, read with transposing
   // LDS loads from a row-major [HB][D] staging copy held in the two tile buffers (heads
   // 0 .. HH-1 in tile0, the rest in tile1; the buffers are free at this point).
+  // P enters the product as fp16 (11 significant bits; bf16 P leaves errors of several percent on
+  // heavily shared rows), so dO does too, scaled by 2^-so with so chosen from this workgroup's
+  // max |dO|: every bf16 value within 2^28 of the max converts exactly, and the partner operand
+  // sm_scale * dS carries the same 2^-so. The staged rows carry 2^so in their exponents.
   constexpr int HH = C::TB / (D * 2);  // heads per tile buffer
   static_assert(HB <= 2 * HH && HH % 16 == 0, "staging copy must fit the tile buffers");
-  bf16x8 qv[NDT][KH], dov[NDT][KH];
+  constexpr int NPT = HB * D / 8 / (NW * 64);  // 16-byte pieces per thread
+  bf16x8 qv[NDT][KH];
+  f16x8 dov[NDT][KH];
+  int so = 0;
   {
     const int64_t base = (token * H + (int64_t)hblk * HB) * D;
-    for (int pass = 0; pass < 2; pass++) {
-      const uint16_t* src = (pass == 0 ? q : dout) + base;
-      for (int i = threadIdx.x; i < HB * D / 8; i += NW * 64) {
-        const int h = i / (D / 8);
-        char* dst = (h < HH ? tile0 + 16 * i : tile1 + 16 * (i - HH * (D / 8)));
-        *(uint4*)dst = *(const uint4*)(src + 8 * i);
-      }
-      __syncthreads();
+    auto piece = [&](int i) -> char* {  // staging-copy address of 16-byte piece i
+      const int h = i / (D / 8);
+      return h < HH ? tile0 + 16 * i : tile1 + 16 * (i - HH * (D / 8));
+    };
+    auto read_frags = [&](auto&& put) {
 #pragma unroll
       for (int dt = 0; dt < NDT; dt++)
 #pragma unroll
@@ -403,13 +425,45 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
           const char* sb = hb0 < HH ? tile0 : tile1;
           const int h0 = hb0 % HH + 8 * kg + ((lane & 15) >> 2);
           const int d = w * DW + 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-          const s16x4 lo = lds_load_tr(sb + (h0 * D + d) * 2);
-          const s16x4 hi = lds_load_tr(sb + ((h0 + 4) * D + d) * 2);
-          if (pass == 0) qv[dt][ks] = join_tr(lo, hi);
-          else dov[dt][ks] = join_tr(lo, hi);
+          put(dt, ks, join_tr(lds_load_tr(sb + (h0 * D + d) * 2), lds_load_tr(sb + ((h0 + 4) * D + d) * 2)));
         }
-      __syncthreads();
+    };
+#pragma unroll
+    for (int k = 0; k < NPT; k++) {
+      const int i = threadIdx.x + k * NW * 64;
+      *(uint4*)piece(i) = *(const uint4*)(q + base + 8 * i);
     }
+    __syncthreads();
+    read_frags([&](int dt, int ks, bf16x8 v) { qv[dt][ks] = v; });
+    __syncthreads();
+    uint4 raw[NPT];
+    float mx = 0.f;
+#pragma unroll
+    for (int k = 0; k < NPT; k++) {
+      raw[k] = *(const uint4*)(dout + base + 8 * (threadIdx.x + k * NW * 64));
+      const bf16x8 v = __builtin_bit_cast(bf16x8, raw[k]);
+#pragma unroll
+      for (int e = 0; e < 8; e++) mx = fmaxf(mx, fabsf((float)v[e]));
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if (lane == 0) red[w] = mx;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NW; k++) mx = fmaxf(mx, red[k]);
+    // mx < 2^(e) with e = frexp exponent: scaled values stay below 2^15
+    if (mx > 0.f && mx <= 3.4028235e38f) so = __builtin_amdgcn_frexp_expf(mx) - 15;
+#pragma unroll
+    for (int k = 0; k < NPT; k++) {
+      const bf16x8 v = __builtin_bit_cast(bf16x8, raw[k]);
+      f16x8 hv;
+#pragma unroll
+      for (int e = 0; e < 8; e++) hv[e] = (_Float16)__builtin_amdgcn_ldexpf((float)v[e], -so);
+      *(f16x8*)piece(threadIdx.x + k * NW * 64) = hv;
+    }
+    __syncthreads();
+    read_frags([&](int dt, int ks, bf16x8 v) { dov[dt][ks] = __builtin_bit_cast(f16x8, v); });
+    __syncthreads();
 #pragma unroll
     for (int dt = 0; dt < NDT; dt++)
 #pragma unroll
@@ -439,81 +493,62 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
 
   int sc_off[C::KSJ];
   bwd_score_offsets<D>(lane, sc_off);
-  // P/dS writes: head hrow, slots 16 mt + 4 g .. +3 (8 bytes). Reads (A operand of dKV): lane l
+  // P/dS writes: head hrow, slots 16 mt + 4 g .. +3 (8 bytes). Reads (B operand of dKV^T): lane l
   // gets slot (l & 31) and heads 16 ks + 8 kg .. +7 from two transposing reads 4 heads apart.
   const int pw_off = (hrow * T + 4 * g) * 2;
   const int pr_off = ((8 * kg + ((lane & 15) >> 2)) * T + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
   const int nblk = (topk + T - 1) / T;
   const int32_t* idx_tok = idx + token * (int64_t)topk;
-  const char* kv_b = (const char*)(kv + b * S_kv * D);
-  float* acc_b = stage ? nullptr : dkv_acc + b * S_kv * D;
+  const G gather((const char*)(kv + b * S_kv * D), S_kv);
   auto load_idx = [&](int blk) -> int32_t {
     const int t = blk * T + lane;
     return (lane < T && t < topk) ? idx_tok[t] : -1;
   };
   auto load_pos = [&](int blk) -> int32_t {
     const int t = blk * T + lane;
-    return (stage && lane < T && t < topk) ? pos_tok[t] : -1;
+    return (STAGED && lane < T && t < topk) ? pos_tok[t] : -1;
   };
 
   int32_t pos_cur = load_pos(0);
   int32_t pos_nxt = nblk > 1 ? load_pos(1) : -1;
   int32_t idx_cur = load_idx(0);
   uint64_t mask_cur = __ballot(slot_in_range(idx_cur, S_kv));
-  if (mask_cur) bwd_issue_tile<D, NW>(kv_b, S_kv, idx_cur, mask_cur, tile0, lane, wu);
+  if (mask_cur) gather.all(idx_cur, mask_cur, tile0, lane, wu);
   int32_t idx_nxt = nblk > 1 ? load_idx(1) : -1;
   wait_all_mem();
 
-  // Deferred staging stores (stage mode, one d group): row k of the previous block's transpose
-  // buffer goes to staging row obdst[k * RPS + lane / LPR]. Row k is read in score stage 2k and
-  // stored in stage 2k + 1 (more rows in flight push this kernel past its registers); the segment
-  // exponents of the 32 rows go out in stage 1; the rest is flushed after the loop.
-  bool pending = false;
-  int pending_e = 0;
+  // 16-byte piece lane % LPR of transpose row (k * RPS + lane / LPR)
+  auto rdpiece = [&](int k) -> i32x4 {
+    const int row = k * RPS + lane / LPR;
+    return *(const i32x4*)(obuf[w] + row * OP + obuf_chunk(row, lane % LPR));
+  };
+  // Deferred staging stores (one d group per wave): the rows a block leaves in the transpose
+  // buffer, with their staging rows in obdst, go out during the next non-empty block's dKV
+  // product, SPK rows per k-step, each read from LDS one k-step ahead of its store. obdst starts at
+  // the spare row, so the first block's stores write the unused buffer there; a block without valid
+  // slots leaves the buffer alone and the next one stores the same rows again (same values).
+  const int32_t spare = (n_tokens * topk + (int32_t)ctok) * n_hblk + hblk;
+  constexpr int SPK = (NI + KH - 1) / KH;  // stores per k-step of the dKV product
+  int pending_e = 0;                       // exponent of slot row lane & 31
+  if constexpr (DEFER) {
+    if (lane < T) obdst[w][lane] = spare;
+  }
   const int dlane = w * DW + 8 * (lane % LPR);  // first d of this lane's 8 values
-  i32x4 dv[1];
-  int32_t dd[1];
-  int32_t ddx = 0;
+  i32x4 dv[SPK];
+  int32_t dd[SPK], ddx = 0;
   auto dread = [&](int k) {
-    dv[0] = *(const i32x4*)(obuf[w] + (k * RPS + lane / LPR) * OP + 16 * (lane % LPR));
-    dd[0] = obdst[w][k * RPS + lane / LPR];
+    if (k < NI) {
+      dv[k % SPK] = rdpiece(k);
+      dd[k % SPK] = obdst[w][k * RPS + lane / LPR];
+    }
   };
   auto dstore = [&](int k) {
-    __builtin_nontemporal_store(dv[0], (i32x4*)(stage + (int64_t)dd[0] * D + dlane));
+    if (k < NI) __builtin_nontemporal_store(dv[k % SPK], (i32x4*)(stage + (int64_t)dd[k % SPK] * D + dlane));
   };
   auto eread = [&]() { ddx = obdst[w][lane & 31]; };
   auto estore = [&]() {
     if (lane < T) stage_exp[(int64_t)ddx * NSEG + w * (DW / SEGW)] = (int8_t)pending_e;
-  };
-  constexpr int NFS = 2 * C::KS;  // score stages
-  auto store_hook = [&](int i) {
-    if constexpr (DEFER) {
-      if (!pending) return;
-      if (i == 0) eread();
-      if (i == 1) estore();
-      if ((i & 1) == 0 && i / 2 < NI) dread(i / 2);
-      if ((i & 1) == 1 && (i - 1) / 2 < NI) dstore((i - 1) / 2);
-    }
-  };
-  // issues whatever the hook did not
-  auto flush_pending = [&](bool after_scores) {
-    if constexpr (DEFER) {
-      if (!pending) return;
-      if (!(after_scores && NFS > 1)) {
-        eread();
-        estore();
-      }
-#pragma unroll
-      for (int k = 0; k < NI; k++) {
-        const bool read_done = after_scores && 2 * k < NFS;
-        const bool store_done = after_scores && 2 * k + 1 < NFS;
-        if (store_done) continue;
-        if (!read_done) dread(k);
-        dstore(k);
-      }
-      pending = false;
-    }
   };
 
   // Each wave waits for its own part of tile blk + 1 right before it stores the rows of tile blk,
@@ -525,11 +560,12 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
     // tile blk complete (each wave waited for its part before its previous stores); the P/dS
     // buffers of the previous block fully consumed. The stores themselves stay in flight.
     lds_barrier();
+    // the next tile is gathered in parts from inside this block's score loop, one every NFS / NP
+    // stages; the previous block's staging stores go out during this block's dKV product, so the
+    // two streams of vector memory instructions do not queue up behind each other
     uint64_t mask_nxt = 0;
-    if (blk + 1 < nblk) {
-      mask_nxt = __ballot(slot_in_range(idx_nxt, S_kv));
-      if (mask_nxt) bwd_issue_tile<D, NW>(kv_b, S_kv, idx_nxt, mask_nxt, other, lane, wu);
-    }
+    if (blk + 1 < nblk) mask_nxt = __ballot(slot_in_range(idx_nxt, S_kv));
+    const int32_t idx_g = idx_nxt;
     const int32_t idx_this = idx_cur;
     idx_cur = idx_nxt;
     idx_nxt = blk + 2 < nblk ? load_idx(blk + 2) : -1;
@@ -539,53 +575,53 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
     const uint64_t mask = mask_cur;
     mask_cur = mask_nxt;
     if (mask == 0) {
+      if (mask_nxt) gather.all(idx_g, mask_nxt, other, lane, wu);
       wait_all_mem();
       return;
     }
+    // unconditional and branch-free: with no next block (mask_nxt == 0) the parts read the zero row
+    // into the idle buffer, which nothing reads before the next wait
+    auto gather_hook = [&](int i) {
+#pragma unroll
+      for (int k = 0; k < G::NP; k++)
+        if (i == (k * NFS) / G::NP + NFS / G::NP / 2) gather.part(k, idx_g, mask_nxt, other, lane, wu);
+    };
 
     f32x4 sacc[2], dpacc[2];
-    bwd_scores<D, PF>(tile, sc_off, qb, dob, sacc, dpacc, store_hook);
-    flush_pending(true);
+    bwd_scores<D, PF>(tile, sc_off, qb, dob, sacc, dpacc, gather_hook);
     // validity of this lane's slots 4g + r (bit r) and 16 + 4g + r (bit 16 + r), one variable shift
     const uint32_t vb = (uint32_t)(mask >> (4 * g));
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) {
-      float p[4], ds[4], plr[4], dslr[4];
+      float p[4], ds[4], dslr[4];
 #pragma unroll
       for (int r = 0; r < 4; r++) {
         p[r] = ((vb >> (16 * mt + r)) & 1u) ? fast_exp2(sacc[mt][r] * scale_log2 - lse_h) : 0.f;
-        ds[r] = sm_scale * p[r] * (dpacc[mt][r] - delta_h);
-        plr[r] = p[r] - (float)(__bf16)p[r];
+        ds[r] = __builtin_amdgcn_ldexpf(sm_scale * p[r] * (dpacc[mt][r] - delta_h), -so);
         dslr[r] = ds[r] - (float)(__bf16)ds[r];
       }
       char* wp = pds + pw_off + 32 * mt;
       *(uint2*)(wp) = pack4_bf16(ds[0], ds[1], ds[2], ds[3]);
       *(uint2*)(wp + SB) = pack4_bf16(dslr[0], dslr[1], dslr[2], dslr[3]);
-      *(uint2*)(wp + 2 * SB) = pack4_bf16(p[0], p[1], p[2], p[3]);
-      *(uint2*)(wp + 3 * SB) = pack4_bf16(plr[0], plr[1], plr[2], plr[3]);
+      const f16x2 p01 = __builtin_convertvector((f32x2){p[0], p[1]}, f16x2);
+      const f16x2 p23 = __builtin_convertvector((f32x2){p[2], p[3]}, f16x2);
+      *(uint2*)(wp + 2 * SB) = make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
     }
     lds_barrier();  // P/dS visible to all waves; the next tile's gather stays in flight
 
-    // dKV[slot, d] for this wave's d-range, DG tiles of 32 d at a time:
-    //   dS_hi^T Q + dS_lo^T Q + P_hi^T dO + P_lo^T dO, k over the block's heads.
-    // C layout: lane holds d = w*DW + 32 dt + (lane & 31), slots 8 (r>>2) + 4 kg + (r & 3).
-    // staging mode: masked slots store into this workgroup's spare row (after all staging rows of
-    // the chunk), so the stores need no per-slot branches
-    const int32_t spare = (n_tokens * topk + (int32_t)ctok) * n_hblk + hblk;
-    const int32_t dst_this = stage ? (slot_in_range(idx_this, S_kv) ? pos_this + hblk : spare) : idx_this;
-    int32_t rowi[16];
-    if (stage && DEFER) {
-      // no per-lane rows needed: they go to obdst below
-    } else if (stage) {
+    // 2^-so dKV^T[d, slot] for this wave's d-range, DG tiles of 32 d at a time:
+    //   Q^T dS_hi + Q^T dS_lo + (2^-so dO)^T P, k over the block's heads.
+    // C layout: lane holds slot (lane & 31), d = w*DW + 32 dt + 8 (r >> 2) + 4 kg + (r & 3).
+    // Masked slots store into this workgroup's spare row (after all staging rows of the chunk),
+    // so the stores need no per-slot branches.
+    const int32_t dst_this = slot_in_range(idx_this, S_kv) ? pos_this + hblk : spare;
+    int32_t rowi[NI];
+    if constexpr (STAGED && !DEFER) {
 #pragma unroll
       for (int n = 0; n < NI; n++) rowi[n] = __shfl(dst_this, n * RPS + lane / LPR);
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; r++) rowi[r] = __shfl(dst_this, 8 * (r >> 2) + 4 * kg + (r & 3));
     }
-    float* outb = stage ? nullptr : acc_b + w * DW + (lane & 31);  // atomic mode only
-    char* ob = obuf[w];
-    auto afrag = [&](int ks, int m) {
+    char* ob = obuf[w] + (lane & 31) * OP + 8 * kg;  // this lane's slot row in the transpose
+    auto bfrag = [&](int ks, int m) {
       const char* p = pds + m * SB + pr_off + ks * 16 * T * 2;
       return join_tr(lds_load_tr(p), lds_load_tr(p + 4 * T * 2));
     };
@@ -596,87 +632,113 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
       for (int i = 0; i < DG; i++)
 #pragma unroll
         for (int r = 0; r < 16; r++) c[i][r] = 0.f;
-      bf16x8 acur[4], anxt[4];
+      bf16x8 bcur[3], bnxt[3];
 #pragma unroll
-      for (int m = 0; m < 4; m++) acur[m] = afrag(0, m);
+      for (int m = 0; m < 3; m++) bcur[m] = bfrag(0, m);
+      if constexpr (DEFER) {
+        eread();
+#pragma unroll
+        for (int k = 0; k < SPK; k++) dread(k);
+      }
 #pragma unroll
       for (int ks = 0; ks < KH; ks++) {
         __builtin_amdgcn_sched_barrier(0);
         if (ks + 1 < KH) {
 #pragma unroll
-          for (int m = 0; m < 4; m++) anxt[m] = afrag(ks + 1, m);
+          for (int m = 0; m < 3; m++) bnxt[m] = bfrag(ks + 1, m);
+        }
+        if constexpr (DEFER) {
+          // the previous block's rows of this k-step, then the reads for the next one
+          if (ks == 0) estore();
+#pragma unroll
+          for (int k = SPK * ks; k < SPK * (ks + 1); k++) dstore(k);
+#pragma unroll
+          for (int k = SPK * (ks + 1); k < SPK * (ks + 2); k++) dread(k);
         }
 #pragma unroll
-        for (int m = 0; m < 4; m++)
+        for (int m = 0; m < 3; m++)
 #pragma unroll
           for (int i = 0; i < DG; i++) {
             const int dt = dg * DG + i;
-            c[i] = mfma32(acur[m], m < 2 ? qv[dt][ks] : dov[dt][ks], c[i]);
+            if (m < 2) c[i] = mfma32(qv[dt][ks], bcur[m], c[i]);
+            else c[i] = mfma32h(dov[dt][ks], __builtin_bit_cast(f16x8, bcur[m]), c[i]);
           }
         if (ks + 1 < KH) {
 #pragma unroll
-          for (int m = 0; m < 4; m++) acur[m] = anxt[m];
+          for (int m = 0; m < 3; m++) bcur[m] = bnxt[m];
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (stage) {
-        // one exponent for this wave's 32 rows of the group, then fp16 column writes into this
-        // wave's transpose buffer (slot row t, d column 32 i + lane & 31)
-        float m = 0.f;
-#pragma unroll
-        for (int i = 0; i < DG; i++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) m = fmaxf(m, fabsf(c[i][r]));
-        const int e = stage_exponent(wave_max(m));
-        if (e != 0) {
+      if constexpr (!STAGED) {
+        if (dg == NDT / DG - 1) wait_all_mem();  // this wave's part of tile blk + 1
+        // fp32 atomics of the valid slots' values (lane: slot lane & 31)
+        const int32_t kvrow = __shfl(idx_this, lane & 31);
+        if ((mask >> (lane & 31)) & 1ull) {
+          float* p = dkv_acc + (b * S_kv + kvrow) * D + w * DW + SEGW * dg + 4 * kg;
 #pragma unroll
           for (int i = 0; i < DG; i++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) c[i][r] = __builtin_amdgcn_ldexpf(c[i][r], -e);
+            for (int r = 0; r < 16; r++)
+              unsafeAtomicAdd(p + 32 * i + 8 * (r >> 2) + (r & 3), __builtin_amdgcn_ldexpf(c[i][r], so));
         }
+        continue;
+      }
+      // one exponent per slot row segment (this lane and lane ^ 32 hold the row's values), then
+      // fp16 runs of four d into this wave's transpose buffer
+      float mx = 0.f;
+#pragma unroll
+      for (int i = 0; i < DG; i++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) mx = fmaxf(mx, fabsf(c[i][r]));
+      const int e = stage_exponent(half_swap_max(mx));
+      int es = e + so;  // the stored exponent also undoes the dO scale
+      es = es < -127 ? -127 : (es > 127 ? 127 : es);
+      if (__ballot(e != 0)) {
 #pragma unroll
         for (int i = 0; i < DG; i++)
 #pragma unroll
-          for (int r = 0; r < 16; r++) {
-            const int t = 8 * (r >> 2) + 4 * kg + (r & 3);
-            *(_Float16*)(ob + t * OP + (32 * i + (lane & 31)) * 2) = (_Float16)c[i][r];
-          }
-        if constexpr (DEFER) {
-          if (lane < T) obdst[w][lane] = dst_this;
-          wait_all_mem();  // this wave's part of tile blk + 1
-          pending = true;
-          pending_e = e;
-          continue;
-        }
-        if (dg == NDT / DG - 1) wait_all_mem();  // this wave's part of tile blk + 1
-        // row reads: lane covers 8 consecutive d of slot row n*RPS + lane/LPR
-        const int d0 = w * DW + SEGW * dg + 8 * (lane % LPR);
-#pragma unroll
-        for (int n = 0; n < NI; n++) {
-          const i32x4 v = *(const i32x4*)(ob + (n * RPS + lane / LPR) * OP + 16 * (lane % LPR));
-          __builtin_nontemporal_store(v, (i32x4*)(stage + (int64_t)rowi[n] * D + d0));
-        }
-        // the group's exponent for its 32 rows (row indices as the lanes below 32 hold them)
-        if (lane < T) stage_exp[(int64_t)dst_this * NSEG + (w * DW + SEGW * dg) / SEGW] = (int8_t)e;
-      } else {
-        if (dg == NDT / DG - 1) wait_all_mem();  // this wave's part of tile blk + 1
-        const uint32_t vk = (uint32_t)(mask >> (4 * kg));  // bit 8 (r>>2) + (r&3): slot of C row r
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-          if ((vk >> (8 * (r >> 2) + (r & 3))) & 1u) {
-            float* p = outb + (int64_t)rowi[r] * D + 32 * dg * DG;
-#pragma unroll
-            for (int i = 0; i < DG; i++) unsafeAtomicAdd(p + 32 * i, c[i][r]);
-          }
-        }
+          for (int r = 0; r < 16; r++) c[i][r] = __builtin_amdgcn_ldexpf(c[i][r], -e);
       }
+#pragma unroll
+      for (int i = 0; i < DG; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const f16x2 a = __builtin_convertvector((f32x2){c[i][4 * j], c[i][4 * j + 1]}, f16x2);
+          const f16x2 b2 = __builtin_convertvector((f32x2){c[i][4 * j + 2], c[i][4 * j + 3]}, f16x2);
+          *(i32x2*)(ob + obuf_chunk(lane & 31, 4 * i + j)) = i32x2{__builtin_bit_cast(int, a), __builtin_bit_cast(int, b2)};
+        }
+      if constexpr (DEFER) {
+        if (lane < T) obdst[w][lane] = dst_this;
+        wait_all_mem();  // this wave's part of tile blk + 1
+        pending_e = es;
+        continue;
+      }
+      if (dg == NDT / DG - 1) wait_all_mem();  // this wave's part of tile blk + 1
+      // row reads: lane covers 8 consecutive d of slot row n*RPS + lane/LPR
+      const int d0 = w * DW + SEGW * dg + 8 * (lane % LPR);
+#pragma unroll
+      for (int n = 0; n < NI; n++) {
+        const i32x4 v = rdpiece(n);
+        __builtin_nontemporal_store(v, (i32x4*)(stage + (int64_t)rowi[n] * D + d0));
+      }
+      // the row exponents of this group (lane < 32 holds slot row lane)
+      if (lane < T) stage_exp[(int64_t)dst_this * NSEG + (w * DW + SEGW * dg) / SEGW] = (int8_t)es;
     }
   };
   for (int blk = 0; blk < nblk; blk += 2) {
     block(IntTag<0>{}, blk);
     if (blk + 1 < nblk) block(IntTag<1>{}, blk + 1);
   }
-  flush_pending(false);
+  if constexpr (DEFER) {  // the last block's rows
+    eread();
+    estore();
+#pragma unroll
+    for (int k = 0; k < NI; k++) {
+      dread(k);
+      dstore(k);
+    }
+  }
+  wait_all_mem();  // no gather may still write LDS when the workgroup ends
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -900,10 +962,16 @@ static hipError_t launch_bwd_main_t(const BwdMainArgs& a, int which, hipStream_t
     if (e != hipSuccess) return e;
   }
   if (!(which & 2)) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, NW>), dim3((unsigned)(a.n_chunk * n_hblk)), dim3(NW * 64), 0, st,
-                     (const uint16_t*)a.q, (const uint16_t*)a.kv, (const uint16_t*)a.d_o, a.idx, a.lse, a.delta,
-                     a.dkv_accum, a.pos, a.stage, a.stage_exp, (int)a.S, a.S_kv, (int)a.H, (int)a.topk, a.sm_scale,
-                     sl2, n_hblk, (int)a.token0, (int)a.n_chunk);
+  if (a.stage)
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, true>), dim3((unsigned)(a.n_chunk * n_hblk)), dim3(NW * 64), 0, st,
+                       (const uint16_t*)a.q, (const uint16_t*)a.kv, (const uint16_t*)a.d_o, a.idx, a.lse, a.delta,
+                       nullptr, a.pos, a.stage, a.stage_exp, (int)a.S, a.S_kv, (int)a.H, (int)a.topk, a.sm_scale,
+                       sl2, n_hblk, (int)a.token0, (int)a.n_chunk);
+  else
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, false>), dim3((unsigned)(a.n_chunk * n_hblk)), dim3(NW * 64), 0, st,
+                       (const uint16_t*)a.q, (const uint16_t*)a.kv, (const uint16_t*)a.d_o, a.idx, a.lse, a.delta,
+                       a.dkv_accum, nullptr, nullptr, nullptr, (int)a.S, a.S_kv, (int)a.H, (int)a.topk, a.sm_scale,
+                       sl2, n_hblk, (int)a.token0, (int)a.n_chunk);
   return hipGetLastError();
 }
 

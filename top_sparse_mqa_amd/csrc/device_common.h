@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace smqa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -12,6 +14,12 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 #define SMQA_LDS __attribute__((address_space(3)))
 
@@ -27,6 +35,10 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // column (l & 15), rows 4*(l>>4) + r.
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// v_mfma_f32_32x32x16_f16: operand layouts as mfma32.
+__device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 lds_load16(const char* p) {
@@ -76,6 +88,7 @@ __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); 
 // operands from there directly), leaving the vector registers to accumulators and in-flight
 // fragments.
 __device__ __forceinline__ void keep_in_agpr(bf16x8& v) { asm volatile("" : "+a"(v)); }
+__device__ __forceinline__ void keep_in_agpr(f16x8& v) { asm volatile("" : "+a"(v)); }
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *(const uint4*)p);
@@ -92,10 +105,6 @@ __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) 
   return __builtin_bit_cast(uint2, v);
 }
 
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Maximum over the four lanes of a hardware quad (DPP quad permutations, no LDS traffic).
 __device__ __forceinline__ float quad_max(float m) {
@@ -108,7 +117,19 @@ __device__ __forceinline__ float quad_max(float m) {
 template <int V>
 struct IntTag {
   static constexpr int value = V;
+  __device__ constexpr operator int() const { return V; }
 };
+
+// f(IntTag<0>{}), ..., f(IntTag<N-1>{}): a loop unrolled by construction, for pipelines whose
+// stages must see their index as a constant (the unroller may decline a large body).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(IntTag<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ float wave_max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 
