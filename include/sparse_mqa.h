@@ -95,6 +95,15 @@ int sparse_mqa_bwd(const void* q, const void* kv, const float* attn_sink, const 
 int sparse_mqa_bwd_preprocess(const void* o, const void* d_o, float* delta, int64_t B, int64_t S,
                               int64_t H, int64_t D, void* stream);
 
+/* Gradient of the attention sink (bwd page: attn_sink is an input of the backward; fwd page:
+ * the sink is a per-head denominator bias with no value vector). With p_sink = exp(sink_h) / Z =
+ * 2^(sink_h log2 e - LSE) and Delta = <O, dO> (sparse_mqa_bwd_preprocess):
+ *   d_sink[h] = -sum_{b,s} 2^(sink_h log2 e - lse[b,s,h]) * delta[b,s,h]        (fp32)
+ * lse and delta are [B,S,H] fp32, attn_sink and d_sink [H] fp32; a -inf sink gets 0. The
+ * reduction order is fixed (deterministic). d_sink must not overlap the inputs. */
+int sparse_mqa_bwd_dsink(const float* lse, const float* delta, const float* attn_sink, float* d_sink, int64_t B,
+                         int64_t S, int64_t H, void* stream);
+
 /* Stage: dQ alone (bwd page, bwd factory): writes dq (bf16) from q, kv, dO, indices, LSE, Delta. */
 int sparse_mqa_bwd_dq(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs,
                       const float* lse, const float* delta, void* dq, int64_t B, int64_t S,

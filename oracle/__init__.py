@@ -137,3 +137,27 @@ def dkv(q, kv, o, do, topk_idxs, lse, sm_scale: Optional[float] = None, rows: Op
         B, S, S_kv, H, D, topk, _scale(sm_scale, D), None if rw is None else rw.ctypes.data,
         n if rw is not None else 0, out.data_ptr())
     return out
+
+
+def dsink(o, do, lse, attn_sink, precision: str = "f64") -> torch.Tensor:
+    """Gradient of L = sum(O * dO) with respect to attn_sink, d_sink [H].
+
+    The sink adds exp(sink_h) to the softmax denominator and carries no value vector (fwd page,
+    attn_sink note), so O = sum_t p_t v_t with p_t = exp(z_t) / Z and dZ/dsink_h = exp(sink_h).
+    Then dO . dO/dsink_h = -p_sink * sum_t p_t (dO . v_t) = -p_sink * Delta, with
+    p_sink = exp(sink_h) / Z = 2^(sink_h log2 e - LSE) (LSE in log2 units) and Delta = <O, dO>
+    from the O that is passed (as for dQ and dKV). Summed over all tokens:
+        d_sink[h] = -sum_{b,s} 2^(sink_h log2 e - LSE[b,s,h]) * Delta[b,s,h].
+    A sink of -inf has p_sink = 0 (its gradient is 0); plain torch ops in the working precision.
+    """
+    dt = _dtype(precision)
+    orr, dor = _real(o, dt), _real(do, dt)
+    B, S, H, D = orr.shape
+    lser = _real(lse, dt).view(B, S, H)
+    sink = attn_sink.detach().cpu().to(torch.float32).to(dt)
+    delta = (orr * dor).sum(-1)
+    log2e = 1.0 / math.log(2.0)
+    finite = torch.isfinite(sink)
+    expo = torch.where(finite.view(1, 1, H), sink.view(1, 1, H) * log2e - lser, torch.full_like(lser, -math.inf))
+    p_sink = torch.exp2(expo)
+    return -(p_sink * delta).sum(dim=(0, 1))

@@ -50,6 +50,29 @@ def check_lse(name: str, got: torch.Tensor, ref: torch.Tensor) -> None:
     assert m <= LSE_ATOL, f"{name}: max |err| {m} > {LSE_ATOL}"
 
 
+def check_dsink(name: str, got: torch.Tensor, ref: torch.Tensor, o: torch.Tensor, do: torch.Tensor,
+                lse: torch.Tensor, sink: torch.Tensor) -> None:
+    """d_sink against the oracle, per head: |err| <= 1e-4 * sum_t p_sink(t) sum_d |O dO| + 1e-30.
+    The scale bounds every term before cancellation; the GPU forms Delta as an fp32 dot of D
+    products (error <= D * 2^-24 of that scale) and sums B*S fp32 terms in a tree, so 1e-4 leaves
+    room while a dropped term, a wrong sign or a wrong head index is off by O(scale)."""
+    g = got.detach().double().cpu()
+    r = ref.detach().double().cpu()
+    H = r.shape[0]
+    assert g.shape == r.shape
+    assert not torch.isnan(g).any(), f"{name}: NaN in GPU output"
+    absdot = (o.double() * do.double()).abs().sum(-1).reshape(-1, H)
+    p = torch.exp2(sink.double().view(1, H) / math.log(2) - lse.double().reshape(-1, H))
+    p = torch.where(torch.isfinite(sink.double()).view(1, H), p, torch.zeros_like(p))
+    scale = (p * absdot).sum(0)
+    err = (g - r).abs()
+    say(f"  {name}: max|err| {float(err.max()):.3e}  max err/scale {float((err / (scale + 1e-30)).max()):.3e}")
+    bad = err > 1e-4 * scale + 1e-30
+    assert not bad.any(), f"{name}: heads {torch.nonzero(bad).view(-1).tolist()} outside the bound"
+    inf_heads = ~torch.isfinite(sink)
+    assert torch.all(g[inf_heads] == 0), f"{name}: heads with a -inf sink must get exactly 0"
+
+
 def sample_tokens(n_tokens: int, extra: int, seed: int, fixed: Iterable[int] = ()) -> List[int]:
     g = torch.Generator().manual_seed(seed)
     base = [t for t in fixed if 0 <= t < n_tokens]

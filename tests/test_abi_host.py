@@ -137,6 +137,18 @@ def test_stage_validation(lib):
     assert lib.sparse_mqa_bwd_postprocess(A, A + 16, 1, 16, 512, None) == ALIAS
 
 
+def test_dsink_validation(lib):
+    assert lib.sparse_mqa_bwd_dsink(None, Bp, C, Dp, 1, 8, 64, None) == NULL
+    assert lib.sparse_mqa_bwd_dsink(A, Bp, C, None, 1, 8, 64, None) == NULL
+    assert lib.sparse_mqa_bwd_dsink(A, Bp, C, Dp, 0, 8, 64, None) == SHAPE
+    assert lib.sparse_mqa_bwd_dsink(A, Bp, C, Dp, 1, 8, -1, None) == SHAPE
+    assert lib.sparse_mqa_bwd_dsink(A, Bp, C, Dp + 2, 1, 8, 64, None) == ALIGN
+    # d_sink over the last head of lse / delta, or over attn_sink itself
+    assert lib.sparse_mqa_bwd_dsink(A, Bp, C, A + 4 * (8 * 64 - 1), 1, 8, 64, None) == ALIAS
+    assert lib.sparse_mqa_bwd_dsink(A, Bp, C, Bp, 1, 8, 64, None) == ALIAS
+    assert lib.sparse_mqa_bwd_dsink(A, Bp, C, C + 4, 1, 8, 64, None) == ALIAS
+
+
 def test_dkv_step_validation(lib):
     """The separately enqueued dKV steps need a one-pass workspace and valid arguments."""
     B, S, S_kv, H, D, K = 1, 8, 16, 64, 512, 4

@@ -362,3 +362,74 @@ def test_token_and_row_subsets_match_full_outputs():
     assert torch.equal(oracle.dkv(x["q"], x["kv"], ob, x["do"], x["topk_idxs"], lb, rows=rows), dk[rows])
     # rows no token references are exactly zero (tokens only see positions <= s < 128)
     assert torch.count_nonzero(dk[128:]) == 0
+
+
+def dense_sink_grad(q, kv, sink, idx, scale, do):
+    """d_sink from torch.autograd through the dense reference (the sink as a leaf)."""
+    ss = sink.clone().requires_grad_(True)
+    o, _ = dense_reference(q, kv, ss, idx, scale)
+    (o * do).sum().backward()
+    return ss.grad
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_dsink_matches_dense_autograd_f64(case):
+    seed, B, S, S_kv, H, D, topk = case
+    q, kv, sink, idx, do = rand_case(seed, B, S, S_kv, H, D, topk)
+    sink = sink.float().double()
+    scale = 0.31
+    o, lse = oracle.fwd(q, kv, sink.float(), idx, sm_scale=scale, precision="f64")
+    ds = oracle.dsink(o.view(B, S, H, D), do, lse.view(B, S, H), sink.float())
+    torch.testing.assert_close(ds, dense_sink_grad(q, kv, sink, idx, scale, do), rtol=1e-9, atol=1e-11)
+
+
+def test_dsink_finite_differences():
+    """Central differences of L(sink) = sum(O(sink) * dO) through the oracle's own forward."""
+    B, S, S_kv, H, D, topk = 1, 6, 11, 3, 8, 7
+    q, kv, sink, idx, do = rand_case(5, B, S, S_kv, H, D, topk)
+    sink = sink.float().double()
+    scale = 0.4
+    o, lse = oracle.fwd(q, kv, sink.float(), idx, sm_scale=scale, precision="f64")
+    ds = oracle.dsink(o.view(B, S, H, D), do, lse.view(B, S, H), sink.float())
+    eps = 2.0 ** -12  # exact in fp32, the precision the oracle takes the sink in
+    for h in range(H):
+        e = torch.zeros(H, dtype=torch.float64)
+        e[h] = eps
+        op, _ = oracle.fwd(q, kv, (sink + e).float(), idx, sm_scale=scale, precision="f64")
+        om, _ = oracle.fwd(q, kv, (sink - e).float(), idx, sm_scale=scale, precision="f64")
+        fd = ((op - om).view(B, S, H, D) * do).sum() / (2 * eps)
+        assert abs(float(ds[h]) - float(fd)) <= 1e-6 * (1 + abs(float(fd))), (h, float(ds[h]), float(fd))
+
+
+def test_dsink_single_slot_closed_form():
+    """One head, one token, one valid slot: Z = e^z + e^sink, O = p v, d_sink = -(e^sink / Z) p (v . dO)."""
+    g = torch.Generator().manual_seed(11)
+    D = 8
+    q = torch.randn(1, 1, 1, D, generator=g, dtype=torch.float64)
+    kv = torch.randn(1, 3, D, generator=g, dtype=torch.float64)
+    do = torch.randn(1, 1, 1, D, generator=g, dtype=torch.float64)
+    idx = torch.tensor([[[2, -1]]], dtype=torch.int32)
+    sink = torch.tensor([0.25], dtype=torch.float32)
+    scale = 0.5
+    o, lse = oracle.fwd(q, kv, sink, idx, sm_scale=scale, precision="f64")
+    z = scale * float((q[0, 0, 0] * kv[0, 2]).sum())
+    zs = math.exp(z) + math.exp(0.25)
+    p = math.exp(z) / zs
+    expect = -(math.exp(0.25) / zs) * p * float((kv[0, 2] * do[0, 0, 0]).sum())
+    ds = oracle.dsink(o.view(1, 1, 1, D), do, lse.view(1, 1, 1), sink)
+    assert abs(float(ds[0]) - expect) <= 1e-12 * (1 + abs(expect))
+
+
+def test_dsink_minus_inf_sink_and_masked_tokens():
+    """A -inf sink has zero gradient (no NaN from its -inf LSE); a fully masked token adds nothing."""
+    B, S, S_kv, H, D, topk = 1, 4, 6, 2, 8, 3
+    q, kv, sink, idx, do = rand_case(9, B, S, S_kv, H, D, topk, extremes=False)
+    idx[0, 1] = -1  # token 1 fully masked
+    sink = torch.tensor([-math.inf, 0.5], dtype=torch.float32)
+    o, lse = oracle.fwd(q, kv, sink, idx, precision="f64")
+    ds = oracle.dsink(o.view(B, S, H, D), do, lse.view(B, S, H), sink)
+    assert float(ds[0]) == 0.0
+    keep = torch.ones(S, dtype=torch.bool)
+    keep[1] = False
+    ds_wo = oracle.dsink(o.view(B, S, H, D)[:, keep], do[:, keep], lse.view(B, S, H)[:, keep], sink)
+    assert torch.equal(ds, ds_wo) or abs(float(ds[1] - ds_wo[1])) < 1e-15

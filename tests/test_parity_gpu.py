@@ -15,8 +15,8 @@ import torch
 import oracle
 import top_sparse_mqa_amd as smqa
 from top_sparse_mqa_amd import synthetic as syn
-from parity_utils import (check_bf16, check_lse, conservation_rhs, referenced_rows, sample_tokens, say,
-                          valid_mask)
+from parity_utils import (check_bf16, check_dsink, check_lse, conservation_rhs, referenced_rows, sample_tokens,
+                          say, valid_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -68,6 +68,16 @@ def full_parity(x, scale=None, tag=""):
     delta = smqa.bwd_preprocess(ob.cuda(), xg["do"])
     torch.cuda.synchronize()
     torch.testing.assert_close(delta.view(-1, H).cpu().double(), delta_ref.double(), rtol=1e-4, atol=1e-4)
+    # attention-sink gradient, through the interface and as a stage on the same Delta
+    dsink_ref = oracle.dsink(ob, x["do"], lb, x["attn_sink"])
+    dq3, dkv3, dsink = smqa.sparse_mqa_bwd_interface(xg["q"], xg["kv"], xg["attn_sink"], ob.cuda(), xg["do"],
+                                                     xg["topk_idxs"], lb.cuda(), sm_scale=scale, return_d_sink=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dq3, dq), "dQ must not depend on return_d_sink"
+    check_dsink(f"{tag} d_sink", dsink, dsink_ref, ob, x["do"], lb, x["attn_sink"])
+    dsink2 = smqa.bwd_dsink(lb.cuda(), delta, xg["attn_sink"])
+    torch.cuda.synchronize()
+    assert torch.equal(dsink2, dsink), "d_sink must be deterministic"
     return o, lse
 
 
@@ -254,6 +264,10 @@ def test_headline_backward_sampled(gpu_lib, headline):
     # bf16 output path equals the round-to-nearest-even of an fp32 accumulation
     _, dkv16 = bwd_gpu(xg, ob.cuda(), lb.cuda())
     check_bf16("dKV bf16", dkv16.view(-1, w.D)[rows], dkv_ref)
+    # attention-sink gradient over every token
+    dsink = smqa.bwd_dsink(lb.cuda(), smqa.bwd_preprocess(ob.cuda(), xg["do"]), xg["attn_sink"])
+    torch.cuda.synchronize()
+    check_dsink("d_sink", dsink, oracle.dsink(ob, x["do"], lb, x["attn_sink"]), ob, x["do"], lb, x["attn_sink"])
 
 
 def _rows_refs(idx: torch.Tensor, S: int, S_kv: int, flat_rows):

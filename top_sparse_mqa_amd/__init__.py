@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     bwd_main,
     bwd_postprocess,
     bwd_workspace_bytes,
+    bwd_dsink,
     bwd_preprocess,
     default_scale,
     load_library,

@@ -28,6 +28,7 @@ _SIGS = {
     "sparse_mqa_bwd": [_c_void_p] * 9 + [ctypes.c_int, _c_void_p, ctypes.c_size_t] + [_i64] * 6
     + [ctypes.c_float, _c_void_p],
     "sparse_mqa_bwd_preprocess": [_c_void_p] * 3 + [_i64] * 4 + [_c_void_p],
+    "sparse_mqa_bwd_dsink": [_c_void_p] * 4 + [_i64] * 3 + [_c_void_p],
     "sparse_mqa_bwd_main": [_c_void_p] * 8 + [_i64] * 6 + [ctypes.c_float, _c_void_p],
     "sparse_mqa_bwd_dq": [_c_void_p] * 7 + [_i64] * 6 + [ctypes.c_float, _c_void_p],
     "sparse_mqa_bwd_dkv": [_c_void_p] * 7 + [ctypes.c_int, _c_void_p, ctypes.c_size_t] + [_i64] * 6
@@ -170,9 +171,11 @@ def sparse_mqa_fwd_interface(q: torch.Tensor, kv: torch.Tensor, attn_sink: torch
 def sparse_mqa_bwd_interface(q: torch.Tensor, kv: torch.Tensor, attn_sink: torch.Tensor, o: torch.Tensor,
                              do: torch.Tensor, topk_idxs: torch.Tensor, lse: torch.Tensor,
                              sm_scale: Optional[float] = None,
-                             return_dkv_accum_dtype: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+                             return_dkv_accum_dtype: bool = False,
+                             return_d_sink: bool = False) -> Tuple[torch.Tensor, ...]:
     """Backward: returns (dQ [B,S,H,D] bf16, dKV [B,S_kv,D] bf16, or fp32 when
-    return_dkv_accum_dtype)."""
+    return_dkv_accum_dtype), and with return_d_sink also d_sink [H] fp32, the gradient of
+    attn_sink."""
     _need(q, "q", torch.bfloat16, 4)
     _need(kv, "kv", torch.bfloat16, 3)
     _need(attn_sink, "attn_sink", torch.float32, 1)
@@ -199,7 +202,24 @@ def sparse_mqa_bwd_interface(q: torch.Tensor, kv: torch.Tensor, attn_sink: torch
         _ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(o), _ptr(do), _ptr(idx), _ptr(lse), _ptr(dq), _ptr(dkv),
         1 if return_dkv_accum_dtype else 0, _ptr(ws), ws_bytes, B, S, S_kv, H, D, topk,
         _scale_arg(sm_scale), _stream()))
+    if return_d_sink:
+        return dq, dkv, bwd_dsink(lse, bwd_preprocess(o, do), attn_sink)
     return dq, dkv
+
+
+def bwd_dsink(lse: torch.Tensor, delta: torch.Tensor, attn_sink: torch.Tensor) -> torch.Tensor:
+    """d_sink[h] = -sum_{b,s} exp(attn_sink[h] - LSE[b,s,h]) * Delta[b,s,h] (fp32 [H]); delta is
+    bwd_preprocess(o, do)."""
+    _need(lse, "lse", torch.float32, 3)
+    _need(delta, "delta", torch.float32, 3)
+    _need(attn_sink, "attn_sink", torch.float32, 1)
+    B, S, H = lse.shape
+    if tuple(delta.shape) != (B, S, H) or attn_sink.shape[0] != H:
+        raise ValueError("delta must be [B,S,H] like lse and attn_sink [H]")
+    d_sink = torch.empty(H, dtype=torch.float32, device=lse.device)
+    _check("sparse_mqa_bwd_dsink", load_library().sparse_mqa_bwd_dsink(
+        _ptr(lse), _ptr(delta), _ptr(attn_sink), _ptr(d_sink), B, S, H, _stream()))
+    return d_sink
 
 
 def bwd_preprocess(o: torch.Tensor, do: torch.Tensor) -> torch.Tensor:

@@ -247,6 +247,21 @@ int sparse_mqa_bwd_preprocess(const void* o, const void* d_o, float* delta, int6
                                                                                                  : SMQA_ERR_HIP;
 }
 
+int sparse_mqa_bwd_dsink(const float* lse, const float* delta, const float* attn_sink, float* d_sink, int64_t B,
+                         int64_t S, int64_t H, void* stream) {
+  if (!lse || !delta || !attn_sink || !d_sink) return SMQA_ERR_NULL;
+  if (B <= 0 || S <= 0 || H <= 0 || H > 65536) return SMQA_ERR_SHAPE;
+  const int64_t rows = count({B, S, H});
+  if (rows < 0) return SMQA_ERR_SHAPE;
+  if (!aligned4(lse) || !aligned4(delta) || !aligned4(attn_sink) || !aligned4(d_sink)) return SMQA_ERR_ALIGN;
+  const Span out{d_sink, H * 4};
+  if (overlap(out, {lse, rows * 4}) || overlap(out, {delta, rows * 4}) || overlap(out, {attn_sink, H * 4}))
+    return SMQA_ERR_ALIAS;
+  return smqa::launch_bwd_dsink(lse, delta, attn_sink, d_sink, B * S, H, (hipStream_t)stream) == hipSuccess
+             ? SMQA_OK
+             : SMQA_ERR_HIP;
+}
+
 int sparse_mqa_bwd_dq(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs, const float* lse,
                       const float* delta, void* dq, int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D,
                       int64_t topk, float sm_scale, void* stream) {

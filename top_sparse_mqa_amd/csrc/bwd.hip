@@ -72,6 +72,31 @@ delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, 
   if (row < rows && chunk == 0) delta[row] = s;
 }
 
+// d_sink[h] = -sum over tokens of 2^(sink_h log2 e - LSE) * Delta: the sink adds exp(sink_h) to
+// the softmax denominator and has no value vector, so its weight 2^(sink log2 e - LSE) scales
+// -<O, dO> (bwd page, attn_sink input; fwd page, attn_sink note). One workgroup per head; the
+// threads' partial sums are combined in a fixed order, so the result is deterministic. A sink of
+// -inf has weight 0 (its gradient is 0, and -inf - LSE is never formed).
+__global__ void __launch_bounds__(256)
+dsink_kernel(const float* __restrict__ lse, const float* __restrict__ delta, const float* __restrict__ sink,
+             float* __restrict__ d_sink, int64_t tokens, int H) {
+  __shared__ float part[4];
+  const int h = blockIdx.x;
+  const float sl = sink[h] * kLog2e;
+  float acc = 0.f;
+  if (sl > -__builtin_inff()) {
+    for (int64_t t = threadIdx.x; t < tokens; t += 256) {
+      const int64_t i = t * H + h;
+      acc += exp2f(sl - lse[i]) * delta[i];
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) d_sink[h] = -((part[0] + part[1]) + (part[2] + part[3]));
+}
+
 __global__ void __launch_bounds__(256) fill_zero_kernel(float4* __restrict__ p, int64_t n4) {
   const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) p[i] = z;
@@ -928,6 +953,12 @@ hipError_t launch_bwd_preprocess(const void* o, const void* d_o, float* delta, i
     hipLaunchKernelGGL(delta_kernel<64>, grid, block, 0, st, (const uint16_t*)o, (const uint16_t*)d_o, delta, rows);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dsink(const float* lse, const float* delta, const float* sink, float* d_sink, int64_t tokens,
+                            int64_t H, hipStream_t st) {
+  hipLaunchKernelGGL(dsink_kernel, dim3((unsigned)H), dim3(256), 0, st, lse, delta, sink, d_sink, tokens, (int)H);
   return hipGetLastError();
 }
 

@@ -49,6 +49,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_preprocess(const void* o, const void* d_o, float* delta, int64_t rows, int64_t D,
                                  hipStream_t st);
 hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t st);
+// d_sink[h] = -sum_t 2^(sink_h log2 e - lse[t,h]) * delta[t,h] over tokens t (one workgroup per head).
+hipError_t launch_bwd_dsink(const float* lse, const float* delta, const float* sink, float* d_sink, int64_t tokens,
+                            int64_t H, hipStream_t st);
 // which: 1 = dQ kernel (all tokens), 2 = dKV kernel (chunk; atomic or staging mode), 3 = both.
 hipError_t launch_bwd_main(const BwdMainArgs& a, int which, hipStream_t st);
 // Staging-row assignment for the tokens [token0, token0 + n_chunk): clears count, ranks every valid
