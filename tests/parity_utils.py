@@ -51,11 +51,13 @@ def check_lse(name: str, got: torch.Tensor, ref: torch.Tensor) -> None:
 
 
 def check_dsink(name: str, got: torch.Tensor, ref: torch.Tensor, o: torch.Tensor, do: torch.Tensor,
-                lse: torch.Tensor, sink: torch.Tensor) -> None:
-    """d_sink against the oracle, per head: |err| <= 1e-4 * sum_t p_sink(t) sum_d |O dO| + 1e-30.
-    The scale bounds every term before cancellation; the GPU forms Delta as an fp32 dot of D
-    products (error <= D * 2^-24 of that scale) and sums B*S fp32 terms in a tree, so 1e-4 leaves
-    room while a dropped term, a wrong sign or a wrong head index is off by O(scale)."""
+                lse: torch.Tensor, sink: torch.Tensor, rel: float = 1e-4) -> None:
+    """d_sink against the oracle, per head: |err| <= rel * sum_t p_sink(t) sum_d |O dO| + 1e-30.
+    The scale bounds every term before cancellation. On the same O and LSE the GPU forms Delta as
+    an fp32 dot of D products (error <= D * 2^-24 of that scale) and sums B*S fp32 terms in a
+    tree, so rel = 1e-4 leaves room while a dropped term, a wrong sign or a wrong head index is
+    off by O(scale). When the GPU's O is its own bf16 forward output rather than the oracle's,
+    each element may differ by one bf16 ulp (2^-7 relative), so rel = 1e-2 bounds that case."""
     g = got.detach().double().cpu()
     r = ref.detach().double().cpu()
     H = r.shape[0]
@@ -67,7 +69,7 @@ def check_dsink(name: str, got: torch.Tensor, ref: torch.Tensor, o: torch.Tensor
     scale = (p * absdot).sum(0)
     err = (g - r).abs()
     say(f"  {name}: max|err| {float(err.max()):.3e}  max err/scale {float((err / (scale + 1e-30)).max()):.3e}")
-    bad = err > 1e-4 * scale + 1e-30
+    bad = err > rel * scale + 1e-30
     assert not bad.any(), f"{name}: heads {torch.nonzero(bad).view(-1).tolist()} outside the bound"
     inf_heads = ~torch.isfinite(sink)
     assert torch.all(g[inf_heads] == 0), f"{name}: heads with a -inf sink must get exactly 0"

@@ -7,6 +7,7 @@ import re
 from pathlib import Path
 
 import pytest
+import torch
 
 import top_sparse_mqa_amd as smqa
 
@@ -171,3 +172,11 @@ def test_dkv_step_validation(lib):
     assert lib.sparse_mqa_bwd_dkv_reduce(A + 8, 0, G, full, *dims, None) == ALIGN
     assert lib.sparse_mqa_bwd_dkv_reduce(A, 0, G, 100, *dims, None) == WORKSPACE
     assert lib.sparse_mqa_bwd_dkv_reduce(G + 256, 1, G, full, *dims, None) == ALIAS
+
+
+def test_autograd_refuses_cpu_tensors():
+    """The differentiable wrapper has no CPU path: CPU tensors are an error, not a fallback."""
+    q = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16, requires_grad=True)
+    kv = torch.zeros(1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        smqa.sparse_mqa(q, kv, torch.zeros(16), torch.zeros(1, 2, 4, dtype=torch.int32))

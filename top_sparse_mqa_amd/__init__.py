@@ -20,3 +20,4 @@ from .binding import (  # noqa: F401
     sparse_mqa_bwd_interface,
     sparse_mqa_fwd_interface,
 )
+from .autograd import SparseMQAFunction, sparse_mqa  # noqa: F401
