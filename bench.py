@@ -98,7 +98,7 @@ class Step:
         p = lambda t: t.data_ptr()  # noqa: E731
         calls = {
             "fwd": lambda: L.sparse_mqa_fwd(p(self.q), p(self.kv), p(self.sink), p(self.idx), p(self.o),
-                                            p(self.lse), B, S, S_kv, H, D, K, self.nan, h),
+                                            p(self.lse), B, S, S_kv, H, D, K, self.nan, 0, h),
             "bwd_preprocess": lambda: L.sparse_mqa_bwd_preprocess(p(self.o), p(self.do), p(self.delta), B, S, H, D, h),
             "bwd_dq": lambda: L.sparse_mqa_bwd_dq(p(self.q), p(self.kv), p(self.do), p(self.idx), p(self.lse),
                                                   p(self.delta), p(self.dq), B, S, S_kv, H, D, K, self.nan, h),

@@ -62,10 +62,14 @@ enum {
 };
 
 /* Forward (fwd page, sparse_mqa_fwd_interface). Reads q, kv, attn_sink, topk_idxs; writes
- * o [B,S,H,D] bf16 and lse [B,S,H] fp32 (log2 units). sm_scale = NaN selects D^-0.5. */
+ * o [B,S,H,D] bf16 and lse [B,S,H] fp32 (log2 units). sm_scale = NaN selects D^-0.5.
+ * reference_rounding (fwd page, the option of that name): 0 forms each score as
+ * fp32(dot * fp32(sm_scale * log2 e)) and runs the softmax in base 2; 1 rounds the scaled logit
+ * fp32(dot * sm_scale) in natural units, subtracts the running max there and only then changes
+ * to base 2 for the exponential; LSE is log2 units in both. Other values: SMQA_ERR_ARG. */
 int sparse_mqa_fwd(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs,
                    void* o, float* lse, int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D,
-                   int64_t topk, float sm_scale, void* stream);
+                   int64_t topk, float sm_scale, int reference_rounding, void* stream);
 
 /* Backward workspace. sparse_mqa_bwd and sparse_mqa_bwd_dkv take a device workspace: Delta
  * [B,S,H] fp32 (sparse_mqa_bwd only), per-row counters and offsets, and the staging rows of the

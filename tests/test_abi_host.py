@@ -51,12 +51,14 @@ def test_status_strings(lib):
     assert lib.sparse_mqa_status_string(99) == b"unknown status"
 
 
-def fwd(lib, q=A, kv=Bp, sink=C, idx=Dp, o=E, lse=F_, B=1, S=8, S_kv=16, H=64, D=512, topk=4, scale=NAN):
-    return lib.sparse_mqa_fwd(q, kv, sink, idx, o, lse, B, S, S_kv, H, D, topk, scale, None)
+def fwd(lib, q=A, kv=Bp, sink=C, idx=Dp, o=E, lse=F_, B=1, S=8, S_kv=16, H=64, D=512, topk=4, scale=NAN, rr=0):
+    return lib.sparse_mqa_fwd(q, kv, sink, idx, o, lse, B, S, S_kv, H, D, topk, scale, rr, None)
 
 
 def test_fwd_validation(lib):
     assert fwd(lib, q=None) == NULL
+    assert fwd(lib, rr=2) == ARG
+    assert fwd(lib, rr=-1) == ARG
     assert fwd(lib, lse=None) == NULL
     assert fwd(lib, B=0) == SHAPE
     assert fwd(lib, topk=-1) == SHAPE

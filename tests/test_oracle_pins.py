@@ -13,6 +13,7 @@ LSE, a transposed operand, a wrong sign in dS, a dKV row off by one) fails at le
 """
 import math
 
+import numpy as np
 import pytest
 import torch
 import torch.nn.functional as F
@@ -433,3 +434,39 @@ def test_dsink_minus_inf_sink_and_masked_tokens():
     keep[1] = False
     ds_wo = oracle.dsink(o.view(B, S, H, D)[:, keep], do[:, keep], lse.view(B, S, H)[:, keep], sink)
     assert torch.equal(ds, ds_wo) or abs(float(ds[1] - ds_wo[1])) < 1e-15
+
+
+def large_logit_case(H=1, D=8, seed=0):
+    """Scores near 2^21 (fp32 spacing 0.25) whose exact dot products are integers < 2^24, so a
+    dot product is exact in fp32 and only the product with sm_scale rounds. Slots differ by
+    O(1) in the logit, so that rounding moves the softmax weights visibly."""
+    g = torch.Generator().manual_seed(seed)
+    K = 6
+    q = torch.zeros(1, 1, H, D)
+    q[..., 0] = 2048.0
+    q[..., 1] = 1.0
+    kv = torch.zeros(1, K, D)
+    kv[0, :, 0] = 7936.0
+    kv[0, :, 1] = torch.tensor([0.0, 1.0, 2.0, 3.0, 5.0, 8.0])
+    kv[0, :, 2:] = torch.randint(-3, 4, (K, D - 2), generator=g).float()
+    idx = torch.arange(K, dtype=torch.int32).view(1, 1, K)
+    return q.to(torch.bfloat16), kv.to(torch.bfloat16), torch.zeros(H), idx
+
+
+def test_f32_oracle_rounds_the_scaled_logit_to_fp32():
+    """fwd page, reference_rounding option: the fp32 arithmetic rounds the scaled logit
+    dot * sm_scale to fp32 before the softmax. Computed here by hand (numpy float32 for the one
+    rounding, float64 for the rest) and compared with the fp32 oracle; the float64 oracle, which
+    keeps the exact logits, lands visibly elsewhere on this case."""
+    q, kv, sink, idx = large_logit_case()
+    sm = 0.13
+    o32, lse32 = oracle.fwd(q, kv, sink, idx, sm_scale=sm, precision="f32")
+    dots = (q[0, 0, 0].double() @ kv[0].double().T).numpy()
+    assert np.all(dots == np.round(dots)) and dots.max() < 2 ** 24
+    z = (dots.astype(np.float32) * np.float32(sm)).astype(np.float32).astype(np.float64)
+    w = np.exp(z - z.max())
+    expect = (w @ kv[0].double().numpy()) / w.sum()
+    np.testing.assert_allclose(o32[0, 0].double().numpy(), expect, rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(float(lse32[0, 0]), (z.max() + math.log(w.sum())) / math.log(2), rtol=1e-7)
+    o64, _ = oracle.fwd(q, kv, sink, idx, sm_scale=sm, precision="f64")
+    assert float((o64[0, 0, 2:] - o32[0, 0, 2:]).abs().max()) > 0.05

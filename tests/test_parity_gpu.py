@@ -15,8 +15,8 @@ import torch
 import oracle
 import top_sparse_mqa_amd as smqa
 from top_sparse_mqa_amd import synthetic as syn
-from parity_utils import (check_bf16, check_dsink, check_lse, conservation_rhs, referenced_rows, sample_tokens,
-                          say, valid_mask)
+from parity_utils import (LSE_ATOL, check_bf16, check_dsink, check_lse, conservation_rhs, referenced_rows,
+                          sample_tokens, say, valid_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -213,6 +213,63 @@ def test_non_default_stream(gpu_lib):
         o, lse = smqa.sparse_mqa_fwd_interface(xg["q"], xg["kv"], xg["attn_sink"], xg["topk_idxs"])
     s.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
+
+
+def test_reference_rounding_mid(gpu_lib):
+    """reference_rounding on an ordinary workload: within the bar of the fp32 oracle (whose
+    arithmetic rounds the scaled logit the same way), and close to the default mode."""
+    w = syn.WORKLOADS["mid_h64_d512_k300"]
+    say("case", w.describe(), "reference_rounding")
+    x = syn.workload_inputs(w)
+    xg = gpu(x)
+    o, lse = smqa.sparse_mqa_fwd_interface(xg["q"], xg["kv"], xg["attn_sink"], xg["topk_idxs"],
+                                           reference_rounding=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.fwd(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"])
+    check_bf16("O rr", o.view(-1, w.H, w.D), o_ref)
+    check_lse("LSE rr", lse.view(-1, w.H), lse_ref)
+    o2, lse2 = fwd_gpu(xg)
+    check_bf16("O rr vs default", o.view(-1, w.H, w.D), o2.view(-1, w.H, w.D))
+    check_lse("LSE rr vs default", lse, lse2)
+
+
+def large_logit_inputs(B=1, S=16, S_kv=128, H=16, D=64, topk=64, seed=3):
+    """Logits near 2^21 from integer-valued bf16 inputs: every dot product is an integer below
+    2^24 (exact in fp32 in any order), so the only rounding before the softmax is that of the
+    scaled logit, and it moves the weights by up to e^(1/8)."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randint(-2, 3, (B, S, H, D), generator=g).float()
+    q[..., 0] = 2048.0
+    kv = torch.randint(-3, 4, (B, S_kv, D), generator=g).float()
+    kv[..., 0] = 7936.0
+    idx = torch.stack([torch.randperm(S_kv, generator=g)[:topk] for _ in range(B * S)]).view(B, S, topk)
+    return {"q": q.to(torch.bfloat16), "kv": kv.to(torch.bfloat16), "attn_sink": torch.zeros(H),
+            "topk_idxs": idx.to(torch.int32)}
+
+
+@pytest.mark.parametrize("H,D", [(16, 64), (64, 512)])
+def test_reference_rounding_large_logits(gpu_lib, H, D):
+    x = large_logit_inputs(H=H, D=D)
+    say("case reference_rounding large logits", dict(H=H, D=D))
+    dots = x["q"].double().view(-1, D) @ x["kv"].double().view(-1, D).T
+    assert float(dots.abs().max()) < 2 ** 24
+    sm = 0.13
+    xg = gpu(x)
+    o, lse = smqa.sparse_mqa_fwd_interface(xg["q"], xg["kv"], xg["attn_sink"], xg["topk_idxs"], sm_scale=sm,
+                                           reference_rounding=True)
+    od, _ = fwd_gpu(xg, sm)
+    o_ref, lse_ref = oracle.fwd(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], sm_scale=sm)
+    check_bf16("O rr", o.view(-1, H, D), o_ref)
+    # LSE near 3e6 (log2 units): fp32 spacing there is 0.25, so the bar is a few spacings
+    g, r = lse.view(-1, H).double().cpu(), lse_ref.double()
+    spacing = torch.tensor(2.0).pow(torch.floor(torch.log2(r.abs())) - 23)
+    err = (g - r).abs()
+    say(f"  LSE rr: max|err| {float(err.max()):.3e} (spacing {float(spacing.max()):.3e})")
+    assert torch.all(err <= 4 * spacing + LSE_ATOL)
+    # the default mode scales into base 2 before rounding: its weights differ here
+    dd = (od.view(-1, H, D).double().cpu() - o_ref.double()).abs()
+    say(f"  O default mode vs fp32 oracle: max|err| {float(dd.max()):.3e}")
+    assert not torch.equal(od, o)
 
 
 # ------------------------------------------------------------------------------------------------

@@ -22,7 +22,7 @@ _c_void_p = ctypes.c_void_p
 _i64 = ctypes.c_int64
 
 _SIGS = {
-    "sparse_mqa_fwd": [_c_void_p] * 6 + [_i64] * 6 + [ctypes.c_float, _c_void_p],
+    "sparse_mqa_fwd": [_c_void_p] * 6 + [_i64] * 6 + [ctypes.c_float, ctypes.c_int, _c_void_p],
     "sparse_mqa_bwd_workspace_bytes": [_i64] * 6,
     "sparse_mqa_bwd_workspace_min_bytes": [_i64] * 6,
     "sparse_mqa_bwd": [_c_void_p] * 9 + [ctypes.c_int, _c_void_p, ctypes.c_size_t] + [_i64] * 6
@@ -141,11 +141,12 @@ def sparse_mqa_fwd_interface(q: torch.Tensor, kv: torch.Tensor, attn_sink: torch
                              reference_rounding: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """Forward: returns (O [B,S,H,D] bf16, LSE [B,S,H] fp32 in log2 units).
 
+    reference_rounding rounds each scaled logit dot * sm_scale to fp32 in natural units and
+    subtracts the running max there before the exponential (the default scales straight into
+    base 2); LSE is in log2 units either way, so the backward is the same.
     block_I, num_stages and threads are tuning knobs of the pages' kernel generator; they are
     accepted and ignored (the gfx950 kernels pick their own tiling)."""
     del block_I, num_stages, threads
-    if reference_rounding:
-        raise NotImplementedError("reference_rounding=True is not implemented")
     _need(q, "q", torch.bfloat16, 4)
     _need(kv, "kv", torch.bfloat16, 3)
     _need(attn_sink, "attn_sink", torch.float32, 1)
@@ -164,7 +165,7 @@ def sparse_mqa_fwd_interface(q: torch.Tensor, kv: torch.Tensor, attn_sink: torch
     lib = load_library()
     _check("sparse_mqa_fwd", lib.sparse_mqa_fwd(
         _ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(idx), _ptr(o), _ptr(lse),
-        B, S, S_kv, H, D, topk, _scale_arg(sm_scale), _stream()))
+        B, S, S_kv, H, D, topk, _scale_arg(sm_scale), 1 if reference_rounding else 0, _stream()))
     return o, lse
 
 

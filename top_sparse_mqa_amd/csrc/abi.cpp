@@ -82,8 +82,9 @@ const char* sparse_mqa_status_string(int status) {
 
 int sparse_mqa_fwd(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idxs, void* o,
                    float* lse, int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk,
-                   float sm_scale, void* stream) {
+                   float sm_scale, int reference_rounding, void* stream) {
   if (!q || !kv || !attn_sink || !topk_idxs || !o || !lse) return SMQA_ERR_NULL;
+  if (reference_rounding != 0 && reference_rounding != 1) return SMQA_ERR_ARG;
   int st = check_shapes(B, S, S_kv, H, D, topk);
   if (st) return st;
   if (!aligned16(q) || !aligned16(kv) || !aligned16(o) || !aligned4(lse) || !aligned4(attn_sink) ||
@@ -97,7 +98,7 @@ int sparse_mqa_fwd(const void* q, const void* kv, const float* attn_sink, const 
   for (const Span& s : ins)
     if (overlap(so, s) || overlap(sl, s)) return SMQA_ERR_ALIAS;
   if (overlap(so, sl)) return SMQA_ERR_ALIAS;
-  smqa::FwdArgs a{q, kv, attn_sink, topk_idxs, o, lse, B, S, S_kv, H, D, topk, scale};
+  smqa::FwdArgs a{q, kv, attn_sink, topk_idxs, o, lse, B, S, S_kv, H, D, topk, scale, reference_rounding};
   return smqa::launch_fwd(a, (hipStream_t)stream) == hipSuccess ? SMQA_OK : SMQA_ERR_HIP;
 }
 

@@ -5,6 +5,8 @@
 // global_load_lds_dwordx4, double-buffered) and used by every head:
 //   S^T[slot, head] = K[slot, :] . Q[head, :]^T    bf16 MFMA 32x32x16, K from LDS, Q in VGPRs
 //   online softmax in log2 units, sink folded into the running max and sum
+//   (RR: the scaled logit is rounded to fp32 in natural units first, and the max is subtracted
+//   before the change to base 2; LSE is written in log2 units either way)
 //   O^T[d, head]   += V^T[d, slot] . P^T[slot, head]  bf16 MFMA, V^T read with ds_read_b64_tr_b16
 // Waves are (head group of 32) x (half of D). Each wave keeps Q for its half of D, computes a
 // partial S^T over that half for all 64 slots, and swaps the fp32 partials with the other half
@@ -23,11 +25,16 @@ __device__ __forceinline__ int fwd_swz(int row) {
   return ((r & 3) << 2) | (r >> 2);
 }
 
-template <int D, int NHG>
+// score_scale multiplies the fp32 dot product: sm_scale * log2(e) (scores in log2 units), or
+// sm_scale alone when RR (scores in natural units, the fwd page's reference_rounding option).
+template <int D, int NHG, bool RR>
 __global__ void __launch_bounds__(NHG * 128)
 fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const float* __restrict__ sink,
            const int32_t* __restrict__ idx, uint16_t* __restrict__ out, float* __restrict__ lse, int S,
-           int64_t S_kv, int H, int topk, float scale_log2, int n_hblk, int n_tokens) {
+           int64_t S_kv, int H, int topk, float score_scale, int n_hblk, int n_tokens) {
+  // EU turns a difference of scores into log2 units; MAXSTEP is 8 in log2 units.
+  constexpr float EU = RR ? kLog2e : 1.f;
+  constexpr float MAXSTEP = RR ? 8.f * 0.693147180559945309f : 8.f;
   constexpr int T = 64;           // slots per block
   constexpr int NW = 2 * NHG;     // waves
   constexpr int DH = D / 2;       // d-columns owned by one wave of a head-group pair
@@ -70,7 +77,7 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) keep_in_agpr(qb[ks]);
   }
-  const float sink2 = head_ok ? sink[head] * kLog2e : 0.f;
+  const float sink2 = head_ok ? (RR ? sink[head] : sink[head] * kLog2e) : 0.f;
   float m_run = sink2;
   // The sink's share of the denominator is carried by the kg == 0 lane of each head.
   float l_run = (kg == 0 && sink2 != -INFINITY) ? 1.f : 0.f;
@@ -224,7 +231,7 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const int r = 4 * r4 + i;
-          const float v = (sacc[mt][r] + ov[i]) * scale_log2;
+          const float v = (sacc[mt][r] + ov[i]) * score_scale;
           sacc[mt][r] = ((vb >> (32 * mt + 8 * r4 + i)) & 1ull) ? v : -INFINITY;
           bmax = fmaxf(bmax, sacc[mt][r]);
         }
@@ -233,8 +240,8 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
     // The running max only moves when the block exceeds it by more than 8 (log2 units), so P
     // stays <= 2^8 and the O rescale below runs on a few blocks only; O / l and m + log2(l)
     // do not depend on where the max sits.
-    const float m_new = (bmax > m_run + 8.f) ? bmax : m_run;  // bmax is finite: a slot is valid
-    const float alpha = fast_exp2(m_run - m_new);
+    const float m_new = (bmax > m_run + MAXSTEP) ? bmax : m_run;  // bmax is finite: a slot is valid
+    const float alpha = fast_exp2((m_run - m_new) * EU);
     m_run = m_new;
 
     float psum = 0.f;
@@ -243,7 +250,7 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
     for (int mt = 0; mt < 2; mt++)
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        const float p = fast_exp2(sacc[mt][r] - m_new);
+        const float p = fast_exp2((sacc[mt][r] - m_new) * EU);
         psum += p;
         pb[mt][r >> 3][r & 7] = (__bf16)p;
       }
@@ -285,25 +292,31 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
         *(uint2*)(orow + d) = pack4_bf16(oacc[dt][4 * r4] * inv, oacc[dt][4 * r4 + 1] * inv,
                                          oacc[dt][4 * r4 + 2] * inv, oacc[dt][4 * r4 + 3] * inv);
       }
-    if (half == 0 && kg == 0) lse[token * H + head] = ltot > 0.f ? m_run + log2f(ltot) : -INFINITY;
+    if (half == 0 && kg == 0)
+      lse[token * H + head] = ltot > 0.f ? (RR ? (m_run + logf(ltot)) * kLog2e : m_run + log2f(ltot)) : -INFINITY;
   }
 }
 
-template <int D, int NHG>
+template <int D, int NHG, bool RR>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const int n_hblk = (int)((a.H + 32 * NHG - 1) / (32 * NHG));
   const int n_tokens = (int)(a.B * a.S);
   const dim3 grid((unsigned)(n_tokens * n_hblk)), block(NHG * 128);
-  hipLaunchKernelGGL((fwd_kernel<D, NHG>), grid, block, 0, st, (const uint16_t*)a.q, (const uint16_t*)a.kv,
+  hipLaunchKernelGGL((fwd_kernel<D, NHG, RR>), grid, block, 0, st, (const uint16_t*)a.q, (const uint16_t*)a.kv,
                      a.sink, a.idx, (uint16_t*)a.o, a.lse, (int)a.S, a.S_kv, (int)a.H, (int)a.topk,
-                     a.sm_scale * kLog2e, n_hblk, n_tokens);
+                     RR ? a.sm_scale : a.sm_scale * kLog2e, n_hblk, n_tokens);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
-  if (a.D == 512) return a.H <= 32 ? launch_fwd_t<512, 1>(a, st) : launch_fwd_t<512, 2>(a, st);
-  if (a.D == 64) return a.H <= 32 ? launch_fwd_t<64, 1>(a, st) : hipErrorInvalidValue;
+template <bool RR>
+static hipError_t launch_fwd_rr(const FwdArgs& a, hipStream_t st) {
+  if (a.D == 512) return a.H <= 32 ? launch_fwd_t<512, 1, RR>(a, st) : launch_fwd_t<512, 2, RR>(a, st);
+  if (a.D == 64) return a.H <= 32 ? launch_fwd_t<64, 1, RR>(a, st) : hipErrorInvalidValue;
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
+  return a.reference_rounding ? launch_fwd_rr<true>(a, st) : launch_fwd_rr<false>(a, st);
 }
 
 }  // namespace smqa

@@ -16,6 +16,7 @@ struct FwdArgs {
   float* lse;
   int64_t B, S, S_kv, H, D, topk;
   float sm_scale;
+  int reference_rounding;  // 1: fp32 scaled logits in natural units (fwd page option)
 };
 
 struct BwdMainArgs {
