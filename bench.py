@@ -60,13 +60,15 @@ def parse():
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write the HBM traffic summary from two rocprofv3 --pmc counter_collection.csv files")
     p.add_argument("--out", help="output file of --summarize-pmc")
+    p.add_argument("--serial", action="store_true",
+                   help="run every kernel on one stream (default: the dKV staging plan on a side stream)")
     return p.parse_args()
 
 
 class Step:
     """Preallocated buffers and the library calls of one fwd+bwd step (no allocation inside)."""
 
-    def __init__(self, smqa, w, x):
+    def __init__(self, smqa, w, x, overlap: bool = True):
         self.lib = smqa.load_library()
         self.w = w
         dev = torch.device("cuda:0")
@@ -85,6 +87,9 @@ class Step:
         self.ws_bytes = self.lib.sparse_mqa_bwd_workspace_bytes(B, S, S_kv, H, D, w.topk)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
         self.stream = torch.cuda.current_stream()
+        # The dKV staging plan (prepare) reads only topk_idxs, so it runs on a second stream (default
+        # priority) beside the forward, preprocess and dQ kernels; the partials wait for it.
+        self.side = torch.cuda.Stream(device=dev) if overlap else None
         self.events = []  # one {kernel: (start, end)} per timed step
         self.nan = float("nan")
 
@@ -93,31 +98,49 @@ class Step:
             raise RuntimeError(f"{name}: status {st} {self.lib.sparse_mqa_status_string(st).decode()}")
 
     def run(self, timed: bool):
-        w, L, h = self.w, self.lib, self.stream.cuda_stream
+        w, L = self.w, self.lib
         B, S, S_kv, H, D, K = w.B, w.S, w.S_kv, w.H, w.D, w.topk
         p = lambda t: t.data_ptr()  # noqa: E731
         calls = {
-            "fwd": lambda: L.sparse_mqa_fwd(p(self.q), p(self.kv), p(self.sink), p(self.idx), p(self.o),
+            "fwd": lambda h: L.sparse_mqa_fwd(p(self.q), p(self.kv), p(self.sink), p(self.idx), p(self.o),
                                             p(self.lse), B, S, S_kv, H, D, K, self.nan, 0, h),
-            "bwd_preprocess": lambda: L.sparse_mqa_bwd_preprocess(p(self.o), p(self.do), p(self.delta), B, S, H, D, h),
-            "bwd_dq": lambda: L.sparse_mqa_bwd_dq(p(self.q), p(self.kv), p(self.do), p(self.idx), p(self.lse),
+            "bwd_preprocess": lambda h: L.sparse_mqa_bwd_preprocess(p(self.o), p(self.do), p(self.delta), B, S, H, D, h),
+            "bwd_dq": lambda h: L.sparse_mqa_bwd_dq(p(self.q), p(self.kv), p(self.do), p(self.idx), p(self.lse),
                                                   p(self.delta), p(self.dq), B, S, S_kv, H, D, K, self.nan, h),
-            "bwd_dkv_prepare": lambda: L.sparse_mqa_bwd_dkv_prepare(p(self.idx), p(self.ws), self.ws_bytes,
+            "bwd_dkv_prepare": lambda h: L.sparse_mqa_bwd_dkv_prepare(p(self.idx), p(self.ws), self.ws_bytes,
                                                                     B, S, S_kv, H, D, K, h),
-            "bwd_dkv_partials": lambda: L.sparse_mqa_bwd_dkv_partials(
+            "bwd_dkv_partials": lambda h: L.sparse_mqa_bwd_dkv_partials(
                 p(self.q), p(self.kv), p(self.do), p(self.idx), p(self.lse), p(self.delta), p(self.ws),
                 self.ws_bytes, B, S, S_kv, H, D, K, self.nan, h),
-            "bwd_dkv_reduce": lambda: L.sparse_mqa_bwd_dkv_reduce(p(self.dkv), 0, p(self.ws), self.ws_bytes,
+            "bwd_dkv_reduce": lambda h: L.sparse_mqa_bwd_dkv_reduce(p(self.dkv), 0, p(self.ws), self.ws_bytes,
                                                                   B, S, S_kv, H, D, K, h),
         }
         ev = {}
-        for k in KERNELS:
+
+        def launch(k, st):
             if timed:
                 ev[k] = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                ev[k][0].record(self.stream)
-            self._check(k, calls[k]())
+                ev[k][0].record(st)
+            self._check(k, calls[k](st.cuda_stream))
             if timed:
-                ev[k][1].record(self.stream)
+                ev[k][1].record(st)
+
+        if self.side is None:
+            for k in KERNELS:
+                launch(k, self.stream)
+        else:
+            # prepare on the side stream once the previous step's dKV kernels are enqueued before it
+            go = torch.cuda.Event()
+            go.record(self.stream)
+            self.side.wait_event(go)
+            launch("bwd_dkv_prepare", self.side)
+            ready = torch.cuda.Event()
+            ready.record(self.side)
+            for k in ("fwd", "bwd_preprocess", "bwd_dq"):
+                launch(k, self.stream)
+            self.stream.wait_event(ready)
+            for k in ("bwd_dkv_partials", "bwd_dkv_reduce"):
+                launch(k, self.stream)
         if timed:
             self.events.append(ev)
 
@@ -266,7 +289,7 @@ def main():
     x = syn.workload_inputs(w)
     valid = ((x["topk_idxs"] >= 0) & (x["topk_idxs"] < w.S_kv)).sum(-1).view(-1)
     n_valid = int(valid.sum())
-    step = Step(smqa, w, x)
+    step = Step(smqa, w, x, overlap=not args.serial)
     if args.calibration_copy:
         src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
@@ -310,7 +333,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": dict(w.describe(), valid_pairs=n_valid, step="forward + backward"),
+        "config": dict(w.describe(), valid_pairs=n_valid, step="forward + backward",
+                       schedule="serial" if args.serial else "dkv prepare on a side stream"),
         "fwd_ms": round(ms_fwd, 4),
         "bwd_ms": round(ms_bwd, 4),
         "fwd_tflops": round(fl_fwd / (ms_fwd * 1e-3) / 1e12, 2),
