@@ -72,7 +72,8 @@ int sparse_mqa_fwd(const void* q, const void* kv, const float* attn_sink, const 
                    int64_t topk, float sm_scale, int reference_rounding, void* stream);
 
 /* Backward workspace. sparse_mqa_bwd and sparse_mqa_bwd_dkv take a device workspace: Delta
- * [B,S,H] fp32 (sparse_mqa_bwd only), per-row counters and offsets, and the staging rows of the
+ * [B,S,H] fp32 (sparse_mqa_bwd only), the kv row norms (which bound dS, so that dS can enter the
+ * dKV product as a scaled fp16 operand), per-row counters and offsets, and the staging rows of the
  * segmented dKV scatter-add (one row per valid (token, slot) pair and 64-head block, and one spare
  * row per token and head block that absorbs the stores of masked slots; a row is D fp16 values
  * with one power-of-two exponent per segment of up to 128 values, summed in fp32).
@@ -124,10 +125,13 @@ int sparse_mqa_bwd_dkv(const void* q, const void* kv, const void* d_o, const int
 /* The three steps of sparse_mqa_bwd_dkv for a single pass, for callers that schedule or time them
  * separately (bwd page, bwd factory: the dKV scatter-add). They need a workspace that holds every
  * token (at least sparse_mqa_bwd_workspace_bytes minus Delta's bytes; SMQA_ERR_WORKSPACE otherwise)
- * and must be enqueued in this order on one stream with the same workspace and sizes:
+ * and must run in this order with the same workspace and sizes:
  *   prepare   ranks each valid slot within its kv row and assigns its staging row;
  *   partials  computes every valid slot's dKV contribution row into the staging rows;
- *   reduce    sums each kv row's staging rows and writes dkv (bf16, or fp32 if dkv_fp32). */
+ *   reduce    sums each kv row's staging rows and writes dkv (bf16, or fp32 if dkv_fp32).
+ * prepare reads only topk_idxs, so it may run on another stream, e.g. beside the forward, as
+ * long as the caller orders it after the workspace's previous use and before partials (events);
+ * partials and reduce go on one stream. */
 int sparse_mqa_bwd_dkv_prepare(const int32_t* topk_idxs, void* workspace, size_t workspace_bytes,
                                int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk,
                                void* stream);

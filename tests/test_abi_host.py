@@ -82,7 +82,8 @@ def r256(n):
 def test_workspace_bytes(lib):
     B, S, S_kv, H, D, K = 1, 4096, 4096, 64, 512, 2048
     n_cnt = 16 * B * S_kv  # sixteen rank counters per kv row
-    fixed = r256((n_cnt + 4) * 4) + r256((n_cnt + 1) * 4) + r256(((n_cnt + 4095) // 4096) * 4)
+    row_norms = r256(B * S_kv * 4)  # |kv_r| per kv row
+    fixed = row_norms + r256((n_cnt + 4) * 4) + r256((n_cnt + 1) * 4) + r256(((n_cnt + 4095) // 4096) * 4)
     full = lib.sparse_mqa_bwd_workspace_bytes(B, S, S_kv, H, D, K)
     # staging: one row per slot plus one spare row per token (masked slots' stores land there); a
     # row is D fp16 values plus one int8 exponent per 128-value segment, in two planes

@@ -144,6 +144,42 @@ def test_edge_shapes_full(gpu_lib, case):
     torch.testing.assert_close(l0[1:].double(), x["attn_sink"][1:].double() / math.log(2), rtol=0, atol=1e-5)
 
 
+def test_operand_scales_and_row_norms(gpu_lib):
+    """Magnitudes away from 1 for the fp16 operands of the dKV product: q scaled by 1/128, one
+    referenced kv row 8x the others (it sets the dS bound of the tokens that reference it) and one
+    unreferenced row 1e5x (it must not change anything). Then dO scaled by 2^10: every gradient
+    is linear in dO and the kernels' scale exponents absorb a power of two, so dQ, Delta, d_sink and
+    dKV must scale by exactly 2^10 (bit for bit; dKV through its fp32 output)."""
+    g = torch.Generator().manual_seed(77)
+    B, S, S_kv, H, D, topk = 1, 8, 64, 64, 512, 32
+    kv = torch.randn(B, S_kv, D, generator=g)
+    kv[0, 5] *= 8.0
+    kv[0, S_kv - 1] *= 1e5
+    idx = torch.stack([torch.randperm(S_kv - 1, generator=g)[:topk] for _ in range(S)]).view(B, S, topk)
+    idx[0, :4, 0] = 5  # tokens 0..3 reference the large row (5 may then repeat, as allowed)
+    x = {
+        "q": (torch.randn(B, S, H, D, generator=g) / 128).to(torch.bfloat16),
+        "kv": kv.to(torch.bfloat16),
+        "attn_sink": torch.randn(H, generator=g),
+        "do": torch.randn(B, S, H, D, generator=g).to(torch.bfloat16),
+        "topk_idxs": idx.to(torch.int32),
+    }
+    say("case operand scales", dict(B=B, S=S, S_kv=S_kv, H=H, D=D, topk=topk))
+    o, lse = full_parity(x, tag="scales")
+    xg = gpu(x)
+    outs = []
+    for f in (1.0, 1024.0):
+        do = (xg["do"].float() * f).to(torch.bfloat16)
+        dq, dkv, ds = smqa.sparse_mqa_bwd_interface(xg["q"], xg["kv"], xg["attn_sink"], o, do, xg["topk_idxs"], lse,
+                                                    return_dkv_accum_dtype=True, return_d_sink=True)
+        torch.cuda.synchronize()
+        outs.append((dq.float(), dkv, ds))
+    (dq1, dkv1, ds1), (dq2, dkv2, ds2) = outs
+    assert torch.equal(dq2, dq1 * 1024) and torch.equal(ds2, ds1 * 1024)
+    # dKV sums staged rows in an order that may differ between calls: compare to fp32 rounding
+    torch.testing.assert_close(dkv2, dkv1 * 1024, rtol=1e-5, atol=1e-3)
+
+
 def test_explicit_scale_and_int64_indices(gpu_lib):
     w = syn.WORKLOADS["tiny_h16_d64"]
     x = syn.workload_inputs(w)

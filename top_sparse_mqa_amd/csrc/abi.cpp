@@ -111,7 +111,7 @@ int sparse_mqa_fwd(const void* q, const void* kv, const float* attn_sink, const 
 namespace {
 
 struct DkvPlan {
-  size_t count, offset, tiles, acc, pos, stage, stage_exp;  // byte offsets into the workspace
+  size_t kvn, count, offset, tiles, acc, pos, stage, stage_exp;  // byte offsets into the workspace
   int64_t chunk;                                  // tokens per chunk
   bool use_acc;                                   // a separate fp32 accumulator in the workspace
   size_t end;                                     // bytes used
@@ -119,7 +119,7 @@ struct DkvPlan {
 
 size_t fixed_dkv_bytes(int64_t B, int64_t S_kv) {
   const int64_t n_cnt = smqa::rank_counters(B * S_kv);
-  return round256((size_t)(n_cnt + 4) * 4) + round256((size_t)(n_cnt + 1) * 4) +
+  return round256((size_t)(B * S_kv) * 4) + round256((size_t)(n_cnt + 4) * 4) + round256((size_t)(n_cnt + 1) * 4) +
          round256((size_t)smqa::scan_tiles(n_cnt) * 4);
 }
 
@@ -137,6 +137,8 @@ bool plan_dkv(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t 
               size_t bytes, DkvPlan* p) {
   const int64_t n_rows = B * S_kv, tokens = B * S, n_cnt = smqa::rank_counters(n_rows);
   size_t o = base;
+  p->kvn = o;  // kv row norms
+  o += round256((size_t)n_rows * 4);
   p->count = o;
   o += round256((size_t)(n_cnt + 4) * 4);
   p->offset = o;
@@ -189,13 +191,15 @@ int run_dkv(const void* q, const void* kv, const void* d_o, const int32_t* idx, 
   uint16_t* stage = (uint16_t*)(ws + p.stage);
   int8_t* stage_exp = (int8_t*)(ws + p.stage_exp);
   float* acc = dkv_fp32 ? (float*)dkv : (p.use_acc ? (float*)(ws + p.acc) : nullptr);
+  float* kvn = (float*)(ws + p.kvn);
+  if (smqa::launch_kv_row_norm(kv, n_rows, D, kvn, st) != hipSuccess) return SMQA_ERR_HIP;
   for (int64_t t0 = 0; t0 < tokens; t0 += p.chunk) {
     const int64_t n = (tokens - t0) < p.chunk ? (tokens - t0) : p.chunk;
     if (smqa::launch_dkv_prepare(idx, count, offset, tiles, pos, B, S, S_kv, topk, smqa::bwd_hblocks(H), t0, n, st) !=
         hipSuccess)
       return SMQA_ERR_HIP;
-    smqa::BwdMainArgs a{q, kv, d_o, idx, lse, delta, nullptr, nullptr, pos, stage, stage_exp, B, S, S_kv, H, D,
-                        topk, scale, t0, n};
+    smqa::BwdMainArgs a{q, kv, d_o, idx, lse, delta, nullptr, nullptr, pos, stage, stage_exp, kvn, B, S, S_kv, H,
+                        D, topk, scale, t0, n};
     if (smqa::launch_bwd_main(a, 2, st) != hipSuccess) return SMQA_ERR_HIP;
     const bool last = t0 + n >= tokens;
     void* out16 = (!dkv_fp32 && last) ? dkv : nullptr;
@@ -277,8 +281,8 @@ int sparse_mqa_bwd_dq(const void* q, const void* kv, const void* d_o, const int3
                       {lse, count({B, S, H}) * 4}, {delta, count({B, S, H}) * 4}};
   for (const Span& s : ins)
     if (overlap(sdq, s)) return SMQA_ERR_ALIAS;
-  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, nullptr, nullptr, nullptr, nullptr, B, S, S_kv, H, D, topk,
-                      scale, 0, B * S};
+  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, nullptr, nullptr, nullptr, nullptr, nullptr, B, S, S_kv, H,
+                      D, topk, scale, 0, B * S};
   return smqa::launch_bwd_main(a, 1, (hipStream_t)stream) == hipSuccess ? SMQA_OK : SMQA_ERR_HIP;
 }
 
@@ -352,8 +356,10 @@ int sparse_mqa_bwd_dkv_partials(const void* q, const void* kv, const void* d_o, 
   for (const Span& s : ins)
     if (overlap(sws, s)) return SMQA_ERR_ALIAS;
   char* ws = (char*)workspace;
+  float* kvn = (float*)(ws + p.kvn);
+  if (smqa::launch_kv_row_norm(kv, B * S_kv, D, kvn, (hipStream_t)stream) != hipSuccess) return SMQA_ERR_HIP;
   smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, nullptr, nullptr, (const int32_t*)(ws + p.pos),
-                      (uint16_t*)(ws + p.stage), (int8_t*)(ws + p.stage_exp), B, S, S_kv, H, D, topk, scale, 0,
+                      (uint16_t*)(ws + p.stage), (int8_t*)(ws + p.stage_exp), kvn, B, S, S_kv, H, D, topk, scale, 0,
                       B * S};
   if (smqa::launch_bwd_main(a, 2, (hipStream_t)stream) != hipSuccess) return SMQA_ERR_HIP;
   return SMQA_OK;
@@ -393,8 +399,8 @@ int sparse_mqa_bwd_main(const void* q, const void* kv, const void* d_o, const in
   for (const Span& s : ins)
     if (overlap(sdq, s) || overlap(sacc, s)) return SMQA_ERR_ALIAS;
   if (overlap(sdq, sacc)) return SMQA_ERR_ALIAS;
-  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, dkv_accum, nullptr, nullptr, nullptr, B, S, S_kv, H, D, topk,
-                      scale, 0, B * S};
+  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, dkv_accum, nullptr, nullptr, nullptr, nullptr, B, S, S_kv,
+                      H, D, topk, scale, 0, B * S};
   return smqa::launch_bwd_main(a, 3, (hipStream_t)stream) == hipSuccess ? SMQA_OK : SMQA_ERR_HIP;
 }
 
@@ -439,8 +445,8 @@ int sparse_mqa_bwd(const void* q, const void* kv, const float* attn_sink, const 
   if ((st = run_dkv(q, kv, d_o, topk_idxs, lse, delta, dkv, dkv_fp32, (char*)workspace, p, B, S, S_kv, H, D, topk,
                     scale, hs)))
     return st;
-  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, nullptr, nullptr, nullptr, nullptr, B, S, S_kv, H, D, topk,
-                      scale, 0, B * S};
+  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, nullptr, nullptr, nullptr, nullptr, nullptr, B, S, S_kv, H,
+                      D, topk, scale, 0, B * S};
   return smqa::launch_bwd_main(a, 1, hs) == hipSuccess ? SMQA_OK : SMQA_ERR_HIP;
 }
 

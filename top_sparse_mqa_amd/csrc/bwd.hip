@@ -15,6 +15,8 @@
 // dQ and dKV run as two kernels: the per-token state both need (Q and dO in two layouts plus
 // the dQ accumulator) does not fit one workgroup's registers at H = 64, D = 512.
 // Both kernels gather a block of 32 slots into LDS with direct-to-LDS loads, double-buffered.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -95,6 +97,26 @@ dsink_kernel(const float* __restrict__ lse, const float* __restrict__ delta, con
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
   __syncthreads();
   if (threadIdx.x == 0) d_sink[h] = -((part[0] + part[1]) + (part[2] + part[3]));
+}
+
+// Row norms |kv_r| (fp32) of all B * S_kv rows; LPR lanes per row, 16 bytes each.
+template <int D>
+__global__ void __launch_bounds__(256)
+kv_row_norm_kernel(const uint16_t* __restrict__ kv, int64_t rows, float* __restrict__ norm) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;  // rows per workgroup pass
+  const int t = threadIdx.x;
+  for (int64_t r = (int64_t)blockIdx.x * RPB + t / LPR; r - t / LPR < rows; r += (int64_t)gridDim.x * RPB) {
+    float ss = 0.f;
+    if (r < rows) {
+      const bf16x8 v = load_bf16x8(kv + r * D + 8 * (t % LPR));
+#pragma unroll
+      for (int e = 0; e < 8; e++) ss += (float)v[e] * (float)v[e];
+    }
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) ss += __shfl_xor(ss, off);
+    if (r < rows && t % LPR == 0) norm[r] = sqrtf(ss);
+  }
 }
 
 __global__ void __launch_bounds__(256) fill_zero_kernel(float4* __restrict__ p, int64_t n4) {
@@ -367,8 +389,8 @@ __global__ void __launch_bounds__(NW * 64)
 bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ dout,
                const int32_t* __restrict__ idx, const float* __restrict__ lse, const float* __restrict__ delta,
                float* __restrict__ dkv_acc, const int32_t* __restrict__ pos, uint16_t* __restrict__ stage,
-               int8_t* __restrict__ stage_exp, int S, int64_t S_kv, int H, int topk, float sm_scale,
-               float scale_log2, int n_hblk, int token0, int n_tokens) {
+               int8_t* __restrict__ stage_exp, const float* __restrict__ row_norm, int S, int64_t S_kv, int H,
+               int topk, float sm_scale, float scale_log2, int n_hblk, int token0, int n_tokens) {
   using C = BwdCommon<D, NW>;
   using G = BwdGather<D, NW>;
   constexpr int T = C::T;
@@ -383,10 +405,12 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
   constexpr int SB = HB * T * 2;  // bytes of one [HB][T] bf16 buffer
   __shared__ __attribute__((aligned(16))) char tile0[C::TB];
   __shared__ __attribute__((aligned(16))) char tile1[C::TB];
-  // B operands of the dKV product, each [head][slot]: 0 = hi and 1 = lo bf16 parts of
-  // sm_scale * dS * 2^-so (lo = x - float(bf16(x)), rounded), 2 = P as fp16.
-  __shared__ __attribute__((aligned(16))) char pds[3 * SB];
-  __shared__ float red[NW];
+  // B operands of the dKV product, each [head][slot]. Staged: fp16 sm_scale * dS * 2^(sq - so),
+  // then fp16 P. Atomic (no kv_norm bound): the hi and lo bf16 parts of sm_scale * dS * 2^-so
+  // (lo = x - float(bf16(x)), rounded), then fp16 P.
+  constexpr int NB = STAGED ? 2 : 3;
+  __shared__ __attribute__((aligned(16))) char pds[NB * SB];
+  __shared__ float red[3][NW];
   // Staging-store transpose. The dKV^T accumulator gives each lane one slot row and runs of four
   // consecutive d; they go to this wave's [32 slots][SEGW d] fp16 buffer as 8-byte writes and come
   // back as 16-byte pieces of whole row segments, so one store instruction covers LPR * 16
@@ -425,16 +449,23 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
   // lane l holds d = w*DW + 32 dt + (l & 31) and heads 16 ks + 8 kg .. +7, read with transposing
   // LDS loads from a row-major [HB][D] staging copy held in the two tile buffers (heads
   // 0 .. HH-1 in tile0, the rest in tile1; the buffers are free at this point).
-  // P enters the product as fp16 (11 significant bits; bf16 P leaves errors of several percent on
-  // heavily shared rows), so dO does too, scaled by 2^-so with so chosen from this workgroup's
-  // max |dO|: every bf16 value within 2^28 of the max converts exactly, and the partner operand
-  // sm_scale * dS carries the same 2^-so. The staged rows carry 2^so in their exponents.
+  // P enters as fp16 (11 significant bits; bf16 P leaves errors of several percent on heavily
+  // shared rows), so dO does too, scaled by 2^-so with so from this workgroup's max |dO|: every
+  // bf16 value within 2^28 of the max converts exactly. Staged, Q is fp16 as well, scaled by 2^-sq
+  // from max |q|, and the dS operand is sm_scale * dS * 2^(sq - so) in fp16, so both products
+  // carry 2^-so, which the staged rows' exponents undo. so is raised where needed so that the dS
+  // operand stays inside the fp16 range: |sm_scale dS| <= sm_scale (|dP| + |Delta|) <= 2 sm_scale
+  // sqrt(D) max|dO| max_t |kv_t| (P <= 1, Cauchy-Schwarz, and |O| <= max_t |kv_t| as O is a
+  // convex combination of the token's kv rows), with max_t over the token's valid slots from the
+  // per-row norms in row_norm. The atomic variant has no row norms: Q stays bf16 and dS goes in as
+  // a hi + lo pair of bf16 (three MFMAs per k-step).
   constexpr int HH = C::TB / (D * 2);  // heads per tile buffer
   static_assert(HB <= 2 * HH && HH % 16 == 0, "staging copy must fit the tile buffers");
   constexpr int NPT = HB * D / 8 / (NW * 64);  // 16-byte pieces per thread
-  bf16x8 qv[NDT][KH];
+  using QV = std::conditional_t<STAGED, f16x8, bf16x8>;
+  QV qv[NDT][KH];
   f16x8 dov[NDT][KH];
-  int so = 0;
+  int so = 0, sqo = 0;  // dO scale exponent; dS operand exponent sq - so (staged)
   {
     const int64_t base = (token * H + (int64_t)hblk * HB) * D;
     auto piece = [&](int i) -> char* {  // staging-copy address of 16-byte piece i
@@ -453,34 +484,88 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
           put(dt, ks, join_tr(lds_load_tr(sb + (h0 * D + d) * 2), lds_load_tr(sb + ((h0 + 4) * D + d) * 2)));
         }
     };
+    uint4 rq[NPT], rd[NPT];
+    float mq = 0.f, md = 0.f, mv = 0.f;
+    if constexpr (STAGED) {  // largest norm among this token's referenced kv rows
+      const int32_t* it = idx + token * (int64_t)topk;
+      const float* nb = row_norm + b * S_kv;
+      constexpr int U = 8;  // independent index loads, then independent norm loads
+      for (int t0 = threadIdx.x; t0 < topk; t0 += U * NW * 64) {
+        int32_t v[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+          const int t = t0 + u * NW * 64;
+          v[u] = t < topk ? it[t] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++)
+          if (slot_in_range(v[u], S_kv)) mv = fmaxf(mv, nb[v[u]]);
+      }
+    }
 #pragma unroll
     for (int k = 0; k < NPT; k++) {
-      const int i = threadIdx.x + k * NW * 64;
-      *(uint4*)piece(i) = *(const uint4*)(q + base + 8 * i);
+      rq[k] = *(const uint4*)(q + base + 8 * (threadIdx.x + k * NW * 64));
+      rd[k] = *(const uint4*)(dout + base + 8 * (threadIdx.x + k * NW * 64));
+    }
+#pragma unroll
+    for (int k = 0; k < NPT; k++) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, rq[k]), c = __builtin_bit_cast(bf16x8, rd[k]);
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        mq = fmaxf(mq, fabsf((float)a[e]));
+        md = fmaxf(md, fabsf((float)c[e]));
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      mq = fmaxf(mq, __shfl_xor(mq, o));
+      md = fmaxf(md, __shfl_xor(md, o));
+      mv = fmaxf(mv, __shfl_xor(mv, o));
+    }
+    if (lane == 0) {
+      red[0][w] = mq;
+      red[1][w] = md;
+      red[2][w] = mv;
     }
     __syncthreads();
-    read_frags([&](int dt, int ks, bf16x8 v) { qv[dt][ks] = v; });
-    __syncthreads();
-    uint4 raw[NPT];
-    float mx = 0.f;
 #pragma unroll
-    for (int k = 0; k < NPT; k++) {
-      raw[k] = *(const uint4*)(dout + base + 8 * (threadIdx.x + k * NW * 64));
-      const bf16x8 v = __builtin_bit_cast(bf16x8, raw[k]);
-#pragma unroll
-      for (int e = 0; e < 8; e++) mx = fmaxf(mx, fabsf((float)v[e]));
+    for (int k = 0; k < NW; k++) {
+      mq = fmaxf(mq, red[0][k]);
+      md = fmaxf(md, red[1][k]);
+      mv = fmaxf(mv, red[2][k]);
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    if (lane == 0) red[w] = mx;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < NW; k++) mx = fmaxf(mx, red[k]);
-    // mx < 2^(e) with e = frexp exponent: scaled values stay below 2^15
-    if (mx > 0.f && mx <= 3.4028235e38f) so = __builtin_amdgcn_frexp_expf(mx) - 15;
+    // scaled maxima stay below 2^15
+    const int sq = (STAGED && mq > 0.f && mq <= 3.4028235e38f) ? __builtin_amdgcn_frexp_expf(mq) - 15 : 0;
+    if (md > 0.f && md <= 3.4028235e38f) {
+      so = __builtin_amdgcn_frexp_expf(md) - 15;
+      if constexpr (STAGED) {
+        const float bound = 2.f * sm_scale * sqrtf((float)D) * md * mv;
+        if (bound > 0.f && bound <= 3.4028235e38f) {
+          const int sd = __builtin_amdgcn_frexp_expf(bound) + sq - 15;
+          so = so > sd ? so : sd;
+        }
+      }
+      so = so < -100 ? -100 : (so > 100 ? 100 : so);
+    }
+    sqo = sq - so;
 #pragma unroll
     for (int k = 0; k < NPT; k++) {
-      const bf16x8 v = __builtin_bit_cast(bf16x8, raw[k]);
+      if constexpr (STAGED) {
+        const bf16x8 v = __builtin_bit_cast(bf16x8, rq[k]);
+        f16x8 hv;
+#pragma unroll
+        for (int e = 0; e < 8; e++) hv[e] = (_Float16)__builtin_amdgcn_ldexpf((float)v[e], -sq);
+        *(f16x8*)piece(threadIdx.x + k * NW * 64) = hv;
+      } else {
+        *(uint4*)piece(threadIdx.x + k * NW * 64) = rq[k];
+      }
+    }
+    __syncthreads();
+    read_frags([&](int dt, int ks, bf16x8 v) { qv[dt][ks] = __builtin_bit_cast(QV, v); });
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NPT; k++) {
+      const bf16x8 v = __builtin_bit_cast(bf16x8, rd[k]);
       f16x8 hv;
 #pragma unroll
       for (int e = 0; e < 8; e++) hv[e] = (_Float16)__builtin_amdgcn_ldexpf((float)v[e], -so);
@@ -618,24 +703,38 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
     const uint32_t vb = (uint32_t)(mask >> (4 * g));
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) {
-      float p[4], ds[4], dslr[4];
+      float p[4], ds[4];
 #pragma unroll
-      for (int r = 0; r < 4; r++) {
+      for (int r = 0; r < 4; r++)
         p[r] = ((vb >> (16 * mt + r)) & 1u) ? fast_exp2(sacc[mt][r] * scale_log2 - lse_h) : 0.f;
-        ds[r] = __builtin_amdgcn_ldexpf(sm_scale * p[r] * (dpacc[mt][r] - delta_h), -so);
-        dslr[r] = ds[r] - (float)(__bf16)ds[r];
-      }
       char* wp = pds + pw_off + 32 * mt;
-      *(uint2*)(wp) = pack4_bf16(ds[0], ds[1], ds[2], ds[3]);
-      *(uint2*)(wp + SB) = pack4_bf16(dslr[0], dslr[1], dslr[2], dslr[3]);
+      if constexpr (STAGED) {
+#pragma unroll
+        for (int r = 0; r < 4; r++)  // saturated to the fp16 range: only inputs outside the bound's assumptions reach it
+          ds[r] = __builtin_amdgcn_fmed3f(
+              __builtin_amdgcn_ldexpf(sm_scale * p[r] * (dpacc[mt][r] - delta_h), sqo), -65504.f, 65504.f);
+        const f16x2 d01 = __builtin_convertvector((f32x2){ds[0], ds[1]}, f16x2);
+        const f16x2 d23 = __builtin_convertvector((f32x2){ds[2], ds[3]}, f16x2);
+        *(uint2*)(wp) = make_uint2(__builtin_bit_cast(uint32_t, d01), __builtin_bit_cast(uint32_t, d23));
+      } else {
+        float dslr[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          ds[r] = __builtin_amdgcn_ldexpf(sm_scale * p[r] * (dpacc[mt][r] - delta_h), -so);
+          dslr[r] = ds[r] - (float)(__bf16)ds[r];
+        }
+        *(uint2*)(wp) = pack4_bf16(ds[0], ds[1], ds[2], ds[3]);
+        *(uint2*)(wp + SB) = pack4_bf16(dslr[0], dslr[1], dslr[2], dslr[3]);
+      }
       const f16x2 p01 = __builtin_convertvector((f32x2){p[0], p[1]}, f16x2);
       const f16x2 p23 = __builtin_convertvector((f32x2){p[2], p[3]}, f16x2);
-      *(uint2*)(wp + 2 * SB) = make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
+      *(uint2*)(wp + (NB - 1) * SB) = make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
     }
     lds_barrier();  // P/dS visible to all waves; the next tile's gather stays in flight
 
-    // 2^-so dKV^T[d, slot] for this wave's d-range, DG tiles of 32 d at a time:
-    //   Q^T dS_hi + Q^T dS_lo + (2^-so dO)^T P, k over the block's heads.
+    // 2^-so dKV^T[d, slot] for this wave's d-range, DG tiles of 32 d at a time, k over the block's
+    // heads: (2^-sq Q)^T (2^(sq-so) sm_scale dS) + (2^-so dO)^T P staged, and
+    // Q^T dS_hi + Q^T dS_lo + (2^-so dO)^T P atomic.
     // C layout: lane holds slot (lane & 31), d = w*DW + 32 dt + 8 (r >> 2) + 4 kg + (r & 3).
     // Masked slots store into this workgroup's spare row (after all staging rows of the chunk),
     // so the stores need no per-slot branches.
@@ -657,9 +756,9 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
       for (int i = 0; i < DG; i++)
 #pragma unroll
         for (int r = 0; r < 16; r++) c[i][r] = 0.f;
-      bf16x8 bcur[3], bnxt[3];
+      bf16x8 bcur[NB], bnxt[NB];
 #pragma unroll
-      for (int m = 0; m < 3; m++) bcur[m] = bfrag(0, m);
+      for (int m = 0; m < NB; m++) bcur[m] = bfrag(0, m);
       if constexpr (DEFER) {
         eread();
 #pragma unroll
@@ -670,7 +769,7 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
         __builtin_amdgcn_sched_barrier(0);
         if (ks + 1 < KH) {
 #pragma unroll
-          for (int m = 0; m < 3; m++) bnxt[m] = bfrag(ks + 1, m);
+          for (int m = 0; m < NB; m++) bnxt[m] = bfrag(ks + 1, m);
         }
         if constexpr (DEFER) {
           // the previous block's rows of this k-step, then the reads for the next one
@@ -681,16 +780,17 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
           for (int k = SPK * (ks + 1); k < SPK * (ks + 2); k++) dread(k);
         }
 #pragma unroll
-        for (int m = 0; m < 3; m++)
+        for (int m = 0; m < NB; m++)
 #pragma unroll
           for (int i = 0; i < DG; i++) {
             const int dt = dg * DG + i;
-            if (m < 2) c[i] = mfma32(qv[dt][ks], bcur[m], c[i]);
-            else c[i] = mfma32h(dov[dt][ks], __builtin_bit_cast(f16x8, bcur[m]), c[i]);
+            if (m == NB - 1) c[i] = mfma32h(dov[dt][ks], __builtin_bit_cast(f16x8, bcur[m]), c[i]);
+            else if constexpr (STAGED) c[i] = mfma32h(qv[dt][ks], __builtin_bit_cast(f16x8, bcur[m]), c[i]);
+            else c[i] = mfma32(qv[dt][ks], bcur[m], c[i]);
           }
         if (ks + 1 < KH) {
 #pragma unroll
-          for (int m = 0; m < 3; m++) bcur[m] = bnxt[m];
+          for (int m = 0; m < NB; m++) bcur[m] = bnxt[m];
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -962,6 +1062,20 @@ hipError_t launch_bwd_dsink(const float* lse, const float* delta, const float* s
   return hipGetLastError();
 }
 
+hipError_t launch_kv_row_norm(const void* kv, int64_t rows, int64_t D, float* norm, hipStream_t st) {
+  const int64_t per_block = 256 / (D / 8);
+  int64_t g = (rows + per_block - 1) / per_block;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  if (D == 512)
+    hipLaunchKernelGGL(kv_row_norm_kernel<512>, dim3((unsigned)g), dim3(256), 0, st, (const uint16_t*)kv, rows, norm);
+  else if (D == 64)
+    hipLaunchKernelGGL(kv_row_norm_kernel<64>, dim3((unsigned)g), dim3(256), 0, st, (const uint16_t*)kv, rows, norm);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t st) {
   const int64_t n4 = n / 4;
   int64_t blocks = (n4 + 255) / 256;
@@ -996,13 +1110,13 @@ static hipError_t launch_bwd_main_t(const BwdMainArgs& a, int which, hipStream_t
   if (a.stage)
     hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, true>), dim3((unsigned)(a.n_chunk * n_hblk)), dim3(NW * 64), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.kv, (const uint16_t*)a.d_o, a.idx, a.lse, a.delta,
-                       nullptr, a.pos, a.stage, a.stage_exp, (int)a.S, a.S_kv, (int)a.H, (int)a.topk, a.sm_scale,
-                       sl2, n_hblk, (int)a.token0, (int)a.n_chunk);
+                       nullptr, a.pos, a.stage, a.stage_exp, a.row_norm, (int)a.S, a.S_kv, (int)a.H, (int)a.topk,
+                       a.sm_scale, sl2, n_hblk, (int)a.token0, (int)a.n_chunk);
   else
     hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, false>), dim3((unsigned)(a.n_chunk * n_hblk)), dim3(NW * 64), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.kv, (const uint16_t*)a.d_o, a.idx, a.lse, a.delta,
-                       a.dkv_accum, nullptr, nullptr, nullptr, (int)a.S, a.S_kv, (int)a.H, (int)a.topk, a.sm_scale,
-                       sl2, n_hblk, (int)a.token0, (int)a.n_chunk);
+                       a.dkv_accum, nullptr, nullptr, nullptr, nullptr, (int)a.S, a.S_kv, (int)a.H, (int)a.topk,
+                       a.sm_scale, sl2, n_hblk, (int)a.token0, (int)a.n_chunk);
   return hipGetLastError();
 }
 

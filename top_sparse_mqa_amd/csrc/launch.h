@@ -31,6 +31,7 @@ struct BwdMainArgs {
   const int32_t* pos;     // staging mode: staging row of each slot of the chunk (-1 if masked)
   uint16_t* stage;        // staging mode: contribution rows (fp16); nullptr selects atomic mode
   int8_t* stage_exp;      // staging mode: one power-of-two exponent per row segment (stage_segments)
+  const float* row_norm;  // staging mode: |kv_r| of every kv row (launch_kv_row_norm)
   int64_t B, S, S_kv, H, D, topk;
   float sm_scale;
   int64_t token0;         // first token of the chunk (dKV kernel)
@@ -50,6 +51,8 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_preprocess(const void* o, const void* d_o, float* delta, int64_t rows, int64_t D,
                                  hipStream_t st);
 hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t st);
+// norm[r] = |kv_r| (fp32) for rows kv[0 .. rows) of D bf16.
+hipError_t launch_kv_row_norm(const void* kv, int64_t rows, int64_t D, float* norm, hipStream_t st);
 // d_sink[h] = -sum_t 2^(sink_h log2 e - lse[t,h]) * delta[t,h] over tokens t (one workgroup per head).
 hipError_t launch_bwd_dsink(const float* lse, const float* delta, const float* sink, float* d_sink, int64_t tokens,
                             int64_t H, hipStream_t st);
