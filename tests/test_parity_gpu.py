@@ -180,6 +180,21 @@ def test_operand_scales_and_row_norms(gpu_lib):
     torch.testing.assert_close(dkv2, dkv1 * 1024, rtol=1e-5, atol=1e-3)
 
 
+@pytest.mark.parametrize("scale", [-0.125, 0.0], ids=["negative", "zero"])
+def test_negative_and_zero_scale(gpu_lib, scale):
+    """sm_scale is any finite value: a negative one (the forward takes it as a positive scale of
+    -Q) and zero (every valid slot gets the same weight)."""
+    w = syn.WORKLOADS["tiny_h16_d64"]
+    say("case", w.describe(), "sm_scale", scale)
+    x = syn.workload_inputs(w)
+    o, lse = full_parity(x, scale=scale, tag=f"scale={scale}")
+    if scale == 0.0:
+        # P is uniform over the valid slots and the sink: LSE = log2(n_valid + e^sink)
+        n = valid_mask(x["topk_idxs"], w.S_kv).sum(-1).double().view(-1, 1)
+        expect = torch.log2(n + torch.exp(x["attn_sink"].double()).view(1, -1))
+        torch.testing.assert_close(lse.view(-1, w.H).double().cpu(), expect, rtol=0, atol=1e-5)
+
+
 def test_explicit_scale_and_int64_indices(gpu_lib):
     w = syn.WORKLOADS["tiny_h16_d64"]
     x = syn.workload_inputs(w)
