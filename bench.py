@@ -343,6 +343,7 @@ def main():
         "bwd_frac_mfma_peak": round(fl_bwd / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "step_frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "fwd_gather_GBps": round(n_valid * 2 * w.D / (ms_fwd * 1e-3) / 1e9, 1),
+        "fwd_gather_frac_hbm": round(n_valid * 2 * w.D / (ms_fwd * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "kernel_ms": {k: round(v, 4) for k, v in ms.items()},
         "wall_s_timed": round(wall, 3),
         "roofline": {
