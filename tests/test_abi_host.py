@@ -64,6 +64,10 @@ def test_fwd_validation(lib):
     assert fwd(lib, topk=-1) == SHAPE
     assert fwd(lib, S_kv=2 ** 31) == SHAPE
     assert fwd(lib, H=48) == UNSUP
+    assert fwd(lib, H=96) == UNSUP
+    assert fwd(lib, H=1088) == UNSUP
+    assert fwd(lib, H=256, o=A) == ALIAS  # a supported head count: validation reaches the alias check
+    assert fwd(lib, H=1024, S=2 ** 24) == SHAPE  # 2^24 tokens x 16 head blocks > 2^28 workgroups
     assert fwd(lib, D=128) == UNSUP
     assert fwd(lib, H=64, D=64) == UNSUP
     assert fwd(lib, q=A + 8) == ALIGN

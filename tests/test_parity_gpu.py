@@ -104,6 +104,8 @@ EDGE = [
     ("h16_d512_k1", 1, 7, 40, 16, 512, 1),
     ("h32_d64_k200_dups", 1, 11, 100, 32, 64, 200),
     ("h64_d512_k33", 1, 5, 33, 64, 512, 33),
+    ("h192_d512_k70", 1, 4, 90, 192, 512, 70),
+    ("h256_d512_k40", 2, 3, 50, 256, 512, 40),
 ]
 
 

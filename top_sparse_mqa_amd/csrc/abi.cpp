@@ -8,8 +8,10 @@
 
 namespace {
 
+// D = 512: H = 16 or 32 (one workgroup per token), or any multiple of 64 up to 1024 (H / 64
+// workgroups of 64 heads per token). D = 64: H = 16 or 32.
 bool supported(int64_t H, int64_t D) {
-  if (D == 512) return H == 16 || H == 32 || H == 64 || H == 128;
+  if (D == 512) return H == 16 || H == 32 || (H % 64 == 0 && H >= 64 && H <= 1024);
   if (D == 64) return H == 16 || H == 32;
   return false;
 }
@@ -43,7 +45,9 @@ int check_shapes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64
   if (B <= 0 || S <= 0 || S_kv <= 0 || H <= 0 || D <= 0 || topk <= 0) return SMQA_ERR_SHAPE;
   if (S_kv > INT32_MAX || topk > INT32_MAX / 2 || S > INT32_MAX) return SMQA_ERR_SHAPE;
   const int64_t tokens = count({B, S});
-  if (tokens < 0 || tokens > (int64_t)INT32_MAX / 8) return SMQA_ERR_SHAPE;
+  // workgroup counts (tokens x head blocks) stay below 2^28
+  int64_t wgs = 0;
+  if (tokens < 0 || !mul_ok(tokens, H > 64 ? H / 64 : 1, &wgs) || wgs > (int64_t)INT32_MAX / 8) return SMQA_ERR_SHAPE;
   if (count({B, S, H, D}) < 0 || count({B, S_kv, D}) < 0 || count({B, S, topk}) < 0) return SMQA_ERR_SHAPE;
   if (!supported(H, D)) return SMQA_ERR_UNSUPPORTED;
   return SMQA_OK;
