@@ -30,7 +30,8 @@
  *   q, O, dO, dQ : [B, S, H, D] bf16       kv, dKV  : [B, S_kv, D] bf16 (dKV fp32 if asked)
  *   attn_sink    : [H] fp32                topk_idxs: [B, S, topk] int32
  *   LSE, Delta   : [B, S, H] fp32          dKV accumulator: [B, S_kv, D] fp32
- * Supported (H, D): D = 512 with H in {16, 32} or any multiple of 64 up to 1024; D = 64 with H in {16, 32}.
+ * Supported (H, D): D in {128, 256, 512} with H in {16, 32} or any multiple of 64 up to 1024; D = 64 with H in
+ * {16, 32}.
  * 1 <= topk <= 2^30, S_kv <= 2^31 - 1, B*S*max(1, H/64) <= 2^28.
  * Pointers to bf16 tensors (q, kv, O, dO, dQ, dKV), the fp32 dKV accumulator and the workspace
  * must be 16-byte aligned; fp32 vectors (attn_sink, LSE, Delta) and topk_idxs 4-byte aligned.

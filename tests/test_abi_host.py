@@ -68,7 +68,9 @@ def test_fwd_validation(lib):
     assert fwd(lib, H=1088) == UNSUP
     assert fwd(lib, H=256, o=A) == ALIAS  # a supported head count: validation reaches the alias check
     assert fwd(lib, H=1024, S=2 ** 24) == SHAPE  # 2^24 tokens x 16 head blocks > 2^28 workgroups
-    assert fwd(lib, D=128) == UNSUP
+    assert fwd(lib, D=96) == UNSUP
+    assert fwd(lib, D=1024) == UNSUP
+    assert fwd(lib, H=64, D=128, o=A) == ALIAS  # D = 128 and 256 are supported
     assert fwd(lib, H=64, D=64) == UNSUP
     assert fwd(lib, q=A + 8) == ALIGN
     assert fwd(lib, idx=Dp + 2) == ALIGN

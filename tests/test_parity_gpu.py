@@ -106,6 +106,10 @@ EDGE = [
     ("h64_d512_k33", 1, 5, 33, 64, 512, 33),
     ("h192_d512_k70", 1, 4, 90, 192, 512, 70),
     ("h256_d512_k40", 2, 3, 50, 256, 512, 40),
+    ("h64_d256_k50", 1, 6, 80, 64, 256, 50),
+    ("h16_d256_k70", 2, 3, 90, 16, 256, 70),
+    ("h32_d128_k40", 1, 7, 60, 32, 128, 40),
+    ("h128_d128_k33", 1, 4, 40, 128, 128, 33),
 ]
 
 

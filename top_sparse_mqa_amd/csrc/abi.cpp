@@ -8,10 +8,10 @@
 
 namespace {
 
-// D = 512: H = 16 or 32 (one workgroup per token), or any multiple of 64 up to 1024 (H / 64
-// workgroups of 64 heads per token). D = 64: H = 16 or 32.
+// D = 128, 256 or 512: H = 16 or 32 (one workgroup per token), or any multiple of 64 up to 1024
+// (H / 64 workgroups of 64 heads per token). D = 64: H = 16 or 32.
 bool supported(int64_t H, int64_t D) {
-  if (D == 512) return H == 16 || H == 32 || (H % 64 == 0 && H >= 64 && H <= 1024);
+  if (D == 128 || D == 256 || D == 512) return H == 16 || H == 32 || (H % 64 == 0 && H >= 64 && H <= 1024);
   if (D == 64) return H == 16 || H == 32;
   return false;
 }
@@ -246,7 +246,7 @@ int sparse_mqa_bwd_preprocess(const void* o, const void* d_o, float* delta, int6
                               int64_t D, void* stream) {
   if (!o || !d_o || !delta) return SMQA_ERR_NULL;
   if (B <= 0 || S <= 0 || H <= 0 || D <= 0) return SMQA_ERR_SHAPE;
-  if (D != 64 && D != 512) return SMQA_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128 && D != 256 && D != 512) return SMQA_ERR_UNSUPPORTED;
   const int64_t rows = count({B, S, H});
   if (rows < 0 || count({B, S, H, D}) < 0) return SMQA_ERR_SHAPE;
   if (!aligned16(o) || !aligned16(d_o) || !aligned4(delta)) return SMQA_ERR_ALIGN;

@@ -1049,6 +1049,10 @@ hipError_t launch_bwd_preprocess(const void* o, const void* d_o, float* delta, i
   const dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(256);
   if (D == 512)
     hipLaunchKernelGGL(delta_kernel<512>, grid, block, 0, st, (const uint16_t*)o, (const uint16_t*)d_o, delta, rows);
+  else if (D == 256)
+    hipLaunchKernelGGL(delta_kernel<256>, grid, block, 0, st, (const uint16_t*)o, (const uint16_t*)d_o, delta, rows);
+  else if (D == 128)
+    hipLaunchKernelGGL(delta_kernel<128>, grid, block, 0, st, (const uint16_t*)o, (const uint16_t*)d_o, delta, rows);
   else if (D == 64)
     hipLaunchKernelGGL(delta_kernel<64>, grid, block, 0, st, (const uint16_t*)o, (const uint16_t*)d_o, delta, rows);
   else
@@ -1069,6 +1073,10 @@ hipError_t launch_kv_row_norm(const void* kv, int64_t rows, int64_t D, float* no
   if (g < 1) g = 1;
   if (D == 512)
     hipLaunchKernelGGL(kv_row_norm_kernel<512>, dim3((unsigned)g), dim3(256), 0, st, (const uint16_t*)kv, rows, norm);
+  else if (D == 256)
+    hipLaunchKernelGGL(kv_row_norm_kernel<256>, dim3((unsigned)g), dim3(256), 0, st, (const uint16_t*)kv, rows, norm);
+  else if (D == 128)
+    hipLaunchKernelGGL(kv_row_norm_kernel<128>, dim3((unsigned)g), dim3(256), 0, st, (const uint16_t*)kv, rows, norm);
   else if (D == 64)
     hipLaunchKernelGGL(kv_row_norm_kernel<64>, dim3((unsigned)g), dim3(256), 0, st, (const uint16_t*)kv, rows, norm);
   else
@@ -1126,6 +1134,14 @@ hipError_t launch_bwd_main(const BwdMainArgs& a, int which, hipStream_t st) {
     if (hb == 64) return launch_bwd_main_t<512, 4>(a, which, st);
     if (hb == 32) return launch_bwd_main_t<512, 2>(a, which, st);
     if (hb == 16) return launch_bwd_main_t<512, 1>(a, which, st);
+  } else if (a.D == 256) {
+    if (hb == 64) return launch_bwd_main_t<256, 4>(a, which, st);
+    if (hb == 32) return launch_bwd_main_t<256, 2>(a, which, st);
+    if (hb == 16) return launch_bwd_main_t<256, 1>(a, which, st);
+  } else if (a.D == 128) {
+    if (hb == 64) return launch_bwd_main_t<128, 4>(a, which, st);
+    if (hb == 32) return launch_bwd_main_t<128, 2>(a, which, st);
+    if (hb == 16) return launch_bwd_main_t<128, 1>(a, which, st);
   } else if (a.D == 64) {
     if (hb == 32) return launch_bwd_main_t<64, 2>(a, which, st);
     if (hb == 16) return launch_bwd_main_t<64, 1>(a, which, st);
@@ -1171,6 +1187,12 @@ hipError_t launch_reduce_rows(const uint16_t* stage, const int8_t* stage_exp, in
                               float* acc, void* out_bf16, int accumulate, int64_t n_rows, int64_t D, hipStream_t st) {
   if (D == 512)
     hipLaunchKernelGGL(reduce_rows_kernel<512>, dim3((unsigned)n_rows), dim3(256), 0, st, stage, stage_exp, nseg,
+                       offset, (f32x4*)acc, (uint4*)out_bf16, accumulate);
+  else if (D == 256)
+    hipLaunchKernelGGL(reduce_rows_kernel<256>, dim3((unsigned)n_rows), dim3(256), 0, st, stage, stage_exp, nseg,
+                       offset, (f32x4*)acc, (uint4*)out_bf16, accumulate);
+  else if (D == 128)
+    hipLaunchKernelGGL(reduce_rows_kernel<128>, dim3((unsigned)n_rows), dim3(256), 0, st, stage, stage_exp, nseg,
                        offset, (f32x4*)acc, (uint4*)out_bf16, accumulate);
   else if (D == 64)
     hipLaunchKernelGGL(reduce_rows_kernel<64>, dim3((unsigned)n_rows), dim3(256), 0, st, stage, stage_exp, nseg,

@@ -311,6 +311,8 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
 template <bool RR>
 static hipError_t launch_fwd_rr(const FwdArgs& a, hipStream_t st) {
   if (a.D == 512) return a.H <= 32 ? launch_fwd_t<512, 1, RR>(a, st) : launch_fwd_t<512, 2, RR>(a, st);
+  if (a.D == 256) return a.H <= 32 ? launch_fwd_t<256, 1, RR>(a, st) : launch_fwd_t<256, 2, RR>(a, st);
+  if (a.D == 128) return a.H <= 32 ? launch_fwd_t<128, 1, RR>(a, st) : launch_fwd_t<128, 2, RR>(a, st);
   if (a.D == 64) return a.H <= 32 ? launch_fwd_t<64, 1, RR>(a, st) : hipErrorInvalidValue;
   return hipErrorInvalidValue;
 }
