@@ -8,9 +8,10 @@
 //                and either a plain store of each valid row into its staging row (segmented
 //                scatter-add, below) or a fp32 atomic add into the accumulator. A kv row sums
 //                thousands of heavily cancelling terms, and 8-bit-mantissa coefficients leave
-//                errors of several percent of the result there: sm_scale*dS enters as a hi + lo
-//                bf16 pair (two MFMAs) and P as fp16, against dO converted to fp16 under a
-//                per-token power-of-two scale (one f16 MFMA).
+//                errors of several percent of the result there, so the products run on fp16
+//                operands (11 bits) under per-token power-of-two scales: staged, Q and dS as fp16
+//                (dS's scale bounded by the token's kv row norms, kv_row_norm); atomic, Q stays
+//                bf16 against a hi + lo bf16 pair of dS. P and dO enter as fp16 in both.
 //   postprocess  fp32 accumulator -> bf16 (round to nearest even)
 // dQ and dKV run as two kernels: the per-token state both need (Q and dO in two layouts plus
 // the dQ accumulator) does not fit one workgroup's registers at H = 64, D = 512.
