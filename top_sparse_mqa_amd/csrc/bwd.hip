@@ -880,33 +880,41 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
 // row's staging segment stays contiguous.
 constexpr int RANK_SUB = 16;
 
+// Workgroup unit u covers slots 256 (u % tpt) .. +255 of chunk token u / tpt (tpt = ceil(topk /
+// 256) units per token), so the token and batch come from one wave-uniform division per unit
+// rather than a 64-bit division per slot.
 __global__ void __launch_bounds__(256)
 rank_kernel(const int32_t* __restrict__ idx, int32_t* __restrict__ count, int32_t* __restrict__ rank,
-            int64_t token0, int64_t n_slots, int64_t S, int64_t S_kv, int topk, int n_hblk, int64_t n_rows) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_slots; i += (int64_t)gridDim.x * 256) {
-    const int64_t slot = token0 * topk + i;
-    const int32_t v = idx[slot];
+            int64_t token0, int64_t n_chunk, int64_t S, int64_t S_kv, int topk, int n_hblk, int64_t n_rows) {
+  const int64_t tpt = (topk + 255) / 256;
+  for (int64_t u = blockIdx.x; u < n_chunk * tpt; u += gridDim.x) {
+    const int64_t ct = u / tpt;
+    const int t = (int)(u - ct * tpt) * 256 + (int)threadIdx.x;
+    if (t >= topk) continue;
+    const int64_t token = token0 + ct;
+    const int32_t v = idx[token * topk + t];
     int32_t r = -1;
-    if (slot_in_range(v, S_kv)) {
-      const int64_t token = slot / topk;
-      const int64_t b = token / S;
-      r = atomicAdd(count + (token % RANK_SUB) * n_rows + b * S_kv + v, n_hblk);
-    }
-    rank[i] = r;
+    if (slot_in_range(v, S_kv))
+      r = atomicAdd(count + (token % RANK_SUB) * n_rows + (token / S) * S_kv + v, n_hblk);
+    rank[ct * topk + t] = r;
   }
 }
 
-// In place: rank[i] -> offset[(row, sub)] + rank[i] for valid slots (stays -1 otherwise).
+// In place: rank -> offset[(row, sub)] + rank for valid slots (stays -1 otherwise); units as in
+// rank_kernel.
 __global__ void __launch_bounds__(256)
 position_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ offset, int32_t* __restrict__ rank,
-                int64_t token0, int64_t n_slots, int64_t S, int64_t S_kv, int topk) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_slots; i += (int64_t)gridDim.x * 256) {
-    const int32_t r = rank[i];
+                int64_t token0, int64_t n_chunk, int64_t S, int64_t S_kv, int topk) {
+  const int64_t tpt = (topk + 255) / 256;
+  for (int64_t u = blockIdx.x; u < n_chunk * tpt; u += gridDim.x) {
+    const int64_t ct = u / tpt;
+    const int t = (int)(u - ct * tpt) * 256 + (int)threadIdx.x;
+    if (t >= topk) continue;
+    const int32_t r = rank[ct * topk + t];
     if (r < 0) continue;
-    const int64_t slot = token0 * topk + i;
-    const int64_t token = slot / topk;
-    const int64_t b = token / S;
-    rank[i] = offset[(b * S_kv + idx[slot]) * RANK_SUB + token % RANK_SUB] + r;
+    const int64_t token = token0 + ct;
+    rank[ct * topk + t] =
+        offset[((token / S) * S_kv + idx[token * topk + t]) * RANK_SUB + token % RANK_SUB] + r;
   }
 }
 
@@ -1164,10 +1172,10 @@ hipError_t launch_dkv_prepare(const int32_t* idx, int32_t* count, int32_t* offse
                               int64_t n_chunk, hipStream_t st) {
   const int64_t n_rows = B * S_kv;
   const int64_t n_cnt = n_rows * RANK_SUB;
-  const int64_t n_slots = n_chunk * topk;
   hipError_t e = launch_fill_zero_f32((float*)count, (n_cnt + 3) / 4 * 4, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rank_kernel, dim3(grid_for(n_slots, 256)), dim3(256), 0, st, idx, count, pos, token0, n_slots, S,
+  const int64_t n_units = n_chunk * ((topk + 255) / 256);
+  hipLaunchKernelGGL(rank_kernel, dim3(grid_for(n_units, 1)), dim3(256), 0, st, idx, count, pos, token0, n_chunk, S,
                      S_kv, (int)topk, n_hblk, n_rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t tiles = scan_tiles(n_cnt);
@@ -1179,8 +1187,8 @@ hipError_t launch_dkv_prepare(const int32_t* idx, int32_t* count, int32_t* offse
   hipLaunchKernelGGL(scan_add_kernel, dim3((unsigned)tiles), dim3(256), 0, st, offset, (const int32_t*)tile_sum,
                      n_cnt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(position_kernel, dim3(grid_for(n_slots, 256)), dim3(256), 0, st, idx, (const int32_t*)offset,
-                     pos, token0, n_slots, S, S_kv, (int)topk);
+  hipLaunchKernelGGL(position_kernel, dim3(grid_for(n_units, 1)), dim3(256), 0, st, idx, (const int32_t*)offset,
+                     pos, token0, n_chunk, S, S_kv, (int)topk);
   return hipGetLastError();
 }
 
