@@ -41,7 +41,7 @@ KERNELS = ("fwd", "bwd_preprocess", "bwd_dq", "bwd_dkv_prepare", "bwd_dkv_partia
 SINGLE = {
     "fwd": ("smqa::fwd_kernel", ("fwd.hip", "device_common.h"), 4),
     "bwd_dq": ("smqa::bwd_dq_kernel", ("bwd.hip", "device_common.h"), 6),
-    "bwd_dkv_partials": ("smqa::bwd_dkv_kernel", ("bwd.hip", "device_common.h"), 8),
+    "bwd_dkv_partials": ("smqa::bwd_dkv_", ("bwd.hip", "device_common.h"), 8),  # _ws_kernel at H=64 D=512
 }
 CALIB_BYTES = 1 << 30        # the calibration copy reads and writes this many bytes
 CALIB_KERNEL = "MulFunctor"  # part of the name of the kernel torch.mul(src, 1.0, out=dst) runs

@@ -12,6 +12,9 @@
 //                operands (11 bits) under per-token power-of-two scales: staged, Q and dS as fp16
 //                (dS's scale bounded by the token's kv row norms, kv_row_norm); atomic, Q stays
 //                bf16 against a hi + lo bf16 pair of dS. P and dO enter as fp16 in both.
+//   bwd_dkv_ws   the staged bwd_dkv at 64 heads per workgroup and D = 512, with specialised
+//                waves: score waves (gather, S^T, dP^T, P, dS) and product waves (dKV^T, staging
+//                stores) share each SIMD, one block apart
 //   postprocess  fp32 accumulator -> bf16 (round to nearest even)
 // dQ and dKV run as two kernels: the per-token state both need (Q and dO in two layouts plus
 // the dQ accumulator) does not fit one workgroup's registers at H = 64, D = 512.
@@ -868,6 +871,401 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
 }
 
 // ---------------------------------------------------------------------------------------------
+// Staged dKV with specialised waves: 2 NW waves per workgroup, two per SIMD. Score waves
+// (0 .. NW-1) gather the kv tiles and produce S^T, dP^T, P and dS of block j for 16 heads each, as
+// bwd_dkv_kernel does; product waves (NW .. 2NW-1) run the dKV^T product of block j - 1 for a
+// d-range of DW each and store its staging rows. Each SIMD holds one wave of each kind, so the
+// gather and store issue, the softmax and the transposes of one wave overlap the MFMAs of the
+// other (with one wave per SIMD they run one after another). Stage j ends with one workgroup
+// barrier that hands block j's P/dS buffer to the product waves; every wave passes the same number
+// of barriers whatever its role (five in the set-up, then nblk + 1 stages). Numerics and staging
+// format are those of bwd_dkv_kernel<D, NW, true>.
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 128)
+bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ dout,
+                  const int32_t* __restrict__ idx, const float* __restrict__ lse, const float* __restrict__ delta,
+                  const int32_t* __restrict__ pos, uint16_t* __restrict__ stage, int8_t* __restrict__ stage_exp,
+                  const float* __restrict__ row_norm, int S, int64_t S_kv, int H, int topk, float sm_scale,
+                  float scale_log2, int n_hblk, int token0, int n_tokens) {
+  using C = BwdCommon<D, NW>;
+  using G = BwdGather<D, NW>;
+  constexpr int T = C::T;
+  constexpr int PF = 6;
+  constexpr int NWT = 2 * NW;   // waves of the workgroup
+  constexpr int HB = 16 * NW;   // heads of this workgroup
+  constexpr int DW = D / NW;    // d-columns of dKV owned by one product wave
+  constexpr int NDT = DW / 32;  // its 32-wide d tiles, accumulated together
+  constexpr int KH = HB / 16;   // 16-head k-steps of the dKV product
+  constexpr int NFS = 2 * C::KS;
+  static_assert(NDT >= 1 && NDT <= 4, "one group of at most four 32-wide d tiles per product wave");
+  constexpr int SB = HB * T * 2;  // bytes of one [HB][T] fp16 buffer
+  __shared__ __attribute__((aligned(16))) char tile0[C::TB];
+  __shared__ __attribute__((aligned(16))) char tile1[C::TB];
+  // dS operand then P of a block, each [head][slot] fp16; block j goes through pds<j & 1>
+  __shared__ __attribute__((aligned(16))) char pds0[2 * SB];
+  __shared__ __attribute__((aligned(16))) char pds1[2 * SB];
+  __shared__ float red[3][NWT];
+  // staging-store transpose per product wave, as in bwd_dkv_kernel (one exponent segment = DW)
+  constexpr int SEGW = NDT * 32;
+  constexpr int NSEG = D / SEGW;
+  constexpr int OP = SEGW * 2;
+  __shared__ __attribute__((aligned(16))) char obuf[NW][T * OP];
+  constexpr int LPR = SEGW / 8, RPS = 64 / LPR, NI = T / RPS;
+  auto obuf_chunk = [](int row, int chunk) { return ((chunk ^ (row & (LPR - 1))) << 4); };
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int g = lane >> 4, kg = lane >> 5;
+  const int item = blockIdx.x;
+  const int64_t ctok = (int64_t)n_tokens - 1 - item / n_hblk;  // token within the chunk
+  const int64_t token = token0 + ctok;
+  const int hblk = item % n_hblk;
+  const int64_t b = token / S;
+  const int nblk = (topk + T - 1) / T;
+  const int32_t* idx_tok = idx + token * (int64_t)topk;
+  auto load_idx = [&](int blk) -> int32_t {
+    const int t = blk * T + lane;
+    return (lane < T && t < topk) ? idx_tok[t] : -1;
+  };
+
+  // (1) Per-token scales (all waves): Q as fp16 times 2^-sq, dO times 2^-so, the dS operand times
+  // 2^(sq - so), with sq, so from max |q|, max |dO| and the largest row norm among the token's
+  // valid slots, exactly as bwd_dkv_kernel derives them. Q and dO then pass through a row-major
+  // [HB][D] fp16 copy in the tile buffers, from which the product waves read them transposed.
+  constexpr int HH = C::TB / (D * 2);  // heads per tile buffer
+  static_assert(HB <= 2 * HH && HH % 16 == 0, "staging copy must fit the tile buffers");
+  constexpr int NPT = HB * D / 8 / (NWT * 64);  // 16-byte pieces per thread
+  static_assert(NPT >= 1 && NPT * NWT * 64 * 8 == HB * D, "whole pieces per thread");
+  auto piece = [&](int i) -> char* {
+    const int h = i / (D / 8);
+    return h < HH ? tile0 + 16 * i : tile1 + 16 * (i - HH * (D / 8));
+  };
+  uint4 rq[NPT], rd[NPT];
+  f16x8 hd[NPT];  // dO pieces as fp16 times 2^-so, written to the copy once Q has been read
+  int so = 0, sqo = 0;
+  {
+    const int64_t base = (token * H + (int64_t)hblk * HB) * D;
+    float mq = 0.f, md = 0.f, mv = 0.f;
+    const float* nb = row_norm + b * S_kv;
+    constexpr int U = 8;  // independent index loads, then independent norm loads
+    for (int t0 = threadIdx.x; t0 < topk; t0 += U * NWT * 64) {
+      int32_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int t = t0 + u * NWT * 64;
+        v[u] = t < topk ? idx_tok[t] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++)
+        if (slot_in_range(v[u], S_kv)) mv = fmaxf(mv, nb[v[u]]);
+    }
+#pragma unroll
+    for (int k = 0; k < NPT; k++) {
+      rq[k] = *(const uint4*)(q + base + 8 * (threadIdx.x + k * NWT * 64));
+      rd[k] = *(const uint4*)(dout + base + 8 * (threadIdx.x + k * NWT * 64));
+    }
+#pragma unroll
+    for (int k = 0; k < NPT; k++) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, rq[k]), c = __builtin_bit_cast(bf16x8, rd[k]);
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        mq = fmaxf(mq, fabsf((float)a[e]));
+        md = fmaxf(md, fabsf((float)c[e]));
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      mq = fmaxf(mq, __shfl_xor(mq, o));
+      md = fmaxf(md, __shfl_xor(md, o));
+      mv = fmaxf(mv, __shfl_xor(mv, o));
+    }
+    if (lane == 0) {
+      red[0][w] = mq;
+      red[1][w] = md;
+      red[2][w] = mv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NWT; k++) {
+      mq = fmaxf(mq, red[0][k]);
+      md = fmaxf(md, red[1][k]);
+      mv = fmaxf(mv, red[2][k]);
+    }
+    const int sq = (mq > 0.f && mq <= 3.4028235e38f) ? __builtin_amdgcn_frexp_expf(mq) - 15 : 0;
+    if (md > 0.f && md <= 3.4028235e38f) {
+      so = __builtin_amdgcn_frexp_expf(md) - 15;
+      const float bound = 2.f * sm_scale * sqrtf((float)D) * md * mv;
+      if (bound > 0.f && bound <= 3.4028235e38f) {
+        const int sd = __builtin_amdgcn_frexp_expf(bound) + sq - 15;
+        so = so > sd ? so : sd;
+      }
+      so = so < -100 ? -100 : (so > 100 ? 100 : so);
+    }
+    sqo = sq - so;
+#pragma unroll
+    for (int k = 0; k < NPT; k++) {
+      const bf16x8 v = __builtin_bit_cast(bf16x8, rq[k]), c = __builtin_bit_cast(bf16x8, rd[k]);
+      f16x8 hv;
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        hv[e] = (_Float16)__builtin_amdgcn_ldexpf((float)v[e], -sq);
+        hd[k][e] = (_Float16)__builtin_amdgcn_ldexpf((float)c[e], -so);
+      }
+      *(f16x8*)piece(threadIdx.x + k * NWT * 64) = hv;
+    }
+  }
+  __syncthreads();  // the Q copy is complete
+  auto put_dout = [&]() {
+#pragma unroll
+    for (int k = 0; k < NPT; k++) *(f16x8*)piece(threadIdx.x + k * NWT * 64) = hd[k];
+  };
+
+  if (wu < NW) {
+    // ---------------- score waves: wave wu owns heads 16 wu .. 16 wu + 15 ----------------
+    const int hrow = 16 * wu + (lane & 15);
+    const int head = hblk * HB + hrow;
+    bf16x8 qb[C::KS], dob[C::KS];
+    {
+      const int64_t off = (token * H + head) * (int64_t)D + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ks++) {
+        qb[ks] = load_bf16x8(q + off + 32 * ks);
+        dob[ks] = load_bf16x8(dout + off + 32 * ks);
+      }
+      // after all loads are issued: pinning waits for the value
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ks++) {
+        keep_in_agpr(qb[ks]);
+        keep_in_agpr(dob[ks]);
+      }
+    }
+    const float lse_h = lse[token * H + head];
+    const float delta_h = delta[token * H + head];
+    __syncthreads();  // the product waves have read Q
+    put_dout();
+    __syncthreads();  // the dO copy is complete
+    __syncthreads();  // the product waves have read dO: the tile buffers are free
+
+    int sc_off[C::KSJ];
+    bwd_score_offsets<D>(lane, sc_off);
+    const int pw_off = (hrow * T + 4 * g) * 2;  // P/dS writes: head hrow, slots 16 mt + 4 g .. +3
+    const G gather((const char*)(kv + b * S_kv * D), S_kv);
+    int32_t idx_cur = load_idx(0);
+    uint64_t mask_cur = __ballot(slot_in_range(idx_cur, S_kv));
+    if (mask_cur) gather.all(idx_cur, mask_cur, tile0, lane, wu);
+    int32_t idx_nxt = nblk > 1 ? load_idx(1) : -1;
+    wait_all_mem();
+    __syncthreads();  // tile 0 is complete
+
+    auto sblock = [&](auto buf_tag, int blk) {
+      constexpr int BUF = decltype(buf_tag)::value;
+      const char* tile = BUF ? tile1 : tile0;
+      char* other = BUF ? tile0 : tile1;
+      char* pw = (BUF ? pds1 : pds0) + pw_off;
+      if (blk < nblk) {
+        uint64_t mask_nxt = 0;
+        if (blk + 1 < nblk) mask_nxt = __ballot(slot_in_range(idx_nxt, S_kv));
+        const int32_t idx_g = idx_nxt;
+        idx_cur = idx_nxt;
+        idx_nxt = blk + 2 < nblk ? load_idx(blk + 2) : -1;
+        const uint64_t mask = mask_cur;
+        mask_cur = mask_nxt;
+        if (mask == 0) {
+          if (mask_nxt) gather.all(idx_g, mask_nxt, other, lane, wu);
+        } else {
+          // the next tile goes out in parts from inside the score loop; with no next block the parts
+          // read the zero row into the idle buffer, which nothing reads before the next wait
+          auto gather_hook = [&](int i) {
+#pragma unroll
+            for (int k = 0; k < G::NP; k++)
+              if (i == (k * NFS) / G::NP + NFS / G::NP / 2) gather.part(k, idx_g, mask_nxt, other, lane, wu);
+          };
+          f32x4 sacc[2], dpacc[2];
+          bwd_scores<D, PF>(tile, sc_off, qb, dob, sacc, dpacc, gather_hook);
+          const uint32_t vb = (uint32_t)(mask >> (4 * g));
+#pragma unroll
+          for (int mt = 0; mt < 2; mt++) {
+            float p[4], ds[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+              p[r] = ((vb >> (16 * mt + r)) & 1u) ? fast_exp2(sacc[mt][r] * scale_log2 - lse_h) : 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+              ds[r] = __builtin_amdgcn_fmed3f(
+                  __builtin_amdgcn_ldexpf(sm_scale * p[r] * (dpacc[mt][r] - delta_h), sqo), -65504.f, 65504.f);
+            const f16x2 d01 = __builtin_convertvector((f32x2){ds[0], ds[1]}, f16x2);
+            const f16x2 d23 = __builtin_convertvector((f32x2){ds[2], ds[3]}, f16x2);
+            const f16x2 p01 = __builtin_convertvector((f32x2){p[0], p[1]}, f16x2);
+            const f16x2 p23 = __builtin_convertvector((f32x2){p[2], p[3]}, f16x2);
+            *(uint2*)(pw + 32 * mt) = make_uint2(__builtin_bit_cast(uint32_t, d01), __builtin_bit_cast(uint32_t, d23));
+            *(uint2*)(pw + 32 * mt + SB) =
+                make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
+          }
+        }
+        wait_all_mem();  // this wave's part of tile blk + 1
+      }
+      lds_barrier();
+    };
+    for (int blk = 0; blk <= nblk; blk += 2) {
+      sblock(IntTag<0>{}, blk);
+      if (blk + 1 <= nblk) sblock(IntTag<1>{}, blk + 1);
+    }
+  } else {
+    // -------- product waves: wave NW + kw owns dKV columns kw DW .. kw DW + DW - 1 --------
+    const int kw = wu - NW;
+    // Q and dO with heads along k, as A operands of dKV^T: lane l holds d = kw DW + 32 dt + (l & 31)
+    // and heads 16 ks + 8 kg .. +7, read with transposing LDS loads from the row-major copy
+    f16x8 qv[NDT][KH], dov[NDT][KH];
+    auto read_frags = [&](f16x8 (&dst)[NDT][KH]) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+        for (int ks = 0; ks < KH; ks++) {
+          const int hb0 = 16 * ks;  // first head of the k-step: all 16 sit in one buffer
+          const char* sb = hb0 < HH ? tile0 : tile1;
+          const int h0 = hb0 % HH + 8 * kg + ((lane & 15) >> 2);
+          const int d = kw * DW + 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+          dst[dt][ks] = __builtin_bit_cast(
+              f16x8, join_tr(lds_load_tr(sb + (h0 * D + d) * 2), lds_load_tr(sb + ((h0 + 4) * D + d) * 2)));
+        }
+    };
+    read_frags(qv);
+#pragma unroll
+    for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+      for (int ks = 0; ks < KH; ks++) keep_in_agpr(qv[dt][ks]);
+    __syncthreads();  // all product waves have read Q
+    put_dout();
+    __syncthreads();  // the dO copy is complete
+    read_frags(dov);
+#pragma unroll
+    for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+      for (int ks = 0; ks < KH; ks++) keep_in_agpr(dov[dt][ks]);
+    __syncthreads();  // all product waves have read dO
+
+    const int32_t* pos_tok = pos + ctok * (int64_t)topk;
+    auto load_pos = [&](int blk) -> int32_t {
+      const int t = blk * T + lane;
+      return (lane < T && t < topk) ? pos_tok[t] : -1;
+    };
+    // masked slots of a partly valid block store into this workgroup's spare row (after all staging
+    // rows of the chunk), so the stores need no per-slot branches
+    const int32_t spare = (n_tokens * topk + (int32_t)ctok) * n_hblk + hblk;
+    int32_t idx_cur = load_idx(0), pos_cur = load_pos(0);
+    __syncthreads();  // tile 0 is complete (the score waves' set-up)
+
+    // A block's products go to c; finish() then writes them out (exponent, fp16 transpose, staging
+    // stores) before the stage ends. The stores thus share the vector memory path with the score
+    // waves' softmax rather than with their gathers; finishing each block at the top of the next
+    // stage instead (over the score waves' MFMAs and gathers) measured no faster, as that path
+    // bounds the kernel.
+    f32x16 c[NDT];
+    int32_t dst_c = 0;  // staging row of slot lane & 31 of the block in c (lanes < T)
+    auto finish = [&]() {
+      // per-lane addresses are derived here from an opaque copy of the lane id, so that the
+      // compiler does not hoist them out of the block loop and hold them in registers
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      // one exponent per slot row segment (this lane and lane ^ 32 hold the row's values)
+      float mx = 0.f;
+#pragma unroll
+      for (int i = 0; i < NDT; i++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) mx = fmaxf(mx, fabsf(c[i][r]));
+      const int e = stage_exponent(half_swap_max(mx));
+      int es = e + so;  // the stored exponent also undoes the dO scale
+      es = es < -127 ? -127 : (es > 127 ? 127 : es);
+      if (__ballot(e != 0)) {
+#pragma unroll
+        for (int i = 0; i < NDT; i++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) c[i][r] = __builtin_amdgcn_ldexpf(c[i][r], -e);
+      }
+      // fp16 runs of four d into this wave's transpose buffer (C layout: lane holds slot lane & 31,
+      // d = kw DW + 32 i + 8 (r >> 2) + 4 kg + (r & 3))
+      char* ob = obuf[kw] + (ln & 31) * OP + 8 * (ln >> 5);
+#pragma unroll
+      for (int i = 0; i < NDT; i++)
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const f16x2 a = __builtin_convertvector((f32x2){c[i][4 * jj], c[i][4 * jj + 1]}, f16x2);
+          const f16x2 b2 = __builtin_convertvector((f32x2){c[i][4 * jj + 2], c[i][4 * jj + 3]}, f16x2);
+          *(i32x2*)(ob + obuf_chunk(ln & 31, 4 * i + jj)) = i32x2{__builtin_bit_cast(int, a), __builtin_bit_cast(int, b2)};
+        }
+      // row read-back: lane covers d0 .. d0 + 7 of slot row n RPS + lane / LPR
+      const int d0 = kw * DW + 8 * (ln % LPR);
+#pragma unroll
+      for (int n = 0; n < NI; n++) {
+        const int row = n * RPS + ln / LPR;
+        const i32x4 v = *(const i32x4*)(obuf[kw] + row * OP + obuf_chunk(row, ln % LPR));
+        const int32_t rowi = __shfl(dst_c, row);
+        __builtin_nontemporal_store(v, (i32x4*)(stage + (int64_t)rowi * D + d0));
+      }
+      if (lane < T) stage_exp[(int64_t)dst_c * NSEG + kw] = (int8_t)es;
+    };
+    auto pblock = [&](auto buf_tag, int j) {
+      constexpr int BUF = decltype(buf_tag)::value;
+      if (j >= 1) {
+        const int blk = j - 1;
+        const int32_t idx_this = idx_cur, pos_this = pos_cur;
+        if (blk + 1 < nblk) {
+          idx_cur = load_idx(blk + 1);
+          pos_cur = load_pos(blk + 1);
+        }
+        const bool valid = slot_in_range(idx_this, S_kv);
+        const uint64_t mask = __ballot(valid);
+        if (mask) {
+          int ln = lane;
+          asm volatile("" : "+v"(ln));
+          // dKV^T B fragments: lane l gets slot (l & 31) and heads 16 ks + 8 kg .. +7, two
+          // transposing reads 4 heads apart; block j - 1 went through pds<(j - 1) & 1>
+          const char* pr = (BUF ? pds0 : pds1) +
+                           ((8 * (ln >> 5) + ((ln & 15) >> 2)) * T + 16 * ((ln >> 4) & 1) + 4 * (ln & 3)) * 2;
+          dst_c = valid ? pos_this + hblk : spare;
+          auto bfrag = [&](int ks, int m) {
+            const char* p = pr + m * SB + ks * 16 * T * 2;
+            return __builtin_bit_cast(f16x8, join_tr(lds_load_tr(p), lds_load_tr(p + 4 * T * 2)));
+          };
+          // 2^-so dKV^T[d, slot] = (2^-sq Q)^T (2^(sq-so) sm_scale dS) + (2^-so dO)^T P
+#pragma unroll
+          for (int i = 0; i < NDT; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) c[i][r] = 0.f;
+          f16x8 bcur[2], bnxt[2];
+          bcur[0] = bfrag(0, 0);
+          bcur[1] = bfrag(0, 1);
+#pragma unroll
+          for (int ks = 0; ks < KH; ks++) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + 1 < KH) {
+              bnxt[0] = bfrag(ks + 1, 0);
+              bnxt[1] = bfrag(ks + 1, 1);
+            }
+#pragma unroll
+            for (int i = 0; i < NDT; i++) c[i] = mfma32h(qv[i][ks], bcur[0], c[i]);
+#pragma unroll
+            for (int i = 0; i < NDT; i++) c[i] = mfma32h(dov[i][ks], bcur[1], c[i]);
+            if (ks + 1 < KH) {
+              bcur[0] = bnxt[0];
+              bcur[1] = bnxt[1];
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          finish();
+        }
+      }
+      lds_barrier();
+    };
+    for (int j = 0; j <= nblk; j += 2) {
+      pblock(IntTag<0>{}, j);
+      if (j + 1 <= nblk) pblock(IntTag<1>{}, j + 1);
+    }
+  }
+  wait_all_mem();
+}
+
+// ---------------------------------------------------------------------------------------------
 // Segmented scatter-add of dKV. Every valid (token, slot) pair gets n_hblk consecutive rows of a
 // staging buffer, grouped by kv row: rank (per-row counter, int atomics) -> exclusive scan of the
 // counts (row offsets) -> pos = offset + rank. The dKV kernel stores each contribution row there
@@ -1124,16 +1522,24 @@ static hipError_t launch_bwd_main_t(const BwdMainArgs& a, int which, hipStream_t
     if (e != hipSuccess) return e;
   }
   if (!(which & 2)) return hipSuccess;
-  if (a.stage)
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, true>), dim3((unsigned)(a.n_chunk * n_hblk)), dim3(NW * 64), 0, st,
-                       (const uint16_t*)a.q, (const uint16_t*)a.kv, (const uint16_t*)a.d_o, a.idx, a.lse, a.delta,
-                       nullptr, a.pos, a.stage, a.stage_exp, a.row_norm, (int)a.S, a.S_kv, (int)a.H, (int)a.topk,
-                       a.sm_scale, sl2, n_hblk, (int)a.token0, (int)a.n_chunk);
-  else
+  if (a.stage) {
+    // 64 heads at D = 512: the specialised-wave kernel (eight waves, two per SIMD)
+    if constexpr (NW == 4 && D == 512)
+      hipLaunchKernelGGL((bwd_dkv_ws_kernel<D, NW>), dim3((unsigned)(a.n_chunk * n_hblk)), dim3(NW * 128), 0, st,
+                         (const uint16_t*)a.q, (const uint16_t*)a.kv, (const uint16_t*)a.d_o, a.idx, a.lse, a.delta,
+                         a.pos, a.stage, a.stage_exp, a.row_norm, (int)a.S, a.S_kv, (int)a.H, (int)a.topk, a.sm_scale,
+                         sl2, n_hblk, (int)a.token0, (int)a.n_chunk);
+    else
+      hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, true>), dim3((unsigned)(a.n_chunk * n_hblk)), dim3(NW * 64), 0, st,
+                         (const uint16_t*)a.q, (const uint16_t*)a.kv, (const uint16_t*)a.d_o, a.idx, a.lse, a.delta,
+                         nullptr, a.pos, a.stage, a.stage_exp, a.row_norm, (int)a.S, a.S_kv, (int)a.H, (int)a.topk,
+                         a.sm_scale, sl2, n_hblk, (int)a.token0, (int)a.n_chunk);
+  } else {
     hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, false>), dim3((unsigned)(a.n_chunk * n_hblk)), dim3(NW * 64), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.kv, (const uint16_t*)a.d_o, a.idx, a.lse, a.delta,
                        a.dkv_accum, nullptr, nullptr, nullptr, nullptr, (int)a.S, a.S_kv, (int)a.H, (int)a.topk,
                        a.sm_scale, sl2, n_hblk, (int)a.token0, (int)a.n_chunk);
+  }
   return hipGetLastError();
 }
 
