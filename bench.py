@@ -3,8 +3,8 @@
 
 One step = one pass of the whole path over one batch of seeded synthetic input: the forward
 (O, LSE), then the backward on those outputs (Delta preprocess, dQ kernel, and the dKV stage:
-row ranking and scan, the dKV kernel writing each pair's contribution row, and the per-row
-reduction that also emits the bf16 dKV). Inputs are resident in HBM before timing starts.
+the staging plan (selection bitmap, scan, positions), the dKV kernel writing each pair's
+contribution row, and the per-row reduction that also emits the bf16 dKV). Inputs are resident in HBM before timing starts.
 
 Prints one JSON line. `value` is the step's algorithmic TFLOP/s: (4 + 10) * H * D flops per valid
 (token, slot) pair (forward 4HD: QK^T and PV; backward 10HD: score recompute, dP, dQ, dKV) divided

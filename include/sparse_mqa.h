@@ -74,7 +74,8 @@ int sparse_mqa_fwd(const void* q, const void* kv, const float* attn_sink, const 
 
 /* Backward workspace. sparse_mqa_bwd and sparse_mqa_bwd_dkv take a device workspace: Delta
  * [B,S,H] fp32 (sparse_mqa_bwd only), the kv row norms (which bound dS, so that dS can enter the
- * dKV product as a scaled fp16 operand), per-row counters and offsets, and the staging rows of the
+ * dKV product as a scaled fp16 operand), the staging plan (one bit per kv row and token of a
+ * chunk, with pair counts and scanned offsets), and the staging rows of the
  * segmented dKV scatter-add (one row per valid (token, slot) pair and 64-head block, and one spare
  * row per token and head block that absorbs the stores of masked slots; a row is D fp16 values
  * with one power-of-two exponent per segment of up to 128 values, summed in fp32).
@@ -91,7 +92,9 @@ size_t sparse_mqa_bwd_workspace_min_bytes(int64_t B, int64_t S, int64_t S_kv, in
  * bf16 postprocess). dq [B,S,H,D] bf16. dkv [B,S_kv,D]: bf16 if dkv_fp32 == 0, else fp32 (the
  * fp32 sums themselves). The call overwrites dq and dkv; it never accumulates into them. Rows no
  * valid slot references come out exactly 0. attn_sink is accepted for the documented signature;
- * the LSE already includes the sink, so dQ and dKV do not read it. */
+ * the LSE already includes the sink, so dQ and dKV do not read it. Results are bitwise
+ * reproducible from call to call as long as no token lists a kv row twice (top-k selections never
+ * do): nothing in the staged path depends on the order in which workgroups run. */
 int sparse_mqa_bwd(const void* q, const void* kv, const float* attn_sink, const void* o,
                    const void* d_o, const int32_t* topk_idxs, const float* lse, void* dq, void* dkv,
                    int dkv_fp32, void* workspace, size_t workspace_bytes, int64_t B, int64_t S,
@@ -127,7 +130,8 @@ int sparse_mqa_bwd_dkv(const void* q, const void* kv, const void* d_o, const int
  * separately (bwd page, bwd factory: the dKV scatter-add). They need a workspace that holds every
  * token (at least sparse_mqa_bwd_workspace_bytes minus Delta's bytes; SMQA_ERR_WORKSPACE otherwise)
  * and must run in this order with the same workspace and sizes:
- *   prepare   ranks each valid slot within its kv row and assigns its staging row;
+ *   prepare   marks every valid (token, kv row) pair in a bitmap and gives each valid slot its
+ *             staging row: a kv row's rows are contiguous and ordered by token;
  *   partials  computes every valid slot's dKV contribution row into the staging rows;
  *   reduce    sums each kv row's staging rows and writes dkv (bf16, or fp32 if dkv_fp32).
  * prepare reads only topk_idxs, so it may run on another stream, e.g. beside the forward, as

@@ -85,22 +85,36 @@ def r256(n):
     return (n + 255) // 256 * 256
 
 
+def dkv_layout_bytes(B, S_kv, H, D, K, chunk, acc):
+    """The dKV workspace layout restated: kv row norms, the selection bitmap (one bit per kv row and
+    chunk token, in 32-bit words) with a pair count and a cursor per word (cleared together as whole
+    16-byte pieces), the scanned offsets (+ total),
+    the scan's tile sums, the fp32 accumulator when chunked with bf16 output, the slots' positions,
+    and the staging rows (one per slot and 64-head block plus one spare per token and head block; a
+    row is D fp16 values and one int8 exponent per segment of min(128, D / (heads per workgroup /
+    16)) values)."""
+    n_rows = B * S_kv
+    words = n_rows * ((chunk + 31) // 32)
+    hb = max(1, H // 64)
+    seg = min(128, D // (min(H, 64) // 16))
+    rows = chunk * (K + 1) * hb
+    return (r256(n_rows * 4) + r256((3 * words + 4) * 4) + r256((words + 1) * 4) + r256(((words + 4095) // 4096) * 4)
+            + (r256(n_rows * D * 4) if acc else 0) + r256(chunk * K * 4) + r256(rows * D * 2)
+            + r256(rows * (D // seg)))
+
+
 def test_workspace_bytes(lib):
     B, S, S_kv, H, D, K = 1, 4096, 4096, 64, 512, 2048
-    n_cnt = 16 * B * S_kv  # sixteen rank counters per kv row
-    row_norms = r256(B * S_kv * 4)  # |kv_r| per kv row
-    fixed = row_norms + r256((n_cnt + 4) * 4) + r256((n_cnt + 1) * 4) + r256(((n_cnt + 4095) // 4096) * 4)
     full = lib.sparse_mqa_bwd_workspace_bytes(B, S, S_kv, H, D, K)
-    # staging: one row per slot plus one spare row per token (masked slots' stores land there); a
-    # row is D fp16 values plus one int8 exponent per 128-value segment, in two planes
-    def stage(rows):
-        return r256(rows * D * 2) + r256(rows * (D // 128))
-    assert full == r256(B * S * H * 4) + fixed + r256(B * S * K * 4) + stage(B * S * (K + 1)) + 512
+    assert full == r256(B * S * H * 4) + dkv_layout_bytes(B, S_kv, H, D, K, B * S, False)
+    # at the headline shape the bitmap and offsets are 2 MiB each; the staging rows dominate
+    assert dkv_layout_bytes(B, S_kv, H, D, K, B * S, False) > 6.4e9
     low = lib.sparse_mqa_bwd_workspace_min_bytes(B, S, S_kv, H, D, K)
-    assert low == r256(B * S * H * 4) + fixed + r256(B * S_kv * D * 4) + r256(K * 4) + stage(K + 1) + 512
+    assert low == r256(B * S * H * 4) + dkv_layout_bytes(B, S_kv, H, D, K, 1, True)
     # H = 128 runs two 64-head workgroups per token: two staging rows per slot (and two spare rows)
-    assert (lib.sparse_mqa_bwd_workspace_bytes(1, 8, 16, 128, 512, 4)
-            - lib.sparse_mqa_bwd_workspace_bytes(1, 8, 16, 64, 512, 4)) == stage(8 * 5 * 2) - stage(8 * 5) + r256(8 * 128 * 4) - r256(8 * 64 * 4)
+    for (b, s_, skv, h, d, k) in ((1, 8, 16, 128, 512, 4), (2, 40, 33, 16, 64, 7), (1, 100, 70, 192, 256, 9)):
+        assert lib.sparse_mqa_bwd_workspace_bytes(b, s_, skv, h, d, k) == (
+            r256(b * s_ * h * 4) + dkv_layout_bytes(b, skv, h, d, k, b * s_, False))
     assert lib.sparse_mqa_bwd_workspace_bytes(0, 1, 1, 16, 64, 1) == 0
     assert lib.sparse_mqa_bwd_workspace_min_bytes(1, 1, 1, 48, 512, 1) == 0
 

@@ -41,8 +41,6 @@ def test_graph_capture_replay(gpu_lib):
         torch.cuda.synchronize()
         o, lse, dq, dkv = outs
         assert torch.equal(o, o0) and torch.equal(lse, lse0), f"replay {rep}: forward differs"
-        assert torch.equal(dq, dq0), f"replay {rep}: dQ differs"
-        # dKV sums staged rows in an order that may differ between runs
-        torch.testing.assert_close(dkv, dkv0, rtol=1e-5, atol=1e-5)
+        assert torch.equal(dq, dq0) and torch.equal(dkv, dkv0), f"replay {rep}: backward differs"
         junk.mul_(1.0001).add_(0.5)  # unrelated eager work between replays
         torch.cuda.synchronize()

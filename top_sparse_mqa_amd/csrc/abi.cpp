@@ -109,72 +109,70 @@ int sparse_mqa_fwd(const void* q, const void* kv, const float* attn_sink, const 
 }  // extern "C"
 
 // ---------------------------------------------------------------------------------------------
-// Backward workspace: [Delta (full bwd only)] [count] [offset] [scan tiles] [acc (multi-chunk, bf16
-// output only)] [pos: chunk*topk int32] [staging: chunk*topk*n_hblk rows of D fp32].
+// Backward workspace: [Delta (full bwd only)] [kv row norms] [selection bitmap, pair counts,
+// cursors] [offsets] [scan tiles] [acc (multi-chunk, bf16 output only)] [pos: chunk*topk int32]
+// [staging rows: chunk*(topk+1)*n_hblk rows of D fp16] [their exponents]. The bitmap part and the
+// offsets scale with the chunk (one bit per kv row and chunk token).
 
 namespace {
 
 struct DkvPlan {
-  size_t kvn, count, offset, tiles, acc, pos, stage, stage_exp;  // byte offsets into the workspace
-  int64_t chunk;                                  // tokens per chunk
-  bool use_acc;                                   // a separate fp32 accumulator in the workspace
-  size_t end;                                     // bytes used
+  size_t kvn, bits, offset, tiles, acc, pos, stage, stage_exp;  // byte offsets into the workspace
+  int64_t chunk;                                               // tokens per chunk
+  bool use_acc;                                                // a separate fp32 accumulator in the workspace
+  size_t end;                                                  // bytes used
 };
 
-size_t fixed_dkv_bytes(int64_t B, int64_t S_kv) {
-  const int64_t n_cnt = smqa::rank_counters(B * S_kv);
-  return round256((size_t)(B * S_kv) * 4) + round256((size_t)(n_cnt + 4) * 4) + round256((size_t)(n_cnt + 1) * 4) +
-         round256((size_t)smqa::scan_tiles(n_cnt) * 4);
-}
-
-// Bytes of one staging row: D fp16 values and one int8 exponent per segment.
-size_t stage_row_bytes(int64_t H, int64_t D) { return (size_t)D * 2 + (size_t)smqa::stage_segments(H, D); }
-// Per token: its slots' positions, one staging row per slot and head block, and one spare row per
-// head block that takes the stores of the token's masked slots.
-size_t per_token_dkv_bytes(int64_t H, int64_t D, int64_t topk) {
-  return (size_t)topk * 4 + (size_t)(topk + 1) * smqa::bwd_hblocks(H) * stage_row_bytes(H, D);
-}
-
-// Lay out the dKV part of the workspace starting at `base`; false if `bytes` cannot hold even one
-// token's staging.
-bool plan_dkv(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, bool dkv_fp32, size_t base,
-              size_t bytes, DkvPlan* p) {
-  const int64_t n_rows = B * S_kv, tokens = B * S, n_cnt = smqa::rank_counters(n_rows);
+// Lay out the dKV part of the workspace from `base` for token chunks of `chunk` tokens; returns the
+// end offset.
+size_t dkv_layout(int64_t B, int64_t S_kv, int64_t H, int64_t D, int64_t topk, int64_t chunk, bool use_acc,
+                  size_t base, DkvPlan* p) {
+  const int64_t n_rows = B * S_kv, words = smqa::dkv_bitmap_words(n_rows, chunk);
   size_t o = base;
   p->kvn = o;  // kv row norms
   o += round256((size_t)n_rows * 4);
-  p->count = o;
-  o += round256((size_t)(n_cnt + 4) * 4);
+  p->bits = o;  // selection bitmap, pair counts and cursors, cleared as whole 16-byte pieces
+  o += round256((size_t)(3 * words + 4) * 4);
   p->offset = o;
-  o += round256((size_t)(n_cnt + 1) * 4);
+  o += round256((size_t)(words + 1) * 4);
   p->tiles = o;
-  o += round256((size_t)smqa::scan_tiles(n_cnt) * 4);
-  const size_t per_tok = per_token_dkv_bytes(H, D, topk);
-  // staging row indices are 32-bit
-  const int64_t max_chunk = (int64_t)(INT32_MAX / ((topk + 1) * smqa::bwd_hblocks(H)));
-  // one pass over all tokens if it fits, else token chunks with an fp32 running sum
-  if (o + per_tok * tokens + 512 <= bytes && tokens <= max_chunk) {
-    p->chunk = tokens;
-    p->use_acc = false;
-    p->acc = 0;
-  } else {
-    p->use_acc = !dkv_fp32;
-    p->acc = o;
-    if (p->use_acc) o += round256((size_t)n_rows * D * 4);
-    if (o + per_tok + 512 > bytes) return false;
-    p->chunk = (int64_t)((bytes - o - 512) / per_tok);
-    if (p->chunk > tokens) p->chunk = tokens;
-    if (p->chunk > max_chunk) p->chunk = max_chunk;
-  }
+  o += round256((size_t)smqa::scan_tiles(words) * 4);
+  p->use_acc = use_acc;
+  p->acc = use_acc ? o : 0;
+  if (use_acc) o += round256((size_t)n_rows * D * 4);
   p->pos = o;
-  o += round256((size_t)p->chunk * topk * 4);
-  const size_t rows = (size_t)p->chunk * (topk + 1) * smqa::bwd_hblocks(H);
+  o += round256((size_t)chunk * topk * 4);
+  // one staging row per slot and head block, and one spare row per token and head block that takes
+  // the stores of the token's masked slots
+  const size_t rows = (size_t)chunk * (topk + 1) * smqa::bwd_hblocks(H);
   p->stage = o;
   o += round256(rows * D * 2);
   p->stage_exp = o;
   o += round256(rows * smqa::stage_segments(H, D));
+  p->chunk = chunk;
   p->end = o;
-  return o <= bytes;
+  return o;
+}
+
+// Lay out the dKV part of the workspace starting at `base`: one pass over all tokens if it fits,
+// else the largest token chunk that fits, with an fp32 running sum; false if `bytes` cannot hold
+// even one token's staging.
+bool plan_dkv(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, bool dkv_fp32, size_t base,
+              size_t bytes, DkvPlan* p) {
+  const int64_t tokens = B * S;
+  // staging row indices are 32-bit
+  const int64_t max_chunk = (int64_t)(INT32_MAX / ((topk + 1) * smqa::bwd_hblocks(H)));
+  if (tokens <= max_chunk && dkv_layout(B, S_kv, H, D, topk, tokens, false, base, p) <= bytes) return true;
+  const bool use_acc = !dkv_fp32;
+  if (dkv_layout(B, S_kv, H, D, topk, 1, use_acc, base, p) > bytes) return false;
+  int64_t lo = 1, hi = tokens < max_chunk ? tokens : max_chunk;
+  while (lo < hi) {  // the largest chunk that fits (the layout grows with the chunk)
+    const int64_t mid = lo + (hi - lo + 1) / 2;
+    if (dkv_layout(B, S_kv, H, D, topk, mid, use_acc, base, p) <= bytes) lo = mid;
+    else hi = mid - 1;
+  }
+  dkv_layout(B, S_kv, H, D, topk, lo, use_acc, base, p);
+  return true;
 }
 
 size_t delta_bytes(int64_t B, int64_t S, int64_t H) { return round256((size_t)(B * S * H) * 4); }
@@ -188,7 +186,7 @@ int run_dkv(const void* q, const void* kv, const void* d_o, const int32_t* idx, 
             void* dkv, int dkv_fp32, char* ws, const DkvPlan& p, int64_t B, int64_t S, int64_t S_kv, int64_t H,
             int64_t D, int64_t topk, float scale, hipStream_t st) {
   const int64_t tokens = B * S, n_rows = B * S_kv;
-  int32_t* count = (int32_t*)(ws + p.count);
+  uint32_t* bits = (uint32_t*)(ws + p.bits);
   int32_t* offset = (int32_t*)(ws + p.offset);
   int32_t* tiles = (int32_t*)(ws + p.tiles);
   int32_t* pos = (int32_t*)(ws + p.pos);
@@ -199,7 +197,7 @@ int run_dkv(const void* q, const void* kv, const void* d_o, const int32_t* idx, 
   if (smqa::launch_kv_row_norm(kv, n_rows, D, kvn, st) != hipSuccess) return SMQA_ERR_HIP;
   for (int64_t t0 = 0; t0 < tokens; t0 += p.chunk) {
     const int64_t n = (tokens - t0) < p.chunk ? (tokens - t0) : p.chunk;
-    if (smqa::launch_dkv_prepare(idx, count, offset, tiles, pos, B, S, S_kv, topk, smqa::bwd_hblocks(H), t0, n, st) !=
+    if (smqa::launch_dkv_prepare(idx, bits, offset, tiles, pos, B, S, S_kv, topk, smqa::bwd_hblocks(H), t0, n, st) !=
         hipSuccess)
       return SMQA_ERR_HIP;
     smqa::BwdMainArgs a{q, kv, d_o, idx, lse, delta, nullptr, nullptr, pos, stage, stage_exp, kvn, B, S, S_kv, H,
@@ -207,8 +205,9 @@ int run_dkv(const void* q, const void* kv, const void* d_o, const int32_t* idx, 
     if (smqa::launch_bwd_main(a, 2, st) != hipSuccess) return SMQA_ERR_HIP;
     const bool last = t0 + n >= tokens;
     void* out16 = (!dkv_fp32 && last) ? dkv : nullptr;
-    if (smqa::launch_reduce_rows(stage, stage_exp, smqa::stage_segments(H, D), offset, acc, out16, t0 > 0 ? 1 : 0,
-                                 n_rows, D, st) != hipSuccess)
+    if (smqa::launch_reduce_rows(stage, stage_exp, smqa::stage_segments(H, D), offset,
+                                 smqa::dkv_bitmap_words(1, n), acc, out16, t0 > 0 ? 1 : 0, n_rows, D,
+                                 st) != hipSuccess)
       return SMQA_ERR_HIP;
   }
   return SMQA_OK;
@@ -230,16 +229,14 @@ extern "C" {
 
 size_t sparse_mqa_bwd_workspace_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk) {
   if (!sizes_ok(B, S, S_kv, H, D, topk)) return 0;
-  return delta_bytes(B, S, H) + fixed_dkv_bytes(B, S_kv) + round256((size_t)(B * S) * topk * 4) +
-         round256((size_t)(B * S) * (topk + 1) * smqa::bwd_hblocks(H) * D * 2) +
-         round256((size_t)(B * S) * (topk + 1) * smqa::bwd_hblocks(H) * smqa::stage_segments(H, D)) + 512;
+  DkvPlan p;
+  return delta_bytes(B, S, H) + dkv_layout(B, S_kv, H, D, topk, B * S, false, 0, &p);
 }
 
 size_t sparse_mqa_bwd_workspace_min_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk) {
   if (!sizes_ok(B, S, S_kv, H, D, topk)) return 0;
-  return delta_bytes(B, S, H) + fixed_dkv_bytes(B, S_kv) + round256((size_t)(B * S_kv) * D * 4) +
-         round256((size_t)topk * 4) + round256((size_t)(topk + 1) * smqa::bwd_hblocks(H) * D * 2) +
-         round256((size_t)(topk + 1) * smqa::bwd_hblocks(H) * smqa::stage_segments(H, D)) + 512;
+  DkvPlan p;
+  return delta_bytes(B, S, H) + dkv_layout(B, S_kv, H, D, topk, 1, true, 0, &p);
 }
 
 int sparse_mqa_bwd_preprocess(const void* o, const void* d_o, float* delta, int64_t B, int64_t S, int64_t H,
@@ -335,7 +332,7 @@ int sparse_mqa_bwd_dkv_prepare(const int32_t* topk_idxs, void* workspace, size_t
   if ((st = single_pass_plan(workspace, workspace_bytes, B, S, S_kv, H, D, topk, 0, &p))) return st;
   if (overlap(Span{workspace, (int64_t)p.end}, Span{topk_idxs, count({B, S, topk}) * 4})) return SMQA_ERR_ALIAS;
   char* ws = (char*)workspace;
-  if (smqa::launch_dkv_prepare(topk_idxs, (int32_t*)(ws + p.count), (int32_t*)(ws + p.offset),
+  if (smqa::launch_dkv_prepare(topk_idxs, (uint32_t*)(ws + p.bits), (int32_t*)(ws + p.offset),
                                (int32_t*)(ws + p.tiles), (int32_t*)(ws + p.pos), B, S, S_kv, topk,
                                smqa::bwd_hblocks(H), 0, B * S, (hipStream_t)stream) != hipSuccess)
     return SMQA_ERR_HIP;
@@ -382,7 +379,8 @@ int sparse_mqa_bwd_dkv_reduce(void* dkv, int dkv_fp32, void* workspace, size_t w
   char* ws = (char*)workspace;
   if (smqa::launch_reduce_rows((const uint16_t*)(ws + p.stage), (const int8_t*)(ws + p.stage_exp),
                                smqa::stage_segments(H, D), (const int32_t*)(ws + p.offset),
-                               dkv_fp32 ? (float*)dkv : nullptr, dkv_fp32 ? nullptr : dkv, 0, B * S_kv, D,
+                               smqa::dkv_bitmap_words(1, B * S), dkv_fp32 ? (float*)dkv : nullptr,
+                               dkv_fp32 ? nullptr : dkv, 0, B * S_kv, D,
                                (hipStream_t)stream) != hipSuccess)
     return SMQA_ERR_HIP;
   return SMQA_OK;

@@ -1267,23 +1267,68 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 
 // ---------------------------------------------------------------------------------------------
 // Segmented scatter-add of dKV. Every valid (token, slot) pair gets n_hblk consecutive rows of a
-// staging buffer, grouped by kv row: rank (per-row counter, int atomics) -> exclusive scan of the
-// counts (row offsets) -> pos = offset + rank. The dKV kernel stores each contribution row there
-// with plain stores, and reduce_rows sums each kv row's segment. This moves the payload through
-// the store and streaming-read paths instead of the fp32 atomic units.
+// staging buffer, grouped by kv row and, within a row, ordered by token. The dKV kernel stores each
+// contribution row there with plain stores, and reduce_rows sums each kv row's segment in that
+// order. This moves the payload through the store and streaming-read paths instead of the fp32
+// atomic units, and the result does not depend on the order in which workgroups run.
+//
+// The plan takes no global atomics on the common path. For a chunk of n_chunk tokens, kv row `row`
+// has nw = ceil(n_chunk / 32) words of a selection bitmap, and chunk token ct owns bit ct / nw of
+// word ct % nw; a set bit records that the token selects the row. Next to each word sits the count
+// of its pairs (bc[e] = {bits, count}, e = row * nw + word). An exclusive scan of n_hblk * count over
+// the words in (row, word) order gives each word the staging row of its first pair. In a word whose
+// count equals its popcount (each of its tokens selects the row once, as top-k selections do), a
+// pair's staging row is that plus n_hblk times the word's pairs below its bit: positions then
+// depend on the indices only, and row r's segment is [offset[r nw], offset[(r + 1) nw]). A word with
+// duplicate (token, row) pairs hands out its range [offset[e], offset[e + 1]) through an atomic
+// cursor cur[e] instead.
 
-// Each kv row has RANK_SUB counters (picked by token), stored sub-major so that the counters of
-// one row sit on different cache lines: a causal workload sends thousands of increments to its
-// first rows, and same-address atomics serialise. Offsets are scanned in (row, sub) order, so a
-// row's staging segment stays contiguous.
-constexpr int RANK_SUB = 16;
+// One workgroup per (word column w0, tile of MARK_ROWS kv rows): the 32 tokens w0 + nw j of the
+// column own every word of the column, so the workgroup builds the tile's words in LDS (LDS
+// atomics) and writes them out with plain stores.
+constexpr int MARK_ROWS = 8192;
 
-// Workgroup unit u covers slots 256 (u % tpt) .. +255 of chunk token u / tpt (tpt = ceil(topk /
-// 256) units per token), so the token and batch come from one wave-uniform division per unit
-// rather than a 64-bit division per slot.
 __global__ void __launch_bounds__(256)
-rank_kernel(const int32_t* __restrict__ idx, int32_t* __restrict__ count, int32_t* __restrict__ rank,
-            int64_t token0, int64_t n_chunk, int64_t S, int64_t S_kv, int topk, int n_hblk, int64_t n_rows) {
+mark_kernel(const int32_t* __restrict__ idx, int2* __restrict__ bc, int64_t token0, int64_t n_chunk, int64_t S,
+            int64_t S_kv, int topk, int64_t nw, int64_t n_rows) {
+  __shared__ uint32_t lb[MARK_ROWS];
+  __shared__ int32_t lc[MARK_ROWS];
+  const int64_t w0 = blockIdx.x % nw;
+  const int64_t r0 = (int64_t)(blockIdx.x / nw) * MARK_ROWS;
+  const int nr = (int)(n_rows - r0 < MARK_ROWS ? n_rows - r0 : MARK_ROWS);
+  for (int r = threadIdx.x; r < nr; r += 256) {
+    lb[r] = 0u;
+    lc[r] = 0;
+  }
+  __syncthreads();
+  for (int j = 0; j < 32; j++) {
+    const int64_t ct = w0 + nw * j;
+    if (ct >= n_chunk) break;
+    const int64_t token = token0 + ct;
+    const int32_t* it = idx + token * topk;
+    const int64_t rb = (token / S) * S_kv - r0;  // this token's batch rows, relative to the tile
+    for (int t = threadIdx.x; t < topk; t += 256) {
+      const int32_t v = it[t];
+      if (slot_in_range(v, S_kv)) {
+        const int64_t r = rb + v;
+        if (r >= 0 && r < nr) {
+          atomicOr(lb + r, 1u << j);
+          atomicAdd(lc + r, 1);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < nr; r += 256) bc[(r0 + r) * nw + w0] = make_int2((int)lb[r], lc[r]);
+}
+
+// pos[ct, slot] = the slot's first staging row, or -1 for a masked slot. Workgroup unit u covers
+// slots 256 (u % tpt) .. +255 of chunk token u / tpt (tpt = ceil(topk / 256) units per token), so
+// the token and batch come from one wave-uniform division per unit.
+__global__ void __launch_bounds__(256)
+position_kernel(const int32_t* __restrict__ idx, const int2* __restrict__ bc, int32_t* __restrict__ cur,
+                const int32_t* __restrict__ offset, int32_t* __restrict__ pos, int64_t token0, int64_t n_chunk,
+                int64_t S, int64_t S_kv, int topk, int64_t nw, int n_hblk) {
   const int64_t tpt = (topk + 255) / 256;
   for (int64_t u = blockIdx.x; u < n_chunk * tpt; u += gridDim.x) {
     const int64_t ct = u / tpt;
@@ -1292,27 +1337,13 @@ rank_kernel(const int32_t* __restrict__ idx, int32_t* __restrict__ count, int32_
     const int64_t token = token0 + ct;
     const int32_t v = idx[token * topk + t];
     int32_t r = -1;
-    if (slot_in_range(v, S_kv))
-      r = atomicAdd(count + (token % RANK_SUB) * n_rows + (token / S) * S_kv + v, n_hblk);
-    rank[ct * topk + t] = r;
-  }
-}
-
-// In place: rank -> offset[(row, sub)] + rank for valid slots (stays -1 otherwise); units as in
-// rank_kernel.
-__global__ void __launch_bounds__(256)
-position_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ offset, int32_t* __restrict__ rank,
-                int64_t token0, int64_t n_chunk, int64_t S, int64_t S_kv, int topk) {
-  const int64_t tpt = (topk + 255) / 256;
-  for (int64_t u = blockIdx.x; u < n_chunk * tpt; u += gridDim.x) {
-    const int64_t ct = u / tpt;
-    const int t = (int)(u - ct * tpt) * 256 + (int)threadIdx.x;
-    if (t >= topk) continue;
-    const int32_t r = rank[ct * topk + t];
-    if (r < 0) continue;
-    const int64_t token = token0 + ct;
-    rank[ct * topk + t] =
-        offset[((token / S) * S_kv + idx[token * topk + t]) * RANK_SUB + token % RANK_SUB] + r;
+    if (slot_in_range(v, S_kv)) {
+      const int64_t e = ((token / S) * S_kv + v) * nw + ct % nw;
+      const int2 w = bc[e];
+      if (w.y == __popc((uint32_t)w.x)) r = offset[e] + n_hblk * __popc((uint32_t)w.x & ((1u << (ct / nw)) - 1u));
+      else r = offset[e] + atomicAdd(cur + e, n_hblk);  // a word with duplicate pairs
+    }
+    pos[ct * topk + t] = r;
   }
 }
 
@@ -1338,10 +1369,10 @@ __device__ __forceinline__ int32_t block_exclusive_scan_256(int32_t v, int32_t* 
   return base + x - v;
 }
 
-// Element e = row * RANK_SUB + sub of the scan reads count[sub * n_rows + row].
+// Scan input: element e is n_hblk times word e's pair count, the staging rows of its pairs.
 __global__ void __launch_bounds__(256)
-scan_tiles_kernel(const int32_t* __restrict__ in, int32_t* __restrict__ out, int32_t* __restrict__ tile_sum,
-                  int64_t n, int64_t n_rows) {
+scan_tiles_kernel(const int2* __restrict__ bc, int32_t* __restrict__ out, int32_t* __restrict__ tile_sum,
+                  int64_t n, int n_hblk) {
   __shared__ int32_t sh[4];
   const int64_t base = (int64_t)blockIdx.x * SCAN_TILE + threadIdx.x * 16;
   int32_t v[16];
@@ -1349,7 +1380,7 @@ scan_tiles_kernel(const int32_t* __restrict__ in, int32_t* __restrict__ out, int
 #pragma unroll
   for (int i = 0; i < 16; i++) {
     const int64_t e = base + i;
-    v[i] = e < n ? in[(e % RANK_SUB) * n_rows + e / RANK_SUB] : 0;
+    v[i] = e < n ? n_hblk * bc[e].y : 0;
     s += v[i];
   }
   int32_t total;
@@ -1392,9 +1423,9 @@ scan_add_kernel(int32_t* __restrict__ out, const int32_t* __restrict__ tile_sum,
 template <int D>
 __global__ void __launch_bounds__(256)
 reduce_rows_kernel(const uint16_t* __restrict__ stage, const int8_t* __restrict__ stage_exp, int nseg,
-                   const int32_t* __restrict__ offset, f32x4* __restrict__ acc, uint4* __restrict__ out_bf16,
-                   int accumulate) {
-  // offset is indexed by (row, sub): the row's segment is [offset[row*RANK_SUB], offset[(row+1)*RANK_SUB]).
+                   const int32_t* __restrict__ offset, int64_t stride, f32x4* __restrict__ acc,
+                   uint4* __restrict__ out_bf16, int accumulate) {
+  // the row's segment is [offset[row * stride], offset[(row + 1) * stride])
   // Thread c of a group takes values 8c .. 8c+7 of every NG-th staging row of the segment.
   constexpr int F8 = D / 8;         // 16-byte pieces of fp16 per row
   constexpr int NG = 256 / F8;      // thread groups
@@ -1402,7 +1433,7 @@ reduce_rows_kernel(const uint16_t* __restrict__ stage, const int8_t* __restrict_
   __shared__ f32x4 part[NG][F8][2];
   const int64_t row = blockIdx.x;
   const int g = threadIdx.x / F8, c = threadIdx.x % F8;
-  const int32_t beg = offset[row * RANK_SUB], end = offset[(row + 1) * RANK_SUB];
+  const int32_t beg = offset[row * stride], end = offset[(row + 1) * stride];
   f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
   auto add = [&](const i32x4& raw, int e) {
     const f16x8 h = __builtin_bit_cast(f16x8, raw);
@@ -1571,47 +1602,51 @@ static unsigned grid_for(int64_t n, int64_t per_block, int64_t cap = 65536) {
 }
 
 int64_t scan_tiles(int64_t n) { return (n + SCAN_TILE - 1) / SCAN_TILE; }
-int64_t rank_counters(int64_t n_rows) { return n_rows * RANK_SUB; }
+int64_t dkv_bitmap_words(int64_t n_rows, int64_t n_chunk) { return n_rows * ((n_chunk + 31) / 32); }
 
-hipError_t launch_dkv_prepare(const int32_t* idx, int32_t* count, int32_t* offset, int32_t* tile_sum, int32_t* pos,
+hipError_t launch_dkv_prepare(const int32_t* idx, uint32_t* plan, int32_t* offset, int32_t* tile_sum, int32_t* pos,
                               int64_t B, int64_t S, int64_t S_kv, int64_t topk, int n_hblk, int64_t token0,
                               int64_t n_chunk, hipStream_t st) {
-  const int64_t n_rows = B * S_kv;
-  const int64_t n_cnt = n_rows * RANK_SUB;
-  hipError_t e = launch_fill_zero_f32((float*)count, (n_cnt + 3) / 4 * 4, st);
+  const int64_t nw = (n_chunk + 31) / 32, n_rows = B * S_kv;
+  const int64_t n = dkv_bitmap_words(n_rows, n_chunk);
+  int2* bc = (int2*)plan;             // {bits, count} per word, written whole by mark_kernel
+  int32_t* cur = (int32_t*)(plan + 2 * n);  // cursors of words with duplicate pairs
+  hipError_t e = launch_fill_zero_f32((float*)cur, (n + 3) / 4 * 4, st);
   if (e != hipSuccess) return e;
+  const int64_t mark_groups = nw * ((n_rows + MARK_ROWS - 1) / MARK_ROWS);
+  if (mark_groups > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mark_kernel, dim3((unsigned)mark_groups), dim3(256), 0, st, idx, bc, token0, n_chunk, S, S_kv,
+                     (int)topk, nw, n_rows);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t tiles = scan_tiles(n);
+  hipLaunchKernelGGL(scan_tiles_kernel, dim3((unsigned)tiles), dim3(256), 0, st, (const int2*)bc, offset, tile_sum,
+                     n, n_hblk);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_totals_kernel, dim3(1), dim3(256), 0, st, tile_sum, tiles, offset, n);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_add_kernel, dim3((unsigned)tiles), dim3(256), 0, st, offset, (const int32_t*)tile_sum, n);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t n_units = n_chunk * ((topk + 255) / 256);
-  hipLaunchKernelGGL(rank_kernel, dim3(grid_for(n_units, 1)), dim3(256), 0, st, idx, count, pos, token0, n_chunk, S,
-                     S_kv, (int)topk, n_hblk, n_rows);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t tiles = scan_tiles(n_cnt);
-  hipLaunchKernelGGL(scan_tiles_kernel, dim3((unsigned)tiles), dim3(256), 0, st, (const int32_t*)count, offset,
-                     tile_sum, n_cnt, n_rows);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_totals_kernel, dim3(1), dim3(256), 0, st, tile_sum, tiles, offset, n_cnt);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_add_kernel, dim3((unsigned)tiles), dim3(256), 0, st, offset, (const int32_t*)tile_sum,
-                     n_cnt);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(position_kernel, dim3(grid_for(n_units, 1)), dim3(256), 0, st, idx, (const int32_t*)offset,
-                     pos, token0, n_chunk, S, S_kv, (int)topk);
+  hipLaunchKernelGGL(position_kernel, dim3(grid_for(n_units, 1)), dim3(256), 0, st, idx, (const int2*)bc, cur,
+                     (const int32_t*)offset, pos, token0, n_chunk, S, S_kv, (int)topk, nw, n_hblk);
   return hipGetLastError();
 }
 
 hipError_t launch_reduce_rows(const uint16_t* stage, const int8_t* stage_exp, int nseg, const int32_t* offset,
-                              float* acc, void* out_bf16, int accumulate, int64_t n_rows, int64_t D, hipStream_t st) {
+                              int64_t stride, float* acc, void* out_bf16, int accumulate, int64_t n_rows, int64_t D,
+                              hipStream_t st) {
   if (D == 512)
     hipLaunchKernelGGL(reduce_rows_kernel<512>, dim3((unsigned)n_rows), dim3(256), 0, st, stage, stage_exp, nseg,
-                       offset, (f32x4*)acc, (uint4*)out_bf16, accumulate);
+                       offset, stride, (f32x4*)acc, (uint4*)out_bf16, accumulate);
   else if (D == 256)
     hipLaunchKernelGGL(reduce_rows_kernel<256>, dim3((unsigned)n_rows), dim3(256), 0, st, stage, stage_exp, nseg,
-                       offset, (f32x4*)acc, (uint4*)out_bf16, accumulate);
+                       offset, stride, (f32x4*)acc, (uint4*)out_bf16, accumulate);
   else if (D == 128)
     hipLaunchKernelGGL(reduce_rows_kernel<128>, dim3((unsigned)n_rows), dim3(256), 0, st, stage, stage_exp, nseg,
-                       offset, (f32x4*)acc, (uint4*)out_bf16, accumulate);
+                       offset, stride, (f32x4*)acc, (uint4*)out_bf16, accumulate);
   else if (D == 64)
     hipLaunchKernelGGL(reduce_rows_kernel<64>, dim3((unsigned)n_rows), dim3(256), 0, st, stage, stage_exp, nseg,
-                       offset, (f32x4*)acc, (uint4*)out_bf16, accumulate);
+                       offset, stride, (f32x4*)acc, (uint4*)out_bf16, accumulate);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

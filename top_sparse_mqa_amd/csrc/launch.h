@@ -58,17 +58,24 @@ hipError_t launch_bwd_dsink(const float* lse, const float* delta, const float* s
                             int64_t H, hipStream_t st);
 // which: 1 = dQ kernel (all tokens), 2 = dKV kernel (chunk; atomic or staging mode), 3 = both.
 hipError_t launch_bwd_main(const BwdMainArgs& a, int which, hipStream_t st);
-// Staging-row assignment for the tokens [token0, token0 + n_chunk): clears count, ranks every valid
-// slot within its kv row, scans the counts into offset[0..n_rows], and turns ranks into rows (pos).
-hipError_t launch_dkv_prepare(const int32_t* idx, int32_t* count, int32_t* offset, int32_t* tile_sum, int32_t* pos,
+// Staging-row assignment for the tokens [token0, token0 + n_chunk). `plan` holds 3 *
+// dkv_bitmap_words 32-bit words: {bitmap word, pair count} per word, then the cursors (written or
+// cleared here). Marks every valid
+// (token, kv row) pair, scans the words' pair counts into offset[0 .. words] and writes each valid
+// slot's first staging row into pos (-1 for masked slots). Positions depend on the indices only
+// unless a token selects a row more than once.
+hipError_t launch_dkv_prepare(const int32_t* idx, uint32_t* plan, int32_t* offset, int32_t* tile_sum, int32_t* pos,
                               int64_t B, int64_t S, int64_t S_kv, int64_t topk, int n_hblk, int64_t token0,
                               int64_t n_chunk, hipStream_t st);
 int64_t scan_tiles(int64_t n);
-// Number of rank counters (and scanned offsets, minus the final total) for n_rows kv rows.
-int64_t rank_counters(int64_t n_rows);
-// Per kv row: sum of its staging segment (+ acc if accumulate); writes acc (fp32) and/or out (bf16).
+// Words of the selection bitmap for n_rows kv rows and a chunk of n_chunk tokens (ceil(n_chunk /
+// 32) per row); also the number of scanned offsets before the final total.
+int64_t dkv_bitmap_words(int64_t n_rows, int64_t n_chunk);
+// Per kv row: sum of its staging segment [offset[row * stride], offset[(row + 1) * stride])
+// (+ acc if accumulate); writes acc (fp32) and/or out (bf16).
 hipError_t launch_reduce_rows(const uint16_t* stage, const int8_t* stage_exp, int nseg, const int32_t* offset,
-                              float* acc, void* out_bf16, int accumulate, int64_t n_rows, int64_t D, hipStream_t st);
+                              int64_t stride, float* acc, void* out_bf16, int accumulate, int64_t n_rows, int64_t D,
+                              hipStream_t st);
 hipError_t launch_bwd_postprocess(const float* acc, void* dkv, int64_t n, hipStream_t st);
 
 }  // namespace smqa
