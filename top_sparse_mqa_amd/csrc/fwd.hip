@@ -1,4 +1,6 @@
-// Forward kernel of top-k sparse MQA for gfx950 (see include/sparse_mqa.h for the contract).
+// Forward kernels of top-k sparse MQA for gfx950 (see include/sparse_mqa.h for the contract).
+// fwd_ws_kernel (below) serves D = 512 with blocks of 64 heads and default rounding; fwd_kernel
+// serves every other shape and reference_rounding.
 //
 // One workgroup per (query token, block of up to 64 heads). All heads of a token share the
 // gathered kv rows, so each block of 64 slots is gathered once into LDS (direct-to-LDS
@@ -297,6 +299,306 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Forward with specialised waves, for D = 512 and blocks of 64 heads (default rounding): eight
+// waves, two per SIMD, in two roles.
+//   Score waves (0-3) gather the 32-slot kv tiles (one 1 KiB row per direct-to-LDS instruction)
+//   and compute S^T for 16 heads each (16x16x32 MFMAs, Q in AGPRs), then the online softmax
+//   (running max and sum per head, sink included) and hand P (bf16, [head][slot]) and each head's
+//   rescale factor to the O waves through LDS.
+//   O waves (4-7) hold O^T for 128 d-columns of all 64 heads in registers and accumulate V^T P^T
+//   one block behind (32x32x16 MFMAs, V^T from transposing LDS reads).
+// Stage j runs block j on the score waves and block j - 1 on the O waves, and ends with one
+// workgroup barrier; three tile buffers let the gather of tile j + 1 land in the one the O waves
+// finished with. Both roles pass the same barriers (one before the stages, nblk + 1 stages, one
+// before the epilogue). A SIMD thus overlaps one role's gather issue, softmax and LDS traffic
+// with the other's MFMAs; with one wave per SIMD (fwd_kernel) they run one after another.
+__device__ __forceinline__ int fws_swz(int row) {
+  const int r = row & 15;
+  return ((r & 1) << 2) ^ (r & 10) ^ (((r >> 2) & 1) * 9);
+}
+
+template <int D>
+__global__ void __launch_bounds__(512)
+fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const float* __restrict__ sink,
+              const int32_t* __restrict__ idx, uint16_t* __restrict__ out, float* __restrict__ lse, int S,
+              int64_t S_kv, int H, int topk, float score_scale, int n_hblk, int n_tokens) {
+  constexpr int T = 32;           // slots per block
+  constexpr int HB = 64;          // heads per workgroup
+  constexpr int ROWB = D * 2;
+  constexpr int CPR = D / 8;      // 16-byte chunks per row
+  constexpr int TB = T * ROWB;
+  constexpr int KS = D / 32;      // k-steps of S^T
+  constexpr int NF = 2 * KS;      // score fragments (k-step, 16-slot half)
+  constexpr int PF = 6;           // score fragment reads in flight
+  constexpr int NP = T / 4;       // gather instructions per score wave
+  constexpr int DW = D / 4;       // O^T d-columns per O wave
+  constexpr int NDT = DW / 32;    // its 32-wide d tiles
+  constexpr int PB = HB * T * 2;  // bytes of one P buffer
+  static_assert(ROWB == 1024 && NDT * 32 == DW, "one kv row per gather instruction");
+  __shared__ __attribute__((aligned(16))) char tile0[TB];
+  __shared__ __attribute__((aligned(16))) char tile1[TB];
+  __shared__ __attribute__((aligned(16))) char tile2[TB];
+  __shared__ __attribute__((aligned(16))) char pbuf0[PB];
+  __shared__ __attribute__((aligned(16))) char pbuf1[PB];
+  __shared__ __attribute__((aligned(16))) char pbuf2[PB];
+  __shared__ float alpha_s[3][HB];
+  __shared__ float fin_l[HB];
+
+  const int lane = threadIdx.x & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int item = blockIdx.x;
+  const int64_t token = (int64_t)n_tokens - 1 - item / n_hblk;  // heavier (later) tokens first
+  const int hblk = item % n_hblk;
+  const int64_t b = token / S;
+  const int nblk = (topk + T - 1) / T;
+  const int32_t* idx_tok = idx + token * (int64_t)topk;
+  auto load_idx = [&](int blk) -> int32_t {
+    const int t = blk * T + lane;
+    return (lane < T && t < topk) ? idx_tok[t] : -1;
+  };
+  auto tile_at = [&](int k) -> char* { return k == 0 ? tile0 : (k == 1 ? tile1 : tile2); };
+  auto pbuf_at = [&](int k) -> char* { return k == 0 ? pbuf0 : (k == 1 ? pbuf1 : pbuf2); };
+
+  if (wu < 4) {
+    // ---------------- score waves: wave wu owns heads 16 wu .. 16 wu + 15 ----------------
+    const int g = lane >> 4;
+    const int hrow = 16 * wu + (lane & 15);
+    const int head = hblk * HB + hrow;
+    // Q as the B operand of S^T = K Q^T: lane holds head (lane & 15), d = 32 ks + 8 g .. +7. It
+    // stays in ordinary vector registers: with no accumulation registers in use the whole 256-register
+    // budget of two waves per SIMD goes to them, which the O waves' 128-register accumulator needs.
+    bf16x8 qb[KS];
+    {
+      const uint16_t* qrow = q + (token * H + head) * (int64_t)D + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) qb[ks] = load_bf16x8(qrow + 32 * ks);
+    }
+    const float sink2 = sink[head] * kLog2e;
+    float m_run = sink2;
+    // the sink's share of the denominator is carried by the g == 0 lane of each head
+    float l_run = (g == 0 && sink2 != -INFINITY) ? 1.f : 0.f;
+    // score fragment offsets: rows lane & 15 (+16 for the second half), chunk 4 ks + g, swizzled
+    // by the row's low bits (fragments four k-steps apart differ by 256 bytes)
+    int sc_off[4];
+    {
+      const int row = lane & 15;
+#pragma unroll
+      for (int j = 0; j < 4; j++) sc_off[j] = row * ROWB + (((4 * j + g) ^ (fws_swz(row) & (CPR - 1))) << 4);
+    }
+    const char* kv_b = (const char*)(kv + b * S_kv * D);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv_b, (int)(S_kv * ROWB));
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(g_zero_row, ROWB);
+    // part k of this wave's share of a tile: row wu + 4 k, masked rows read the zero row
+    auto gpart = [&](int k, int32_t my_idx, uint64_t mask, char* tile) {
+      const int r = wu + 4 * k;
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int32_t ri = __builtin_amdgcn_readlane(my_idx, r);
+      const uint32_t voff = (uint32_t)((ln ^ (fws_swz(r) & (CPR - 1))) << 4);
+      const bool v = (mask >> r) & 1ull;
+      dma16_buf(v ? rk : rz, voff, v ? (uint32_t)ri * ROWB : 0u, tile + r * ROWB);
+    };
+    uint64_t mask_cur;
+    {
+      const int32_t i0 = load_idx(0);
+      mask_cur = __ballot(slot_in_range(i0, S_kv));
+      if (mask_cur) {
+#pragma unroll
+        for (int k = 0; k < NP; k++) gpart(k, i0, mask_cur, tile0);
+      }
+    }
+    int32_t idx_nxt = nblk > 1 ? load_idx(1) : -1;
+    wait_all_mem();
+    uint64_t mask_nxt = __ballot(slot_in_range(idx_nxt, S_kv));
+    __syncthreads();  // tile 0 is complete
+
+    auto sblock = [&](auto buf_tag, int blk) {
+      constexpr int BUF = decltype(buf_tag)::value;
+      const char* tile = tile_at(BUF);
+      char* nxt = tile_at((BUF + 1) % 3);
+      char* pw = pbuf_at(BUF) + (hrow * T + 4 * g) * 2;
+      if (blk < nblk) {
+        const uint64_t mask = mask_cur, mask_g = mask_nxt;
+        const int32_t idx_g = idx_nxt;
+        const int32_t idx_new = blk + 2 < nblk ? load_idx(blk + 2) : -1;
+        if (mask == 0) {
+          if (mask_g) {
+#pragma unroll
+            for (int k = 0; k < NP; k++) gpart(k, idx_g, mask_g, nxt);
+          }
+        } else {
+          // S^T for the block: fragment i = (k-step i / 2, half i % 2); PF reads run ahead, every
+          // stage fenced; the next tile's gather goes out in parts (the zero row when there is no
+          // next block, into a buffer nothing reads before the next wait)
+          f32x4 sacc[2];
+#pragma unroll
+          for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) sacc[mt][r] = 0.f;
+          auto frag = [&](int i) {
+            const int ks = i >> 1, mt = i & 1;
+            return lds_load16(tile + sc_off[ks % 4] + 256 * (ks / 4) + mt * 16 * ROWB);
+          };
+          constexpr int NB = PF + 1;
+          bf16x8 fr[NB];
+#pragma unroll
+          for (int i = 0; i < PF; i++) fr[i] = frag(i);
+          static_for<NF>([&](auto it) {
+            constexpr int i = decltype(it)::value;
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (i + PF < NF) fr[(i + PF) % NB] = frag(i + PF);
+            sacc[i & 1] = mfma16(fr[i % NB], qb[i >> 1], sacc[i & 1]);
+            if constexpr (i % (NF / NP) == NF / NP / 2) gpart(i / (NF / NP), idx_g, mask_g, nxt);
+          });
+          __builtin_amdgcn_sched_barrier(0);
+          // online softmax in log2 units; this lane holds head hrow, slots 16 mt + 4 g + r
+          const uint32_t vb = (uint32_t)(mask >> (4 * g));
+          float sv[8];
+          float bmax = -INFINITY;
+#pragma unroll
+          for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+              const float v = ((vb >> (16 * mt + r)) & 1u) ? sacc[mt][r] * score_scale : -INFINITY;
+              sv[4 * mt + r] = v;
+              bmax = fmaxf(bmax, v);
+            }
+          bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+          bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+          // the running max only moves when the block exceeds it by more than 8, so P <= 2^8 and
+          // the O rescale runs on few blocks; O / l and m + log2(l) do not depend on where it sits
+          const float m_new = (bmax > m_run + 8.f) ? bmax : m_run;  // bmax is finite: a slot is valid
+          const float alpha = fast_exp2(m_run - m_new);
+          m_run = m_new;
+          float ps = 0.f;
+          float p[8];
+#pragma unroll
+          for (int k = 0; k < 8; k++) {
+            p[k] = fast_exp2(sv[k] - m_new);
+            ps += p[k];
+          }
+          l_run = l_run * alpha + ps;
+#pragma unroll
+          for (int mt = 0; mt < 2; mt++)
+            *(uint2*)(pw + 32 * mt) = pack4_bf16(p[4 * mt], p[4 * mt + 1], p[4 * mt + 2], p[4 * mt + 3]);
+          if (g == 0) alpha_s[BUF][hrow] = alpha;
+        }
+        // the next indices are used here, so that later waits never include this stage's gathers
+        mask_cur = mask_g;
+        mask_nxt = __ballot(slot_in_range(idx_new, S_kv));
+        idx_nxt = idx_new;
+        wait_all_mem();  // this wave's part of tile blk + 1
+      }
+      lds_barrier();
+    };
+    for (int blk = 0; blk <= nblk; blk += 3) {
+      sblock(IntTag<0>{}, blk);
+      if (blk + 1 <= nblk) sblock(IntTag<1>{}, blk + 1);
+      if (blk + 2 <= nblk) sblock(IntTag<2>{}, blk + 2);
+    }
+    // denominator of each head: the four lanes (g) of the head hold parts of it
+    const float l1 = l_run + __shfl_xor(l_run, 16);
+    const float ltot = l1 + __shfl_xor(l1, 32);
+    if (g == 0) {
+      fin_l[hrow] = ltot;
+      lse[token * H + head] = ltot > 0.f ? m_run + log2f(ltot) : -INFINITY;
+    }
+    __syncthreads();  // the denominators are in LDS
+  } else {
+    // ---------- O waves: wave 4 + ow owns d-columns ow DW .. ow DW + DW - 1 of all heads ----------
+    const int ow = wu - 4;
+    // O^T[d, head] for d tile dt and head half hh: lane holds head 32 hh + (lane & 31),
+    // d = ow DW + 32 dt + 8 (r >> 2) + 4 (lane >> 5) + (r & 3)
+    f32x16 oacc[NDT][2];
+#pragma unroll
+    for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) oacc[dt][hh][r] = 0.f;
+    int32_t idx_cur = load_idx(0);
+    __syncthreads();  // tile 0 is complete (the score waves' set-up)
+
+    auto oblock = [&](auto buf_tag, int j) {
+      constexpr int BUF = decltype(buf_tag)::value;
+      constexpr int PBUF = (BUF + 2) % 3;  // block j - 1 went through buffers (j - 1) % 3
+      if (j >= 1 && j <= nblk) {
+        const int32_t idx_this = idx_cur;
+        if (j < nblk) idx_cur = load_idx(j);
+        const uint64_t mask = __ballot(slot_in_range(idx_this, S_kv));
+        if (mask) {
+          int ln = lane;
+          asm volatile("" : "+v"(ln));
+          const char* tile = tile_at(PBUF);
+          const char* pp = pbuf_at(PBUF);
+          const float a0 = alpha_s[PBUF][ln & 31], a1 = alpha_s[PBUF][32 + (ln & 31)];
+          if (__any(a0 != 1.f || a1 != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+              for (int r = 0; r < 16; r++) {
+                oacc[dt][0][r] *= a0;
+                oacc[dt][1][r] *= a1;
+              }
+          }
+          // V^T A fragments: for k-step kk (slots 16 kk .. +15), lane l gets d = dbase + (l & 31) and
+          // slots s0 .. s0 + 7, s0 = 16 kk + 8 (l >> 5), from two transposing reads four rows apart
+          const int vrow = 8 * (ln >> 5) + ((ln & 15) >> 2);
+          const int vch = 2 * ((ln >> 4) & 1) + ((ln & 3) >> 1);
+          const int hoff = 8 * (ln & 1);
+          auto vfrag = [&](int kk, int dt) {
+            const int r0 = 16 * kk + vrow, c = ow * (DW / 8) + 4 * dt + vch;
+            const char* p0 = tile + r0 * ROWB + ((c ^ (fws_swz(r0) & (CPR - 1))) << 4) + hoff;
+            const char* p1 = tile + (r0 + 4) * ROWB + ((c ^ (fws_swz(r0 + 4) & (CPR - 1))) << 4) + hoff;
+            return join_tr(lds_load_tr(p0), lds_load_tr(p1));
+          };
+#pragma unroll
+          for (int kk = 0; kk < 2; kk++) {
+            // P^T B fragments: lane holds head 32 hh + (l & 31), slots 16 kk + 8 (l >> 5) .. +7
+            bf16x8 pv[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; hh++)
+              pv[hh] = lds_load16(pp + ((32 * hh + (ln & 31)) * T + 16 * kk + 8 * (ln >> 5)) * 2);
+            bf16x8 va[NDT];
+#pragma unroll
+            for (int dt = 0; dt < NDT; dt++) va[dt] = vfrag(kk, dt);
+#pragma unroll
+            for (int dt = 0; dt < NDT; dt++) {
+              oacc[dt][0] = mfma32(va[dt], pv[0], oacc[dt][0]);
+              oacc[dt][1] = mfma32(va[dt], pv[1], oacc[dt][1]);
+            }
+          }
+        }
+      }
+      lds_barrier();
+    };
+    for (int j = 0; j <= nblk; j += 3) {
+      oblock(IntTag<0>{}, j);
+      if (j + 1 <= nblk) oblock(IntTag<1>{}, j + 1);
+      if (j + 2 <= nblk) oblock(IntTag<2>{}, j + 2);
+    }
+    __syncthreads();  // the denominators are in LDS
+    // epilogue: normalise and store O (bf16), four consecutive d per 8-byte store
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++) {
+      const int hr = 32 * hh + (lane & 31);
+      const float l = fin_l[hr];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      uint16_t* orow = out + (token * H + hblk * HB + hr) * (int64_t)D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; r4++) {
+          const int d = ow * DW + 32 * dt + 8 * r4 + 4 * (lane >> 5);
+          *(uint2*)(orow + d) = pack4_bf16(oacc[dt][hh][4 * r4] * inv, oacc[dt][hh][4 * r4 + 1] * inv,
+                                           oacc[dt][hh][4 * r4 + 2] * inv, oacc[dt][hh][4 * r4 + 3] * inv);
+        }
+    }
+  }
+  wait_all_mem();
+}
+
 template <int D, int NHG, bool RR>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const int n_hblk = (int)((a.H + 32 * NHG - 1) / (32 * NHG));
@@ -310,6 +612,16 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
 
 template <bool RR>
 static hipError_t launch_fwd_rr(const FwdArgs& a, hipStream_t st) {
+  if constexpr (!RR) {
+    if (a.D == 512 && a.H % 64 == 0) {  // blocks of 64 heads: the specialised-wave kernel
+      const int n_hblk = (int)(a.H / 64);
+      const int n_tokens = (int)(a.B * a.S);
+      hipLaunchKernelGGL((fwd_ws_kernel<512>), dim3((unsigned)(n_tokens * n_hblk)), dim3(512), 0, st,
+                         (const uint16_t*)a.q, (const uint16_t*)a.kv, a.sink, a.idx, (uint16_t*)a.o, a.lse, (int)a.S,
+                         a.S_kv, (int)a.H, (int)a.topk, a.sm_scale * kLog2e, n_hblk, n_tokens);
+      return hipGetLastError();
+    }
+  }
   if (a.D == 512) return a.H <= 32 ? launch_fwd_t<512, 1, RR>(a, st) : launch_fwd_t<512, 2, RR>(a, st);
   if (a.D == 256) return a.H <= 32 ? launch_fwd_t<256, 1, RR>(a, st) : launch_fwd_t<256, 2, RR>(a, st);
   if (a.D == 128) return a.H <= 32 ? launch_fwd_t<128, 1, RR>(a, st) : launch_fwd_t<128, 2, RR>(a, st);
