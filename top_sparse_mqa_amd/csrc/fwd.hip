@@ -331,7 +331,7 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
   constexpr int KS = D / 32;      // k-steps of S^T
   constexpr int NF = 2 * KS;      // score fragments (k-step, 16-slot half)
   constexpr int PF = 6;           // score fragment reads in flight
-  constexpr int NP = T / 4;       // gather instructions per score wave
+  constexpr int NP = T / 8;       // gather instructions per wave (all eight waves gather)
   constexpr int DW = D / 4;       // O^T d-columns per O wave
   constexpr int NDT = DW / 32;    // its 32-wide d tiles
   constexpr int PB = HB * T * 2;  // bytes of one P buffer
@@ -359,6 +359,28 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
   };
   auto tile_at = [&](int k) -> char* { return k == 0 ? tile0 : (k == 1 ? tile1 : tile2); };
   auto pbuf_at = [&](int k) -> char* { return k == 0 ? pbuf0 : (k == 1 ? pbuf1 : pbuf2); };
+  // Tile gathers are shared by all eight waves: part k of wave wu is row wu + 8 k (one kv row per
+  // instruction; masked rows read the zero row). The buffer a stage gathers into is read by neither
+  // role during that stage, so the O waves issue their parts at once and the score waves spread
+  // theirs over the score loop.
+  const char* kv_b = (const char*)(kv + b * S_kv * D);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv_b, (int)(S_kv * ROWB));
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(g_zero_row, ROWB);
+  auto gpart = [&](int k, int32_t my_idx, uint64_t mask, char* tile) {
+    const int r = wu + 8 * k;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int32_t ri = __builtin_amdgcn_readlane(my_idx, r);
+    const uint32_t voff = (uint32_t)((ln ^ (fws_swz(r) & (CPR - 1))) << 4);
+    const bool v = (mask >> r) & 1ull;
+    dma16_buf(v ? rk : rz, voff, v ? (uint32_t)ri * ROWB : 0u, tile + r * ROWB);
+  };
+  const int32_t idx0 = load_idx(0);
+  const uint64_t mask0 = __ballot(slot_in_range(idx0, S_kv));
+  if (mask0) {
+#pragma unroll
+    for (int k = 0; k < NP; k++) gpart(k, idx0, mask0, tile0);
+  }
 
   if (wu < 4) {
     // ---------------- score waves: wave wu owns heads 16 wu .. 16 wu + 15 ----------------
@@ -386,28 +408,7 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
 #pragma unroll
       for (int j = 0; j < 4; j++) sc_off[j] = row * ROWB + (((4 * j + g) ^ (fws_swz(row) & (CPR - 1))) << 4);
     }
-    const char* kv_b = (const char*)(kv + b * S_kv * D);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv_b, (int)(S_kv * ROWB));
-    const __amdgpu_buffer_rsrc_t rz = make_rsrc(g_zero_row, ROWB);
-    // part k of this wave's share of a tile: row wu + 4 k, masked rows read the zero row
-    auto gpart = [&](int k, int32_t my_idx, uint64_t mask, char* tile) {
-      const int r = wu + 4 * k;
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int32_t ri = __builtin_amdgcn_readlane(my_idx, r);
-      const uint32_t voff = (uint32_t)((ln ^ (fws_swz(r) & (CPR - 1))) << 4);
-      const bool v = (mask >> r) & 1ull;
-      dma16_buf(v ? rk : rz, voff, v ? (uint32_t)ri * ROWB : 0u, tile + r * ROWB);
-    };
-    uint64_t mask_cur;
-    {
-      const int32_t i0 = load_idx(0);
-      mask_cur = __ballot(slot_in_range(i0, S_kv));
-      if (mask_cur) {
-#pragma unroll
-        for (int k = 0; k < NP; k++) gpart(k, i0, mask_cur, tile0);
-      }
-    }
+    uint64_t mask_cur = mask0;
     int32_t idx_nxt = nblk > 1 ? load_idx(1) : -1;
     wait_all_mem();
     uint64_t mask_nxt = __ballot(slot_in_range(idx_nxt, S_kv));
@@ -517,15 +518,26 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
       for (int hh = 0; hh < 2; hh++)
 #pragma unroll
         for (int r = 0; r < 16; r++) oacc[dt][hh][r] = 0.f;
-    int32_t idx_cur = load_idx(0);
-    __syncthreads();  // tile 0 is complete (the score waves' set-up)
+    // indices of blocks j - 1 (products), j and j + 1 (gather) at the top of stage j
+    int32_t idx_m1 = -1, idx_0 = idx0, idx_p1 = nblk > 1 ? load_idx(1) : -1;
+    wait_all_mem();
+    __syncthreads();  // tile 0 is complete
 
     auto oblock = [&](auto buf_tag, int j) {
       constexpr int BUF = decltype(buf_tag)::value;
       constexpr int PBUF = (BUF + 2) % 3;  // block j - 1 went through buffers (j - 1) % 3
+      const int32_t idx_this = idx_m1;
+      if (j + 1 < nblk) {  // this wave's rows of tile j + 1
+        const uint64_t mask_g = __ballot(slot_in_range(idx_p1, S_kv));
+        if (mask_g) {
+#pragma unroll
+          for (int k = 0; k < NP; k++) gpart(k, idx_p1, mask_g, tile_at((BUF + 1) % 3));
+        }
+      }
+      idx_m1 = idx_0;
+      idx_0 = idx_p1;
+      idx_p1 = j + 2 < nblk ? load_idx(j + 2) : -1;
       if (j >= 1 && j <= nblk) {
-        const int32_t idx_this = idx_cur;
-        if (j < nblk) idx_cur = load_idx(j);
         const uint64_t mask = __ballot(slot_in_range(idx_this, S_kv));
         if (mask) {
           int ln = lane;
@@ -571,6 +583,7 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
           }
         }
       }
+      wait_all_mem();  // this wave's rows of tile j + 1
       lds_barrier();
     };
     for (int j = 0; j <= nblk; j += 3) {
