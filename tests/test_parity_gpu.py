@@ -150,6 +150,30 @@ def test_edge_shapes_full(gpu_lib, case):
     torch.testing.assert_close(l0[1:].double(), x["attn_sink"][1:].double() / math.log(2), rtol=0, atol=1e-5)
 
 
+@pytest.mark.parametrize("H", [64, 128])
+def test_empty_blocks_64_head_kernels(gpu_lib, H):
+    """The 64-head D = 512 kernels skip 32-slot blocks with no valid slot in both of their wave
+    roles; here whole blocks are masked for every token (at the start, in the middle, between
+    valid blocks), one token keeps only its last block, one token has none, and the last block is
+    ragged (topk = 200)."""
+    B, S, S_kv, D, topk = 1, 6, 400, 512, 200
+    say("case", "empty blocks", dict(H=H))
+    g = torch.Generator().manual_seed(31 + H)
+    x = {
+        "q": torch.randn(B, S, H, D, generator=g).to(torch.bfloat16),
+        "kv": torch.randn(B, S_kv, D, generator=g).to(torch.bfloat16),
+        "attn_sink": torch.randn(H, generator=g),
+        "do": torch.randn(B, S, H, D, generator=g).to(torch.bfloat16),
+    }
+    idx = torch.stack([torch.randperm(S_kv, generator=g)[:topk] for _ in range(B * S)]).view(B, S, topk)
+    idx[:, :, 0:32] = -1      # first block
+    idx[:, :, 96:160] = -1    # two middle blocks
+    idx[0, 2, :192] = -1      # only the ragged last block left
+    idx[0, 4, :] = -1         # nothing left
+    x["topk_idxs"] = idx.to(torch.int32)
+    full_parity(x, tag=f"empty blocks H={H}")
+
+
 def test_operand_scales_and_row_norms(gpu_lib):
     """Magnitudes away from 1 for the fp16 operands of the dKV product: q scaled by 1/128, one
     referenced kv row 8x the others (it sets the dS bound of the tokens that reference it) and one
