@@ -39,7 +39,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 KERNELS = ("fwd", "bwd_preprocess", "bwd_dq", "bwd_dkv_prepare", "bwd_dkv_partials", "bwd_dkv_reduce")
 # single-kernel steps: rocprofv3 kernel name prefix, source files, algorithmic flops per valid pair / (H*D)
 SINGLE = {
-    "fwd": ("smqa::fwd_kernel", ("fwd.hip", "device_common.h"), 4),
+    "fwd": ("smqa::fwd_", ("fwd.hip", "device_common.h"), 4),  # fwd_ws_kernel at H=64k D=512
     "bwd_dq": ("smqa::bwd_dq_kernel", ("bwd.hip", "device_common.h"), 6),
     "bwd_dkv_partials": ("smqa::bwd_dkv_", ("bwd.hip", "device_common.h"), 8),  # _ws_kernel at H=64 D=512
 }
