@@ -386,6 +386,223 @@ bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
 }
 
 // ---------------------------------------------------------------------------------------------
+// dQ with specialised waves, for D = 512 and blocks of 64 heads: eight waves, two per SIMD.
+//   Score waves (0-3) compute S^T and dP^T for 16 heads each (16x16x32 MFMAs), then P and
+//   dS = P (dP - Delta), and hand dS (bf16, [head][slot]) to the dQ waves through LDS.
+//   dQ waves (4-7) hold dQ^T for 128 d-columns of all 64 heads, add K^T dS^T one block behind
+//   (32x32x16 MFMAs, K^T from transposing reads of the same tile) and gather the tiles.
+// Stage j runs block j on the score waves and block j - 1 on the dQ waves and ends with one
+// workgroup barrier; three tile buffers let the dQ waves gather tile j + 1 during stage j (the
+// buffer neither role reads then). Q and dO stay in ordinary vector registers, so the whole
+// 256-register budget of two waves per SIMD is there for them and for the dQ accumulator.
+template <int D>
+__global__ void __launch_bounds__(512)
+bwd_dq_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ dout,
+                 const int32_t* __restrict__ idx, const float* __restrict__ lse, const float* __restrict__ delta,
+                 uint16_t* __restrict__ dq, int S, int64_t S_kv, int H, int topk, float sm_scale, float scale_log2,
+                 int n_hblk, int n_tokens) {
+  using C = BwdCommon<D, 4>;
+  constexpr int T = C::T;
+  constexpr int HB = 64;
+  constexpr int ROWB = C::ROWB, CPR = C::CPR, TB = C::TB;
+  constexpr int PF = 6;
+  constexpr int NP = T / 4;       // gather instructions per dQ wave (the dQ waves gather every row)
+  constexpr int DW = D / 4;       // dQ^T d-columns per dQ wave
+  constexpr int NDT = DW / 32;
+  constexpr int DB = HB * T * 2;  // bytes of one dS buffer
+  static_assert(ROWB == 1024 && NDT * 32 == DW, "one kv row per gather instruction");
+  __shared__ __attribute__((aligned(16))) char tile0[TB];
+  __shared__ __attribute__((aligned(16))) char tile1[TB];
+  __shared__ __attribute__((aligned(16))) char tile2[TB];
+  __shared__ __attribute__((aligned(16))) char dsb0[DB];
+  __shared__ __attribute__((aligned(16))) char dsb1[DB];
+  __shared__ __attribute__((aligned(16))) char dsb2[DB];
+
+  const int lane = threadIdx.x & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int item = blockIdx.x;
+  const int64_t token = (int64_t)n_tokens - 1 - item / n_hblk;  // heavier (later) tokens first
+  const int hblk = item % n_hblk;
+  const int64_t b = token / S;
+  const int nblk = (topk + T - 1) / T;
+  const int32_t* idx_tok = idx + token * (int64_t)topk;
+  auto load_idx = [&](int blk) -> int32_t {
+    const int t = blk * T + lane;
+    return (lane < T && t < topk) ? idx_tok[t] : -1;
+  };
+  auto tile_at = [&](int k) -> char* { return k == 0 ? tile0 : (k == 1 ? tile1 : tile2); };
+  auto dsb_at = [&](int k) -> char* { return k == 0 ? dsb0 : (k == 1 ? dsb1 : dsb2); };
+  // Part k of dQ wave wu - 4's share of a tile: row (wu - 4) + 4 k, one kv row per instruction,
+  // masked rows read the zero row; the row's 16-byte chunks are swizzled as the score and
+  // transposing reads expect. Only the dQ waves gather: the score waves' 64 MFMAs per block make
+  // them the longer role, and gathering from their score loop cost ~10%.
+  const char* kv_b = (const char*)(kv + b * S_kv * D);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv_b, (int)(S_kv * ROWB));
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(g_zero_row_bwd, ROWB);
+  auto gpart = [&](int k, int32_t my_idx, uint64_t mask, char* tile) {
+    const int r = (wu - 4) + 4 * k;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int32_t ri = __builtin_amdgcn_readlane(my_idx, r);
+    const uint32_t voff = (uint32_t)((ln ^ (bwd_swz(r) & (CPR - 1))) << 4);
+    const bool v = (mask >> r) & 1ull;
+    dma16_buf(v ? rk : rz, voff, v ? (uint32_t)ri * ROWB : 0u, tile + r * ROWB);
+  };
+  const int32_t idx0 = load_idx(0);
+  const uint64_t mask0 = __ballot(slot_in_range(idx0, S_kv));
+  if (mask0 && wu >= 4) {
+#pragma unroll
+    for (int k = 0; k < NP; k++) gpart(k, idx0, mask0, tile0);
+  }
+
+  if (wu < 4) {
+    // ---------------- score waves: wave wu owns heads 16 wu .. 16 wu + 15 ----------------
+    const int g = lane >> 4;
+    const int hrow = 16 * wu + (lane & 15);
+    const int head = hblk * HB + hrow;
+    bf16x8 qb[C::KS], dob[C::KS];
+    {
+      const int64_t off = (token * H + head) * (int64_t)D + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ks++) {
+        qb[ks] = load_bf16x8(q + off + 32 * ks);
+        dob[ks] = load_bf16x8(dout + off + 32 * ks);
+      }
+    }
+    const float lse_h = lse[token * H + head];
+    const float delta_h = delta[token * H + head];
+    int sc_off[C::KSJ];
+    bwd_score_offsets<D>(lane, sc_off);
+    const int dw_off = (hrow * T + 4 * g) * 2;  // dS writes: head hrow, slots 16 mt + 4 g .. +3
+    uint64_t mask_cur = mask0;
+    uint64_t mask_nxt = __ballot(slot_in_range(nblk > 1 ? load_idx(1) : -1, S_kv));
+    __syncthreads();  // tile 0 is complete (the dQ waves' gathers)
+
+    auto sblock = [&](auto buf_tag, int blk) {
+      constexpr int BUF = decltype(buf_tag)::value;
+      const char* tile = tile_at(BUF);
+      char* dw = dsb_at(BUF) + dw_off;
+      if (blk < nblk) {
+        const uint64_t mask = mask_cur;
+        const int32_t idx_new = blk + 2 < nblk ? load_idx(blk + 2) : -1;
+        if (mask != 0) {
+          f32x4 sacc[2], dpacc[2];
+          bwd_scores<D, PF>(tile, sc_off, qb, dob, sacc, dpacc, [](int) {});
+          const uint32_t vb = (uint32_t)(mask >> (4 * g));
+#pragma unroll
+          for (int mt = 0; mt < 2; mt++) {
+            float ds[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+              const float p = ((vb >> (16 * mt + r)) & 1u) ? fast_exp2(sacc[mt][r] * scale_log2 - lse_h) : 0.f;
+              ds[r] = p * (dpacc[mt][r] - delta_h);
+            }
+            *(uint2*)(dw + 32 * mt) = pack4_bf16(ds[0], ds[1], ds[2], ds[3]);
+          }
+        }
+        mask_cur = mask_nxt;
+        mask_nxt = __ballot(slot_in_range(idx_new, S_kv));
+      }
+      lds_barrier();
+    };
+    for (int blk = 0; blk <= nblk; blk += 3) {
+      sblock(IntTag<0>{}, blk);
+      if (blk + 1 <= nblk) sblock(IntTag<1>{}, blk + 1);
+      if (blk + 2 <= nblk) sblock(IntTag<2>{}, blk + 2);
+    }
+  } else {
+    // ------- dQ waves: wave 4 + qw owns d-columns qw DW .. qw DW + DW - 1 of all 64 heads -------
+    const int qw = wu - 4;
+    // dQ^T[d, head] for d tile dt and head half hh: lane holds head 32 hh + (lane & 31),
+    // d = qw DW + 32 dt + 8 (r >> 2) + 4 (lane >> 5) + (r & 3)
+    f32x16 acc[NDT][2];
+#pragma unroll
+    for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[dt][hh][r] = 0.f;
+    // indices of blocks j - 1 (products), j and j + 1 (gather) at the top of stage j
+    int32_t idx_m1 = -1, idx_0 = idx0, idx_p1 = nblk > 1 ? load_idx(1) : -1;
+    wait_all_mem();
+    __syncthreads();  // tile 0 is complete
+
+    auto qblock = [&](auto buf_tag, int j) {
+      constexpr int BUF = decltype(buf_tag)::value;
+      constexpr int PBUF = (BUF + 2) % 3;  // block j - 1 went through buffers (j - 1) % 3
+      const int32_t idx_this = idx_m1;
+      if (j + 1 < nblk) {  // this wave's rows of tile j + 1, issued before its products
+        const uint64_t mask_g = __ballot(slot_in_range(idx_p1, S_kv));
+        if (mask_g) {
+#pragma unroll
+          for (int k = 0; k < NP; k++) gpart(k, idx_p1, mask_g, tile_at((BUF + 1) % 3));
+        }
+      }
+      idx_m1 = idx_0;
+      idx_0 = idx_p1;
+      idx_p1 = j + 2 < nblk ? load_idx(j + 2) : -1;
+      if (j >= 1 && j <= nblk) {
+        const uint64_t mask = __ballot(slot_in_range(idx_this, S_kv));
+        if (mask) {
+          int ln = lane;
+          asm volatile("" : "+v"(ln));
+          const char* tile = tile_at(PBUF);
+          const char* dsp = dsb_at(PBUF);
+          // K^T A fragments: for k-step kk (slots 16 kk .. +15), lane l gets d = dbase + (l & 31) and
+          // slots 16 kk + 8 (l >> 5) .. +7, from two transposing reads four rows apart
+          const int krow = 8 * (ln >> 5) + ((ln & 15) >> 2);
+          const int kch = 2 * ((ln >> 4) & 1) + ((ln & 3) >> 1);
+          const int hoff = 8 * (ln & 1);
+          auto kfrag = [&](int kk, int dt) {
+            const int r0 = 16 * kk + krow, c = qw * (DW / 8) + 4 * dt + kch;
+            const char* p0 = tile + r0 * ROWB + ((c ^ (bwd_swz(r0) & (CPR - 1))) << 4) + hoff;
+            const char* p1 = tile + (r0 + 4) * ROWB + ((c ^ (bwd_swz(r0 + 4) & (CPR - 1))) << 4) + hoff;
+            return join_tr(lds_load_tr(p0), lds_load_tr(p1));
+          };
+#pragma unroll
+          for (int kk = 0; kk < 2; kk++) {
+            // dS^T B fragments: lane holds head 32 hh + (l & 31), slots 16 kk + 8 (l >> 5) .. +7
+            bf16x8 dv[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; hh++)
+              dv[hh] = lds_load16(dsp + ((32 * hh + (ln & 31)) * T + 16 * kk + 8 * (ln >> 5)) * 2);
+            bf16x8 ka[NDT];
+#pragma unroll
+            for (int dt = 0; dt < NDT; dt++) ka[dt] = kfrag(kk, dt);
+#pragma unroll
+            for (int dt = 0; dt < NDT; dt++) {
+              acc[dt][0] = mfma32(ka[dt], dv[0], acc[dt][0]);
+              acc[dt][1] = mfma32(ka[dt], dv[1], acc[dt][1]);
+            }
+          }
+        }
+      }
+      wait_all_mem();  // this wave's rows of tile j + 1
+      lds_barrier();
+    };
+    for (int j = 0; j <= nblk; j += 3) {
+      qblock(IntTag<0>{}, j);
+      if (j + 1 <= nblk) qblock(IntTag<1>{}, j + 1);
+      if (j + 2 <= nblk) qblock(IntTag<2>{}, j + 2);
+    }
+    // dQ = sm_scale * (dS K), bf16, four consecutive d per 8-byte store
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++) {
+      uint16_t* row = dq + (token * H + hblk * HB + 32 * hh + (lane & 31)) * (int64_t)D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; r4++) {
+          const int d = qw * DW + 32 * dt + 8 * r4 + 4 * (lane >> 5);
+          *(uint2*)(row + d) = pack4_bf16(acc[dt][hh][4 * r4] * sm_scale, acc[dt][hh][4 * r4 + 1] * sm_scale,
+                                          acc[dt][hh][4 * r4 + 2] * sm_scale, acc[dt][hh][4 * r4 + 3] * sm_scale);
+        }
+    }
+  }
+  wait_all_mem();
+}
+
+// ---------------------------------------------------------------------------------------------
 // STAGED: every valid slot's dKV row goes to its staging row (pos, stage, stage_exp); otherwise it
 // is added into the fp32 accumulator dkv_acc with fp32 atomics (the workspace-free variant).
 template <int D, int NW, bool STAGED>
@@ -1544,6 +1761,17 @@ template <int D, int NW>
 static hipError_t launch_bwd_main_t(const BwdMainArgs& a, int which, hipStream_t st) {
   const int n_hblk = (int)(a.H / (16 * NW));
   const float sl2 = a.sm_scale * kLog2e;
+  if constexpr (NW == 4 && D == 512) {
+    if (which & 1) {  // 64 heads at D = 512: the specialised-wave dQ kernel
+      const int n_tokens = (int)(a.B * a.S);
+      hipLaunchKernelGGL((bwd_dq_ws_kernel<D>), dim3((unsigned)(n_tokens * n_hblk)), dim3(512), 0, st,
+                         (const uint16_t*)a.q, (const uint16_t*)a.kv, (const uint16_t*)a.d_o, a.idx, a.lse, a.delta,
+                         (uint16_t*)a.dq, (int)a.S, a.S_kv, (int)a.H, (int)a.topk, a.sm_scale, sl2, n_hblk, n_tokens);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      which &= ~1;
+    }
+  }
   if (which & 1) {
     const int n_tokens = (int)(a.B * a.S);
     hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3((unsigned)(n_tokens * n_hblk)), dim3(NW * 64), 0, st,
