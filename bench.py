@@ -40,7 +40,7 @@ KERNELS = ("fwd", "bwd_preprocess", "bwd_dq", "bwd_dkv_prepare", "bwd_dkv_partia
 # single-kernel steps: rocprofv3 kernel name prefix, source files, algorithmic flops per valid pair / (H*D)
 SINGLE = {
     "fwd": ("smqa::fwd_", ("fwd.hip", "device_common.h"), 4),  # fwd_ws_kernel at H=64k D=512
-    "bwd_dq": ("smqa::bwd_dq_kernel", ("bwd.hip", "device_common.h"), 6),
+    "bwd_dq": ("smqa::bwd_dq_", ("bwd.hip", "device_common.h"), 6),  # _ws_kernel at H=64k D=512
     "bwd_dkv_partials": ("smqa::bwd_dkv_", ("bwd.hip", "device_common.h"), 8),  # _ws_kernel at H=64 D=512
 }
 CALIB_BYTES = 1 << 30        # the calibration copy reads and writes this many bytes
