@@ -313,6 +313,16 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
 // finished with. Both roles pass the same barriers (one before the stages, nblk + 1 stages, one
 // before the epilogue). A SIMD thus overlaps one role's gather issue, softmax and LDS traffic
 // with the other's MFMAs; with one wave per SIMD (fwd_kernel) they run one after another.
+// Maximum over lanes l, l ^ 16, l ^ 32 and l ^ 48, with the two lane-swap instructions (no LDS
+// round trip): a 16-lane swap leaves a lane holding its own value and that of l ^ 16, a 32-lane
+// swap then pairs l with l ^ 32.
+__device__ __forceinline__ float max_xor16_32(float m) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
 __device__ __forceinline__ int fws_swz(int row) {
   const int r = row & 15;
   return ((r & 1) << 2) ^ (r & 10) ^ (((r >> 2) & 1) * 9);
@@ -465,8 +475,7 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
               sv[4 * mt + r] = v;
               bmax = fmaxf(bmax, v);
             }
-          bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-          bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+          bmax = max_xor16_32(bmax);
           // the running max only moves when the block exceeds it by more than 8, so P <= 2^8 and
           // the O rescale runs on few blocks; O / l and m + log2(l) do not depend on where it sits
           const float m_new = (bmax > m_run + 8.f) ? bmax : m_run;  // bmax is finite: a slot is valid
