@@ -54,7 +54,8 @@ enum {
   SMQA_OK = 0,
   SMQA_ERR_NULL = 1,        /* a required pointer is NULL */
   SMQA_ERR_SHAPE = 2,       /* a size is <= 0 or beyond a stated limit */
-  SMQA_ERR_UNSUPPORTED = 3, /* (H, D) has no compiled kernel */
+  SMQA_ERR_UNSUPPORTED = 3, /* (H, D) has no compiled kernel, or one batch's kv rows
+                               (S_kv * D * 2 bytes) reach 4 GiB */
   SMQA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
   SMQA_ERR_ALIAS = 5,       /* an output overlaps an input or another output */
   SMQA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than sparse_mqa_bwd_workspace_bytes */

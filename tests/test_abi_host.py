@@ -69,6 +69,10 @@ def test_fwd_validation(lib):
     assert fwd(lib, H=256, o=A) == ALIAS  # a supported head count: validation reaches the alias check
     assert fwd(lib, H=1024, S=2 ** 24) == SHAPE  # 2^24 tokens x 16 head blocks > 2^28 workgroups
     assert fwd(lib, D=96) == UNSUP
+    # one batch's kv rows are gathered through a 32-bit byte range: 4 GiB and above are refused
+    assert fwd(lib, S_kv=(1 << 22) - 1) not in (UNSUP, SHAPE)
+    assert fwd(lib, S_kv=1 << 22) == UNSUP
+    assert fwd(lib, S_kv=1 << 25, D=64, H=16) == UNSUP
     assert fwd(lib, D=1024) == UNSUP
     assert fwd(lib, H=64, D=128, o=A) == ALIAS  # D = 128 and 256 are supported
     assert fwd(lib, H=64, D=64) == UNSUP

@@ -50,6 +50,8 @@ int check_shapes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64
   if (tokens < 0 || !mul_ok(tokens, H > 64 ? H / 64 : 1, &wgs) || wgs > (int64_t)INT32_MAX / 8) return SMQA_ERR_SHAPE;
   if (count({B, S, H, D}) < 0 || count({B, S_kv, D}) < 0 || count({B, S, topk}) < 0) return SMQA_ERR_SHAPE;
   if (!supported(H, D)) return SMQA_ERR_UNSUPPORTED;
+  // the tile gathers address one batch's kv rows through a 32-bit byte range
+  if (S_kv * D * 2 > (int64_t)UINT32_MAX) return SMQA_ERR_UNSUPPORTED;
   return SMQA_OK;
 }
 

@@ -168,7 +168,7 @@ struct BwdGather {
   __amdgpu_buffer_rsrc_t rk, rz;  // kv rows of this batch; the zero row (masked slots)
 
   __device__ __forceinline__ BwdGather(const char* kv_b_, int64_t S_kv)
-      : kv_b(kv_b_), rk(make_rsrc(kv_b_, (int)(S_kv * C::ROWB))), rz(make_rsrc(g_zero_row_bwd, C::ROWB)) {}
+      : kv_b(kv_b_), rk(make_rsrc(kv_b_, (int)(uint32_t)(S_kv * C::ROWB))), rz(make_rsrc(g_zero_row_bwd, C::ROWB)) {}
 
   // part k of this wave's share of the tile whose slots' indices sit in my_idx (lane t = slot t)
   __device__ __forceinline__ void part(int k, int32_t my_idx, uint64_t mask, char* tile, int lane, int wu) const {
@@ -437,7 +437,7 @@ bwd_dq_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv
   // transposing reads expect. Only the dQ waves gather: the score waves' 64 MFMAs per block make
   // them the longer role, and gathering from their score loop cost ~10%.
   const char* kv_b = (const char*)(kv + b * S_kv * D);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv_b, (int)(S_kv * ROWB));
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv_b, (int)(uint32_t)(S_kv * ROWB));
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(g_zero_row_bwd, ROWB);
   auto gpart = [&](int k, int32_t my_idx, uint64_t mask, char* tile) {
     const int r = (wu - 4) + 4 * k;

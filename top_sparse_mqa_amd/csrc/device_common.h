@@ -61,7 +61,9 @@ __device__ __forceinline__ bf16x8 join_tr(s16x4 lo, s16x4 hi) {
 __device__ __forceinline__ void dma16(const void* gsrc, char* lds_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (SMQA_LDS void*)(SMQA_LDS char*)lds_base, 16, 0, 0);
 }
-// Buffer resource over [base, base + bytes) for raw (unswizzled, stride 0) buffer loads.
+// Buffer resource over [base, base + bytes) for raw (unswizzled, stride 0) buffer loads. The
+// record count is an unsigned 32-bit field: `bytes` carries its bit pattern, so a range must stay
+// below 4 GiB (the library refuses kv tensors whose rows of one batch reach that).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }

@@ -105,7 +105,7 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
       // wave-uniform, the row offset goes in the scalar offset; masked rows read the zero row.
       // The lane id is passed through an empty asm so the per-row lane offsets are computed
       // here instead of being hoisted out of the block loop into 16 live registers.
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv_b, (int)(S_kv * ROWB));
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv_b, (int)(uint32_t)(S_kv * ROWB));
       const __amdgpu_buffer_rsrc_t rz = make_rsrc(g_zero_row, ROWB);
       int ln = lane;
       asm volatile("" : "+v"(ln));
@@ -374,7 +374,7 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
   // role during that stage, so the O waves issue their parts at once and the score waves spread
   // theirs over the score loop.
   const char* kv_b = (const char*)(kv + b * S_kv * D);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv_b, (int)(S_kv * ROWB));
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv_b, (int)(uint32_t)(S_kv * ROWB));
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(g_zero_row, ROWB);
   auto gpart = [&](int k, int32_t my_idx, uint64_t mask, char* tile) {
     const int r = wu + 8 * k;
