@@ -1502,8 +1502,9 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 
 // One workgroup per (word column w0, tile of MARK_ROWS kv rows): the 32 tokens w0 + nw j of the
 // column own every word of the column, so the workgroup builds the tile's words in LDS (LDS
-// atomics) and writes them out with plain stores.
-constexpr int MARK_ROWS = 8192;
+// atomics) and writes them out with plain stores. 32 KiB of LDS lets a workgroup sit beside a
+// forward or dQ workgroup (~111 KiB) on one CU when the plan runs on a side stream.
+constexpr int MARK_ROWS = 4096;
 
 __global__ void __launch_bounds__(256)
 mark_kernel(const int32_t* __restrict__ idx, int2* __restrict__ bc, int64_t token0, int64_t n_chunk, int64_t S,
