@@ -1665,6 +1665,17 @@ reduce_rows_kernel(const uint16_t* __restrict__ stage, const int8_t* __restrict_
   const int seg = 8 * c * nseg / D;  // exponent segment of this thread's 8 values
   auto lde = [&](int32_t i) { return (int)stage_exp[(int64_t)i * nseg + seg]; };
   int32_t i = beg + g;
+  // eight rows in flight per thread, then four, then one (the order of the sums stays row order)
+  for (; i + 7 * NG < end; i += 8 * NG) {
+    i32x4 r[8];
+    int e[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) r[k] = ld(i + k * NG);
+#pragma unroll
+    for (int k = 0; k < 8; k++) e[k] = lde(i + k * NG);
+#pragma unroll
+    for (int k = 0; k < 8; k++) add(r[k], e[k]);
+  }
   for (; i + 3 * NG < end; i += 4 * NG) {
     const i32x4 r0 = ld(i), r1 = ld(i + NG), r2 = ld(i + 2 * NG), r3 = ld(i + 3 * NG);
     const int e0 = lde(i), e1 = lde(i + NG), e2 = lde(i + 2 * NG), e3 = lde(i + 3 * NG);
