@@ -104,6 +104,8 @@ EDGE = [
     ("h16_d512_k1", 1, 7, 40, 16, 512, 1),
     ("h32_d64_k200_dups", 1, 11, 100, 32, 64, 200),
     ("h64_d512_k33", 1, 5, 33, 64, 512, 33),
+    ("h64_d512_k5", 1, 3, 20, 64, 512, 5),     # one partial block through the specialised kernels
+    ("h64_d512_k1", 2, 3, 10, 64, 512, 1),
     ("h192_d512_k70", 1, 4, 90, 192, 512, 70),
     ("h256_d512_k40", 2, 3, 50, 256, 512, 40),
     ("h64_d256_k50", 1, 6, 80, 64, 256, 50),
