@@ -1,6 +1,6 @@
 // Forward kernels of top-k sparse MQA for gfx950 (see include/sparse_mqa.h for the contract).
-// fwd_ws_kernel (below) serves D = 512 with blocks of 64 heads and default rounding; fwd_kernel
-// serves every other shape and reference_rounding.
+// fwd_ws_kernel (below) serves D = 512 with blocks of 64 heads; fwd_kernel serves every other
+// shape.
 //
 // One workgroup per (query token, block of up to 64 heads). All heads of a token share the
 // gathered kv rows, so each block of 64 slots is gathered once into LDS (direct-to-LDS
@@ -300,8 +300,9 @@ fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, cons
 }
 
 // ---------------------------------------------------------------------------------------------
-// Forward with specialised waves, for D = 512 and blocks of 64 heads (default rounding): eight
-// waves, two per SIMD, in two roles.
+// Forward with specialised waves, for D = 512 and blocks of 64 heads: eight waves, two per SIMD,
+// in two roles. RR as in fwd_kernel (scores in natural units, the max subtracted before the change
+// to base 2).
 //   Score waves (0-3) gather the 32-slot kv tiles (one 1 KiB row per direct-to-LDS instruction)
 //   and compute S^T for 16 heads each (16x16x32 MFMAs, Q in AGPRs), then the online softmax
 //   (running max and sum per head, sink included) and hand P (bf16, [head][slot]) and each head's
@@ -328,7 +329,7 @@ __device__ __forceinline__ int fws_swz(int row) {
   return ((r & 1) << 2) ^ (r & 10) ^ (((r >> 2) & 1) * 9);
 }
 
-template <int D>
+template <int D, bool RR>
 __global__ void __launch_bounds__(512)
 fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const float* __restrict__ sink,
               const int32_t* __restrict__ idx, uint16_t* __restrict__ out, float* __restrict__ lse, int S,
@@ -345,6 +346,9 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
   constexpr int DW = D / 4;       // O^T d-columns per O wave
   constexpr int NDT = DW / 32;    // its 32-wide d tiles
   constexpr int PB = HB * T * 2;  // bytes of one P buffer
+  // EU turns a difference of scores into log2 units; MAXSTEP is 8 in log2 units.
+  constexpr float EU = RR ? kLog2e : 1.f;
+  constexpr float MAXSTEP = RR ? 8.f * 0.693147180559945309f : 8.f;
   static_assert(ROWB == 1024 && NDT * 32 == DW, "one kv row per gather instruction");
   __shared__ __attribute__((aligned(16))) char tile0[TB];
   __shared__ __attribute__((aligned(16))) char tile1[TB];
@@ -406,7 +410,7 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
 #pragma unroll
       for (int ks = 0; ks < KS; ks++) qb[ks] = load_bf16x8(qrow + 32 * ks);
     }
-    const float sink2 = sink[head] * kLog2e;
+    const float sink2 = RR ? sink[head] : sink[head] * kLog2e;
     float m_run = sink2;
     // the sink's share of the denominator is carried by the g == 0 lane of each head
     float l_run = (g == 0 && sink2 != -INFINITY) ? 1.f : 0.f;
@@ -463,7 +467,8 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
             if constexpr (i % (NF / NP) == NF / NP / 2) gpart(i / (NF / NP), idx_g, mask_g, nxt);
           });
           __builtin_amdgcn_sched_barrier(0);
-          // online softmax in log2 units; this lane holds head hrow, slots 16 mt + 4 g + r
+          // online softmax (log2 units, or natural units under RR); this lane holds head hrow,
+          // slots 16 mt + 4 g + r
           const uint32_t vb = (uint32_t)(mask >> (4 * g));
           float sv[8];
           float bmax = -INFINITY;
@@ -478,14 +483,14 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
           bmax = max_xor16_32(bmax);
           // the running max only moves when the block exceeds it by more than 8, so P <= 2^8 and
           // the O rescale runs on few blocks; O / l and m + log2(l) do not depend on where it sits
-          const float m_new = (bmax > m_run + 8.f) ? bmax : m_run;  // bmax is finite: a slot is valid
-          const float alpha = fast_exp2(m_run - m_new);
+          const float m_new = (bmax > m_run + MAXSTEP) ? bmax : m_run;  // bmax is finite: a slot is valid
+          const float alpha = fast_exp2((m_run - m_new) * EU);
           m_run = m_new;
           float ps = 0.f;
           float p[8];
 #pragma unroll
           for (int k = 0; k < 8; k++) {
-            p[k] = fast_exp2(sv[k] - m_new);
+            p[k] = fast_exp2((sv[k] - m_new) * EU);
             ps += p[k];
           }
           l_run = l_run * alpha + ps;
@@ -512,7 +517,7 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
     const float ltot = l1 + __shfl_xor(l1, 32);
     if (g == 0) {
       fin_l[hrow] = ltot;
-      lse[token * H + head] = ltot > 0.f ? m_run + log2f(ltot) : -INFINITY;
+      lse[token * H + head] = ltot > 0.f ? (RR ? (m_run + logf(ltot)) * kLog2e : m_run + log2f(ltot)) : -INFINITY;
     }
     __syncthreads();  // the denominators are in LDS
   } else {
@@ -634,17 +639,15 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
 
 template <bool RR>
 static hipError_t launch_fwd_rr(const FwdArgs& a, hipStream_t st) {
-  if constexpr (!RR) {
-    if (a.D == 512 && a.H % 64 == 0) {  // blocks of 64 heads: the specialised-wave kernel
-      const int n_hblk = (int)(a.H / 64);
-      const int n_tokens = (int)(a.B * a.S);
-      hipLaunchKernelGGL((fwd_ws_kernel<512>), dim3((unsigned)(n_tokens * n_hblk)), dim3(512), 0, st,
-                         (const uint16_t*)a.q, (const uint16_t*)a.kv, a.sink, a.idx, (uint16_t*)a.o, a.lse, (int)a.S,
-                         a.S_kv, (int)a.H, (int)a.topk, a.sm_scale * kLog2e, n_hblk, n_tokens);
-      return hipGetLastError();
-    }
+  if (a.D == 512 && a.H % 64 == 0) {  // blocks of 64 heads: the specialised-wave kernel
+    const int n_hblk = (int)(a.H / 64);
+    const int n_tokens = (int)(a.B * a.S);
+    hipLaunchKernelGGL((fwd_ws_kernel<512, RR>), dim3((unsigned)(n_tokens * n_hblk)), dim3(512), 0, st,
+                       (const uint16_t*)a.q, (const uint16_t*)a.kv, a.sink, a.idx, (uint16_t*)a.o, a.lse, (int)a.S,
+                       a.S_kv, (int)a.H, (int)a.topk, RR ? a.sm_scale : a.sm_scale * kLog2e, n_hblk, n_tokens);
+    return hipGetLastError();
   }
-  if (a.D == 512) return a.H <= 32 ? launch_fwd_t<512, 1, RR>(a, st) : launch_fwd_t<512, 2, RR>(a, st);
+  if (a.D == 512) return a.H <= 32 ? launch_fwd_t<512, 1, RR>(a, st) : hipErrorInvalidValue;
   if (a.D == 256) return a.H <= 32 ? launch_fwd_t<256, 1, RR>(a, st) : launch_fwd_t<256, 2, RR>(a, st);
   if (a.D == 128) return a.H <= 32 ? launch_fwd_t<128, 1, RR>(a, st) : launch_fwd_t<128, 2, RR>(a, st);
   if (a.D == 64) return a.H <= 32 ? launch_fwd_t<64, 1, RR>(a, st) : hipErrorInvalidValue;
