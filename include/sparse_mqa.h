@@ -132,7 +132,8 @@ int sparse_mqa_bwd_dkv(const void* q, const void* kv, const void* d_o, const int
  * token (at least sparse_mqa_bwd_workspace_bytes minus Delta's bytes; SMQA_ERR_WORKSPACE otherwise)
  * and must run in this order with the same workspace and sizes:
  *   prepare   marks every valid (token, kv row) pair in a bitmap and gives each valid slot its
- *             staging row: a kv row's rows are contiguous and ordered by token;
+ *             staging row: a kv row's rows are contiguous, in an order fixed by the
+ *             token indices;
  *   partials  computes every valid slot's dKV contribution row into the staging rows;
  *   reduce    sums each kv row's staging rows and writes dkv (bf16, or fp32 if dkv_fp32).
  * prepare reads only topk_idxs, so it may run on another stream, e.g. beside the forward, as

@@ -528,3 +528,62 @@ def test_gather_b4_masked_sampled(gpu_lib):
     o, lse, dkv32 = end_to_end_sampled(w, x, toks, rows)
     ref_rows = referenced_rows(x["topk_idxs"], w.S_kv).view(-1)
     assert torch.count_nonzero(dkv32.view(-1, w.D).cpu()[~ref_rows]) == 0
+
+
+def _plan_arrays(steps, w):
+    """pos [tokens, topk] and offset [words + 1] read back from a one-pass dKV workspace, at the
+    byte offsets of the documented layout (kv row norms, plan words, offsets, scan tiles, pos)."""
+    r256 = lambda n: (n + 255) // 256 * 256
+    n_rows, tokens = w.B * w.S_kv, w.B * w.S
+    nw = (tokens + 31) // 32
+    words = n_rows * nw
+    o_off = r256(n_rows * 4) + r256((3 * words + 4) * 4)
+    o_pos = o_off + r256((words + 1) * 4) + r256(((words + 4095) // 4096) * 4)
+    ws = steps.workspace.cpu()
+    offset = ws[o_off:o_off + (words + 1) * 4].view(torch.int32).clone()
+    pos = ws[o_pos:o_pos + tokens * w.topk * 4].view(torch.int32).view(tokens, w.topk).clone()
+    return pos, offset, nw
+
+
+@pytest.mark.parametrize("case", ["distinct", "duplicates"])
+def test_staging_plan_structure(gpu_lib, case):
+    """The dKV staging plan as the prepare step leaves it in the workspace: every valid (token,
+    slot) pair owns n_hblk consecutive staging rows, the pairs of a kv row fill that row's segment
+    [offset[r nw], offset[(r + 1) nw]) exactly, masked slots get -1, and (distinct indices) the
+    order inside a segment is (token mod nw, token div nw), independent of timing."""
+    if case == "distinct":
+        w = syn.WORKLOADS["mid_h64_d512_k300"]
+        x = syn.workload_inputs(w)
+        n_hblk = 1
+    else:  # random indices with repeats and out-of-range values, two 64-head blocks
+        w = syn.Workload("plan_dups", 2, 40, 70, 128, 512, 90, "causal_distinct", 0, 0)
+        g = torch.Generator().manual_seed(77)
+        x = {"q": torch.randn(w.B, w.S, w.H, w.D, generator=g).to(torch.bfloat16),
+             "kv": torch.randn(w.B, w.S_kv, w.D, generator=g).to(torch.bfloat16),
+             "do": torch.randn(w.B, w.S, w.H, w.D, generator=g).to(torch.bfloat16),
+             "topk_idxs": torch.randint(-3, w.S_kv + 3, (w.B, w.S, w.topk), generator=g).to(torch.int32)}
+        n_hblk = 2
+    say("case", "staging plan", case)
+    xg = gpu({k: x[k] for k in ("q", "kv", "do", "topk_idxs")})
+    lse = torch.zeros(w.B, w.S, w.H, device="cuda")
+    delta = torch.zeros(w.B, w.S, w.H, device="cuda")
+    steps = smqa.DkvSteps(xg["q"], xg["kv"], xg["do"], xg["topk_idxs"], lse, delta)
+    steps.prepare()
+    torch.cuda.synchronize()
+    pos, offset, nw = _plan_arrays(steps, w)
+    idx = x["topk_idxs"].view(w.B * w.S, w.topk).long()
+    valid = (idx >= 0) & (idx < w.S_kv)
+    assert torch.equal(pos[~valid], torch.full_like(pos[~valid], -1))
+    p = pos[valid].long()
+    n_pairs = int(valid.sum())
+    assert int(offset[-1]) == n_hblk * n_pairs
+    assert torch.equal(torch.sort(p).values, n_hblk * torch.arange(n_pairs))  # each pair n_hblk rows, no overlap
+    ct = torch.arange(w.B * w.S).view(-1, 1).expand_as(idx)
+    row = (ct // w.S) * w.S_kv + idx.clamp(0, w.S_kv - 1)
+    r, t = row[valid], ct[valid]
+    assert bool((p >= offset[r * nw].long()).all()) and bool((p < offset[(r + 1) * nw].long()).all())
+    if case == "distinct":
+        # inside a row's segment the pairs follow (token mod nw, token div nw)
+        key = r * (32 * nw) + (t % nw) * 32 + t // nw
+        order = torch.argsort(p)
+        assert bool((key[order][1:] > key[order][:-1]).all())

@@ -1484,7 +1484,8 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 
 // ---------------------------------------------------------------------------------------------
 // Segmented scatter-add of dKV. Every valid (token, slot) pair gets n_hblk consecutive rows of a
-// staging buffer, grouped by kv row and, within a row, ordered by token. The dKV kernel stores each
+// staging buffer, grouped by kv row and, within a row, in an order fixed by the token indices
+// (token ct sorts by (ct % nw, ct / nw), nw below). The dKV kernel stores each
 // contribution row there with plain stores, and reduce_rows sums each kv row's segment in that
 // order. This moves the payload through the store and streaming-read paths instead of the fp32
 // atomic units, and the result does not depend on the order in which workgroups run.
