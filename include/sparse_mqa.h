@@ -32,7 +32,8 @@
  *   LSE, Delta   : [B, S, H] fp32          dKV accumulator: [B, S_kv, D] fp32
  * Supported (H, D): D in {128, 256, 512} with H in {16, 32} or any multiple of 64 up to 1024; D = 64 with H in
  * {16, 32}.
- * 1 <= topk <= 2^30, S_kv <= 2^31 - 1, B*S*max(1, H/64) <= 2^28.
+ * 1 <= topk <= 2^30, S_kv <= 2^31 - 1, B*S*max(1, H/64) < 2^23 (one workgroup of up to 512
+ * threads per token and block of 64 heads, and a launch holds fewer than 2^32 threads).
  * Pointers to bf16 tensors (q, kv, O, dO, dQ, dKV), the fp32 dKV accumulator and the workspace
  * must be 16-byte aligned; fp32 vectors (attn_sink, LSE, Delta) and topk_idxs 4-byte aligned.
  * Outputs must not overlap inputs or each other (SMQA_ERR_ALIAS).
@@ -78,8 +79,9 @@ int sparse_mqa_fwd(const void* q, const void* kv, const float* attn_sink, const 
  * dKV product as a scaled fp16 operand), the staging plan (one bit per kv row and token of a
  * chunk, with pair counts and scanned offsets), and the staging rows of the
  * segmented dKV scatter-add (one row per valid (token, slot) pair and 64-head block, and one spare
- * row per token and head block that absorbs the stores of masked slots; a row is D fp16 values
- * with one power-of-two exponent per segment of up to 128 values, summed in fp32).
+ * row per token and head block that absorbs the stores of masked slots; a row is D int16 values
+ * with one power-of-two exponent per segment of up to 128 values -- block floating point -- summed
+ * in fp32).
  * sparse_mqa_bwd_workspace_bytes is the size for one pass over all tokens (an upper bound that
  * assumes every slot valid); any size >= sparse_mqa_bwd_workspace_min_bytes also works, and the
  * tokens are then processed in chunks with an fp32 running sum. Both return 0 for invalid sizes. */
@@ -95,7 +97,13 @@ size_t sparse_mqa_bwd_workspace_min_bytes(int64_t B, int64_t S, int64_t S_kv, in
  * valid slot references come out exactly 0. attn_sink is accepted for the documented signature;
  * the LSE already includes the sink, so dQ and dKV do not read it. Results are bitwise
  * reproducible from call to call as long as no token lists a kv row twice (top-k selections never
- * do): nothing in the staged path depends on the order in which workgroups run. */
+ * do): nothing in the staged path depends on the order in which workgroups run.
+ * Precondition on lse (as the bwd page's parameter list implies, it is the forward's output for
+ * the same q, kv, attn_sink, topk_idxs and sm_scale): lse[b,s,h] must be at least log2 of the
+ * head's softmax denominator, so that every P_t <= 1. The dKV kernels size the fixed-point range of
+ * their fp16 dS operand from that (and from Delta and the kv row norms); a smaller lse makes P
+ * exceed 1, and dS values beyond the range are then saturated (wrong dKV, status still SMQA_OK).
+ * o enters only through Delta and may be any bf16 tensor. */
 int sparse_mqa_bwd(const void* q, const void* kv, const float* attn_sink, const void* o,
                    const void* d_o, const int32_t* topk_idxs, const float* lse, void* dq, void* dkv,
                    int dkv_fp32, void* workspace, size_t workspace_bytes, int64_t B, int64_t S,
@@ -151,10 +159,12 @@ int sparse_mqa_bwd_dkv_reduce(void* dkv, int dkv_fp32, void* workspace, size_t w
                               int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk,
                               void* stream);
 
-/* Stage, workspace-free variant of the main backward: writes dq and adds every valid slot's dKV
- * contribution into dkv_accum [B,S_kv,D] fp32 with fp32 atomic adds. dkv_accum must be zeroed by
- * the caller first; rows no slot references are untouched. Slower than the staged path on MI355X
- * (the fp32 atomic rate bounds it) but needs no staging memory. */
+/* Stage, workspace-free variant of the main backward (bwd page, bwd factory: its fp32 accumulator
+ * [B,S_kv,D], accum_dtype, that the postprocess factory then converts): writes dq and adds every
+ * valid slot's dKV contribution into dkv_accum [B,S_kv,D] fp32 with fp32 atomic adds. dkv_accum
+ * must be zeroed by the caller first; rows no slot references are untouched. Slower than the staged
+ * path on MI355X (the fp32 atomic rate bounds it) but needs no staging memory. The order of the
+ * atomic adds, and so the last bits of dkv_accum, may vary from call to call. */
 int sparse_mqa_bwd_main(const void* q, const void* kv, const void* d_o, const int32_t* topk_idxs,
                         const float* lse, const float* delta, void* dq, float* dkv_accum, int64_t B,
                         int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale,

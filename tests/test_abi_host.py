@@ -25,11 +25,35 @@ G = 0x70000000
 NAN = float("nan")
 
 
+# entry points that take only sizes (no device pointers, nothing enqueued)
+QUERIES = {"sparse_mqa_bwd_workspace_bytes", "sparse_mqa_bwd_workspace_min_bytes", "sparse_mqa_status_string"}
+
+
+class ValidationOnly:
+    """The library as these tests may use it: every call that takes device pointers must be
+    rejected by validation. A status of OK or SMQA_ERR_HIP would mean kernels were (or were tried
+    to be) enqueued on the fake addresses above, which on a GPU host could fault the device."""
+
+    def __init__(self, lib):
+        self._lib = lib
+
+    def __getattr__(self, name):
+        fn = getattr(self._lib, name)
+        if name in QUERIES or not name.startswith("sparse_mqa_"):
+            return fn
+
+        def checked(*args):
+            st = fn(*args)
+            assert st not in (OK, HIP), f"{name} passed validation in a host test (status {st})"
+            return st
+        return checked
+
+
 @pytest.fixture(scope="module")
 def lib():
     if not smqa.LIB_PATH.exists():
         pytest.fail("libsparse_mqa.so is not built (python -m top_sparse_mqa_amd.build)")
-    return smqa.load_library()
+    return ValidationOnly(smqa.load_library())
 
 
 def declared_functions():
@@ -67,10 +91,13 @@ def test_fwd_validation(lib):
     assert fwd(lib, H=96) == UNSUP
     assert fwd(lib, H=1088) == UNSUP
     assert fwd(lib, H=256, o=A) == ALIAS  # a supported head count: validation reaches the alias check
-    assert fwd(lib, H=1024, S=2 ** 24) == SHAPE  # 2^24 tokens x 16 head blocks > 2^28 workgroups
+    assert fwd(lib, H=1024, S=2 ** 19) == SHAPE  # 2^19 tokens x 16 head blocks = 2^23 workgroups
+    assert fwd(lib, H=1024, S=2 ** 19 - 1, o=A) == ALIAS  # one token fewer: below the limit
+    assert fwd(lib, H=64, S=2 ** 23) == SHAPE  # 2^23 workgroups of 512 threads = 2^32 threads
     assert fwd(lib, D=96) == UNSUP
     # one batch's kv rows are gathered through a 32-bit byte range: 4 GiB and above are refused
-    assert fwd(lib, S_kv=(1 << 22) - 1) not in (UNSUP, SHAPE)
+    # just below the limit: validation reaches the alias check (kv's 4 GiB then covers o)
+    assert fwd(lib, S_kv=(1 << 22) - 1) == ALIAS
     assert fwd(lib, S_kv=1 << 22) == UNSUP
     assert fwd(lib, S_kv=1 << 25, D=64, H=16) == UNSUP
     assert fwd(lib, D=1024) == UNSUP
@@ -95,7 +122,7 @@ def dkv_layout_bytes(B, S_kv, H, D, K, chunk, acc):
     16-byte pieces), the scanned offsets (+ total),
     the scan's tile sums, the fp32 accumulator when chunked with bf16 output, the slots' positions,
     and the staging rows (one per slot and 64-head block plus one spare per token and head block; a
-    row is D fp16 values and one int8 exponent per segment of min(128, D / (heads per workgroup /
+    row is D int16 values and one int8 exponent per segment of min(128, D / (heads per workgroup /
     16)) values)."""
     n_rows = B * S_kv
     words = n_rows * ((chunk + 31) // 32)
@@ -136,10 +163,13 @@ def test_bwd_validation(lib):
     assert bwd(lib, ws=None) == WORKSPACE
     assert bwd(lib, wsb=100) == WORKSPACE
     low = lib.sparse_mqa_bwd_workspace_min_bytes(1, 8, 16, 64, 512, 4)
-    # the minimum passes validation (the launch then fails without a GPU); one token's staging
-    # (positions + 5 rows of 512 fp16 values and 4 exponents) less does not
-    assert bwd(lib, wsb=low, ws=0x7A000000) not in (WORKSPACE, ALIAS, ALIGN, NULL)
-    assert bwd(lib, wsb=low - (4 * 4 + 5 * (1024 + 4)), ws=0x7A000000) == WORKSPACE
+    # The minimum passes the workspace check; one token's staging (positions + 5 rows of 512 int16
+    # values and 4 exponents) less does not. The alias check runs after the workspace check, so
+    # an output overlap stops both calls before anything is enqueued (no call here reaches a launch,
+    # with or without a GPU).
+    overlapping_dkv = 0x71000000 + 64
+    assert bwd(lib, wsb=low, ws=0x7A000000, dkv=overlapping_dkv) == ALIAS
+    assert bwd(lib, wsb=low - (4 * 4 + 5 * (1024 + 4)), ws=0x7A000000, dkv=overlapping_dkv) == WORKSPACE
     assert bwd(lib, ws=G + 4) == ALIGN
     assert bwd(lib, dq=A) == ALIAS
     assert bwd(lib, dkv=0x71000000 + 64) == ALIAS

@@ -35,32 +35,25 @@ def test_autograd_grads_match_oracle(gpu_lib, name):
     o_ref, lse_ref = oracle.fwd(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"])
     check_bf16("O", o.detach().view(-1, H, D), o_ref)
     check_lse("LSE", lse.view(-1, H), lse_ref)
-    ob = o_ref.view(w.B, w.S, H, D).to(torch.bfloat16)
-    lb = lse_ref.view(w.B, w.S, H)
+    # The backward autograd ran received the GPU forward's O (bf16) and LSE; the oracle's backward
+    # is evaluated on exactly those. (Fed the oracle's own forward instead, the two backwards differ
+    # through Delta = <O, dO>: where attention is peaked, |O| reaches 2-4 and one bf16 ulp of O
+    # there moves Delta, and the dKV of the rows those tokens pick, by up to ~0.1 -- a difference
+    # of inputs, not of the kernels.)
+    ob = o.detach().cpu()
+    lb = lse.detach().cpu()
     dq_ref, _ = oracle.dq(x["q"], x["kv"], ob, x["do"], x["topk_idxs"], lb)
     dkv_ref = oracle.dkv(x["q"], x["kv"], ob, x["do"], x["topk_idxs"], lb)
     check_bf16("dQ", q.grad.view(-1, H, D), dq_ref)
-    # End to end, the backward's Delta comes from the GPU's forward O, which differs from the
-    # oracle's by up to one bf16 ulp per element; a kv row that many (token, head) pairs reference
-    # sums those differences, so the elementwise bar (met by the dKV kernel on identical inputs in
-    # the parity tests) is applied where it is meaningful here, the small case, and the relative
-    # L2 gate everywhere.
-    if w.S <= 128:
-        check_bf16("dKV", kv.grad.view(-1, D), dkv_ref)
-    else:
-        g, r = kv.grad.double().cpu().view(-1, D), dkv_ref.double()
-        rel = float((g - r).norm() / r.norm())
-        say(f"  dKV end to end: rel-L2 {rel:.3e}")
-        assert rel <= 1e-2
+    check_bf16("dKV", kv.grad.view(-1, D), dkv_ref)
     check_dsink("d_sink", sink.grad, oracle.dsink(ob, x["do"], lb, x["attn_sink"]), ob, x["do"], lb,
-                x["attn_sink"], rel=1e-2)
-    # the wrapper routes the interface's results: same dQ and d_sink bit for bit on the same O
-    # and LSE, and dKV up to the summation order of its fp32 reduction
+                x["attn_sink"])
+    # the wrapper routes the interface's results: dQ, dKV and d_sink bit for bit on the same O and
+    # LSE (the staged backward sums in an order fixed by the indices)
     dq2, dkv2, ds2 = smqa.sparse_mqa_bwd_interface(q.detach(), kv.detach(), sink.detach(), o.detach(),
                                                    x["do"].cuda(), idx, lse, return_d_sink=True)
     torch.cuda.synchronize()
-    assert torch.equal(dq2, q.grad) and torch.equal(ds2, sink.grad)
-    torch.testing.assert_close(dkv2.float(), kv.grad.float(), rtol=1e-2, atol=1e-2)
+    assert torch.equal(dq2, q.grad) and torch.equal(ds2, sink.grad) and torch.equal(dkv2, kv.grad)
 
 
 def test_autograd_partial_requires_grad(gpu_lib):

@@ -120,6 +120,45 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def check_shapes(q: torch.Tensor, kv: Optional[torch.Tensor] = None, topk_idxs: Optional[torch.Tensor] = None, *,
+                 o: Optional[torch.Tensor] = None, do: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, delta: Optional[torch.Tensor] = None,
+                 attn_sink: Optional[torch.Tensor] = None, dkv_accum: Optional[torch.Tensor] = None) -> None:
+    """Raises ValueError unless the given tensors have the pages' shapes for one (B, S, S_kv, H, D,
+    topk): q, o, do [B,S,H,D]; kv, dkv_accum [B,S_kv,D]; topk_idxs [B,S,topk]; lse, delta [B,S,H];
+    attn_sink [H]; all on q's device. The library trusts the sizes it is given, so every entry point
+    of this binding runs this check before it calls the library."""
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B,S,H,D], got shape {tuple(q.shape)}")
+    B, S, H, D = q.shape
+    given = {"kv": kv, "topk_idxs": topk_idxs, "o": o, "do": do, "lse": lse, "delta": delta,
+             "attn_sink": attn_sink, "dkv_accum": dkv_accum}
+    for name, t in given.items():
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    S_kv = None
+    if kv is not None:
+        if kv.dim() != 3 or kv.shape[0] != B or kv.shape[2] != D:
+            raise ValueError(f"kv shape {tuple(kv.shape)} does not match q {tuple(q.shape)} ([B,S_kv,D])")
+        S_kv = kv.shape[1]
+    if topk_idxs is not None and (topk_idxs.dim() != 3 or topk_idxs.shape[0] != B or topk_idxs.shape[1] != S):
+        raise ValueError(f"topk_idxs must be [B,S,topk] = [{B},{S},topk], got {tuple(topk_idxs.shape)}")
+    for name in ("o", "do"):
+        t = given[name]
+        if t is not None and tuple(t.shape) != (B, S, H, D):
+            raise ValueError(f"{name} must have the shape of q {tuple(q.shape)}, got {tuple(t.shape)}")
+    for name in ("lse", "delta"):
+        t = given[name]
+        if t is not None and tuple(t.shape) != (B, S, H):
+            raise ValueError(f"{name} must be [B,S,H] = [{B},{S},{H}], got {tuple(t.shape)}")
+    if attn_sink is not None and tuple(attn_sink.shape) != (H,):
+        raise ValueError(f"attn_sink must be [H] = [{H}], got {tuple(attn_sink.shape)}")
+    if dkv_accum is not None:
+        want = (B, S_kv if S_kv is not None else dkv_accum.shape[1], D)
+        if tuple(dkv_accum.shape) != want:
+            raise ValueError(f"dkv_accum must be [B,S_kv,D] = {list(want)}, got {tuple(dkv_accum.shape)}")
+
+
 def _indices_int32(topk_idxs: torch.Tensor, s_kv: int) -> torch.Tensor:
     """int32 indices for the ABI. int64 input is narrowed after every value outside
     [0, S_kv) is replaced by -1, so narrowing cannot turn a masked index into a valid one."""
@@ -150,14 +189,9 @@ def sparse_mqa_fwd_interface(q: torch.Tensor, kv: torch.Tensor, attn_sink: torch
     _need(q, "q", torch.bfloat16, 4)
     _need(kv, "kv", torch.bfloat16, 3)
     _need(attn_sink, "attn_sink", torch.float32, 1)
+    check_shapes(q, kv, topk_idxs, attn_sink=attn_sink)
     B, S, H, D = q.shape
-    if kv.shape[0] != B or kv.shape[2] != D:
-        raise ValueError(f"kv shape {tuple(kv.shape)} does not match q {tuple(q.shape)}")
     S_kv = kv.shape[1]
-    if attn_sink.shape[0] != H:
-        raise ValueError("attn_sink must have H entries")
-    if topk_idxs.dim() != 3 or topk_idxs.shape[0] != B or topk_idxs.shape[1] != S:
-        raise ValueError(f"topk_idxs must be [B,S,topk], got {tuple(topk_idxs.shape)}")
     idx = _indices_int32(topk_idxs, S_kv)
     topk = idx.shape[2]
     o = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=q.device)
@@ -183,14 +217,9 @@ def sparse_mqa_bwd_interface(q: torch.Tensor, kv: torch.Tensor, attn_sink: torch
     _need(o, "o", torch.bfloat16, 4)
     _need(do, "do", torch.bfloat16, 4)
     _need(lse, "lse", torch.float32, 3)
+    check_shapes(q, kv, topk_idxs, o=o, do=do, lse=lse, attn_sink=attn_sink)
     B, S, H, D = q.shape
     S_kv = kv.shape[1]
-    if o.shape != q.shape or do.shape != q.shape:
-        raise ValueError("o and do must have the shape of q")
-    if tuple(lse.shape) != (B, S, H):
-        raise ValueError("lse must be [B,S,H]")
-    if topk_idxs.dim() != 3 or topk_idxs.shape[0] != B or topk_idxs.shape[1] != S:
-        raise ValueError(f"topk_idxs must be [B,S,topk], got {tuple(topk_idxs.shape)}")
     idx = _indices_int32(topk_idxs, S_kv)
     topk = idx.shape[2]
     lib = load_library()
@@ -215,8 +244,10 @@ def bwd_dsink(lse: torch.Tensor, delta: torch.Tensor, attn_sink: torch.Tensor) -
     _need(delta, "delta", torch.float32, 3)
     _need(attn_sink, "attn_sink", torch.float32, 1)
     B, S, H = lse.shape
-    if tuple(delta.shape) != (B, S, H) or attn_sink.shape[0] != H:
+    if tuple(delta.shape) != (B, S, H) or tuple(attn_sink.shape) != (H,):
         raise ValueError("delta must be [B,S,H] like lse and attn_sink [H]")
+    if delta.device != lse.device or attn_sink.device != lse.device:
+        raise ValueError("lse, delta and attn_sink must be on one device")
     d_sink = torch.empty(H, dtype=torch.float32, device=lse.device)
     _check("sparse_mqa_bwd_dsink", load_library().sparse_mqa_bwd_dsink(
         _ptr(lse), _ptr(delta), _ptr(attn_sink), _ptr(d_sink), B, S, H, _stream()))
@@ -227,6 +258,7 @@ def bwd_preprocess(o: torch.Tensor, do: torch.Tensor) -> torch.Tensor:
     """Delta[b,s,h] = sum_d O*dO (fp32)."""
     _need(o, "o", torch.bfloat16, 4)
     _need(do, "do", torch.bfloat16, 4)
+    check_shapes(o, do=do)
     B, S, H, D = o.shape
     delta = torch.empty((B, S, H), dtype=torch.float32, device=o.device)
     _check("sparse_mqa_bwd_preprocess", load_library().sparse_mqa_bwd_preprocess(
@@ -244,6 +276,7 @@ def bwd_main(q: torch.Tensor, kv: torch.Tensor, do: torch.Tensor, topk_idxs: tor
     _need(lse, "lse", torch.float32, 3)
     _need(delta, "delta", torch.float32, 3)
     _need(dkv_accum, "dkv_accum", torch.float32, 3)
+    check_shapes(q, kv, topk_idxs, do=do, lse=lse, delta=delta, dkv_accum=dkv_accum)
     B, S, H, D = q.shape
     S_kv = kv.shape[1]
     idx = _indices_int32(topk_idxs, S_kv)
@@ -260,6 +293,7 @@ def _main_stage_args(q, kv, do, topk_idxs, lse, delta):
     _need(do, "do", torch.bfloat16, 4)
     _need(lse, "lse", torch.float32, 3)
     _need(delta, "delta", torch.float32, 3)
+    check_shapes(q, kv, topk_idxs, do=do, lse=lse, delta=delta)
     return _indices_int32(topk_idxs, kv.shape[1])
 
 
@@ -268,6 +302,9 @@ def bwd_dq(q: torch.Tensor, kv: torch.Tensor, do: torch.Tensor, topk_idxs: torch
     """dQ kernel of the main backward stage alone."""
     idx = _main_stage_args(q, kv, do, topk_idxs, lse, delta)
     B, S, H, D = q.shape
+    if out is not None:
+        _need(out, "out", torch.bfloat16, 4)
+        check_shapes(q, o=out)
     dq = torch.empty_like(q) if out is None else out
     _check("sparse_mqa_bwd_dq", load_library().sparse_mqa_bwd_dq(
         _ptr(q), _ptr(kv), _ptr(do), _ptr(idx), _ptr(lse), _ptr(delta), _ptr(dq),
@@ -285,6 +322,8 @@ def bwd_dkv(q: torch.Tensor, kv: torch.Tensor, do: torch.Tensor, topk_idxs: torc
     dkv = torch.empty((B, S_kv, D), dtype=torch.float32 if dkv_fp32 else torch.bfloat16, device=q.device)
     if workspace is None:
         workspace = torch.empty(bwd_workspace_bytes(B, S, S_kv, H, D, topk), dtype=torch.uint8, device=q.device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
+        raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
     _check("sparse_mqa_bwd_dkv", load_library().sparse_mqa_bwd_dkv(
         _ptr(q), _ptr(kv), _ptr(do), _ptr(idx), _ptr(lse), _ptr(delta), _ptr(dkv), 1 if dkv_fp32 else 0,
         _ptr(workspace), workspace.numel(), B, S, S_kv, H, D, topk, _scale_arg(sm_scale), _stream()))

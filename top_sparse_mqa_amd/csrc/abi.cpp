@@ -45,9 +45,11 @@ int check_shapes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64
   if (B <= 0 || S <= 0 || S_kv <= 0 || H <= 0 || D <= 0 || topk <= 0) return SMQA_ERR_SHAPE;
   if (S_kv > INT32_MAX || topk > INT32_MAX / 2 || S > INT32_MAX) return SMQA_ERR_SHAPE;
   const int64_t tokens = count({B, S});
-  // workgroup counts (tokens x head blocks) stay below 2^28
+  // One workgroup of up to 512 threads per (token, block of 64 heads): a launch may hold at most
+  // 2^32 - 1 threads, so the workgroup count stays below 2^23. (The per-row and per-element kernels
+  // loop over their work and cap their grids.)
   int64_t wgs = 0;
-  if (tokens < 0 || !mul_ok(tokens, H > 64 ? H / 64 : 1, &wgs) || wgs > (int64_t)INT32_MAX / 8) return SMQA_ERR_SHAPE;
+  if (tokens < 0 || !mul_ok(tokens, H > 64 ? H / 64 : 1, &wgs) || wgs >= ((int64_t)1 << 23)) return SMQA_ERR_SHAPE;
   if (count({B, S, H, D}) < 0 || count({B, S_kv, D}) < 0 || count({B, S, topk}) < 0) return SMQA_ERR_SHAPE;
   if (!supported(H, D)) return SMQA_ERR_UNSUPPORTED;
   // the tile gathers address one batch's kv rows through a 32-bit byte range
@@ -162,8 +164,12 @@ size_t dkv_layout(int64_t B, int64_t S_kv, int64_t H, int64_t D, int64_t topk, i
 bool plan_dkv(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, bool dkv_fp32, size_t base,
               size_t bytes, DkvPlan* p) {
   const int64_t tokens = B * S;
-  // staging row indices are 32-bit
-  const int64_t max_chunk = (int64_t)(INT32_MAX / ((topk + 1) * smqa::bwd_hblocks(H)));
+  // staging row indices are 32-bit; the scan of the bitmap words runs one workgroup per 4096
+  // words, and a launch holds fewer than 2^24 workgroups of 256 threads
+  int64_t max_chunk = (int64_t)(INT32_MAX / ((topk + 1) * smqa::bwd_hblocks(H)));
+  const int64_t max_nw = (((int64_t)1 << 24) - 1) * 4096 / (B * S_kv);
+  if (max_nw < 1) return false;
+  if (max_nw * 32 < max_chunk) max_chunk = max_nw * 32;
   if (tokens <= max_chunk && dkv_layout(B, S_kv, H, D, topk, tokens, false, base, p) <= bytes) return true;
   const bool use_acc = !dkv_fp32;
   if (dkv_layout(B, S_kv, H, D, topk, 1, use_acc, base, p) > bytes) return false;

@@ -9,9 +9,11 @@
 //                scatter-add, below) or a fp32 atomic add into the accumulator. A kv row sums
 //                thousands of heavily cancelling terms, and 8-bit-mantissa coefficients leave
 //                errors of several percent of the result there, so the products run on fp16
-//                operands (11 bits) under per-token power-of-two scales: staged, Q and dS as fp16
-//                (dS's scale bounded by the token's kv row norms, kv_row_norm); atomic, Q stays
-//                bf16 against a hi + lo bf16 pair of dS. P and dO enter as fp16 in both.
+//                operands (11 bits) under per-token power-of-two scales, with dS as a hi + lo
+//                pair (three MFMAs per k-step): staged, Q and dS as fp16 (dS's scale bounded by
+//                the token's kv row norms, kv_row_norm, and Delta); atomic, Q stays bf16 against
+//                a bf16 hi + lo pair of dS. P and dO enter as fp16 in both. Staged rows are int16
+//                block floating point (one exponent per segment of up to 128 values).
 //   bwd_dkv_ws   the staged bwd_dkv at 64 heads per workgroup and D = 512, with specialised
 //                waves: score waves (gather, S^T, dP^T, P, dS) and product waves (dKV^T, staging
 //                stores) share each SIMD, one block apart
@@ -39,21 +41,84 @@ __device__ __forceinline__ int bwd_swz(int row) {
   return ((r & 1) << 2) ^ (r & 10) ^ (((r >> 2) & 1) * 9);
 }
 
-// Staging rows hold D fp16 values plus one int8 exponent per segment of SEG values: value =
-// fp16 * 2^e. Each row segment picks its own exponent: 0 while its largest magnitude m lies in
-// [2^-10, 2^14) -- there fp16 keeps 11 significant bits down to m / 16 and smaller values err by
-// at most 2^-25 -- else the one that brings m to [2^13, 2^14). This halves the traffic of the
-// staged scatter-add against fp32 rows.
-__device__ __forceinline__ int stage_exponent(float m) {
-  if (!(m > 0.f && m <= 3.4028235e38f)) return 0;  // zero, inf or NaN: stored as is
-  if (m >= 0.0009765625f && m < 16384.f) return 0;
-  int e = __builtin_amdgcn_frexp_expf(m) - 14;      // m < 2^(e + 14)
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
 // Maximum of lanes l and l ^ 32 (one cross-half lane swap).
 __device__ __forceinline__ float half_swap_max(float m) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
   return fmaxf(m, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+
+// Staging rows are block floating point: D int16 values plus one int8 exponent per segment of up
+// to 128 values, value = k * 2^e. A segment's exponent puts its largest magnitude m in
+// [2^14, 32767.5), so every value of the segment errs by at most m * 2^-15 after rounding to the
+// nearest integer. Summed over the thousands of rows a kv row collects, this absolute bound per
+// value is what matters: against fp16 values (11 significant bits each) it cuts the error of the
+// sums several-fold at the same 2 bytes per value, half the traffic of fp32 rows.
+//
+// Exponent of a segment whose largest magnitude is m (0 for m = 0): m * 2^-e lies in
+// [2^14, 32767.5), so no value of the segment rounds beyond the int16 range.
+__device__ __forceinline__ int bfp16_exponent(float m) {
+  if (!(m > 0.f && m <= 3.4028235e38f)) return 0;
+  int e = __builtin_amdgcn_frexp_expf(m) - 15;
+  if (__builtin_amdgcn_ldexpf(m, -e) >= 32767.5f) e++;
+  return e;
+}
+// Two values times sc (a power of two) rounded to the nearest integers, as an int16 pair (a in the
+// low half). Adding 1.5 * 2^23 leaves round(x) in the low mantissa bits of the sum for |x| < 2^22,
+// and the fma rounds only once, so this is round-to-nearest-even of a * sc exactly.
+__device__ __forceinline__ uint32_t bfp16_pair(float a, float b, float sc) {
+  constexpr float kRound = 12582912.0f;
+  const uint32_t ia = __float_as_uint(__builtin_fmaf(a, sc, kRound));
+  const uint32_t ib = __float_as_uint(__builtin_fmaf(b, sc, kRound));
+  return __builtin_amdgcn_perm(ib, ia, 0x05040100u);
+}
+// Block-floating-point encoding of one staging-row segment whose values this lane holds in the NT
+// MFMA accumulators c (lanes l and l ^ 32 together hold the segment): picks the exponent from the segment's
+// largest magnitude, pre-scales rows of tiny values so that 2^-e stays a normal float, and returns
+// the scale sc to apply to the values and the exponent to store (e + so, the product's 2^-so
+// undone). Segments whose values are all below 2^-112 are stored as zeros.
+template <int NT>
+__device__ __forceinline__ float bfp16_scale(f32x16 (&c)[NT], int so, int* es_out) {
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT; i++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) mx = fmaxf(mx, fabsf(c[i][r]));
+  int e = bfp16_exponent(half_swap_max(mx));
+  if (__ballot(e < -126)) {
+    const int pre = e < -126 ? -126 - e : 0;
+#pragma unroll
+    for (int i = 0; i < NT; i++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) c[i][r] = __builtin_amdgcn_ldexpf(c[i][r], pre);
+    e += pre;
+  }
+  int es = e + so;
+  float sc = __builtin_amdgcn_ldexpf(1.0f, -e);
+  if (es < -127) {
+    es = 0;
+    sc = 0.f;
+  }
+  *es_out = es > 127 ? 127 : es;
+  return sc;
+}
+// Bound on |sm_scale * dS| over a token's valid slots and a block of heads, for the scale of the dS
+// operand of the dKV product: with P <= 1 (the LSE passed in is at least the log of each head's
+// softmax denominator, as the forward's is), |dS| <= |dP| + |Delta|, and |dP| = |<dO_h, kv_t>| <=
+// sqrt(D) max|dO| max_t |kv_t| (Cauchy-Schwarz); |Delta| is taken from the Delta passed in
+// (max_delta = its largest magnitude over the block's heads).
+__device__ __forceinline__ float dS_operand_bound(float sm_scale, int D, float max_do, float max_row_norm,
+                                                  float max_delta) {
+  return fabsf(sm_scale) * (sqrtf((float)D) * max_do * max_row_norm + max_delta);
+}
+// dS as an fp16 pair hi + lo (lo = the rounding error of hi, itself rounded to fp16): with a single
+// fp16 dS operand the dKV product's rounding dominates the error of heavily shared rows.
+__device__ __forceinline__ void f16_hilo4(const float (&x)[4], uint2* hi, uint2* lo) {
+  const f16x2 h01 = __builtin_convertvector((f32x2){x[0], x[1]}, f16x2);
+  const f16x2 h23 = __builtin_convertvector((f32x2){x[2], x[3]}, f16x2);
+  const f16x2 l01 = __builtin_convertvector((f32x2){x[0] - (float)h01[0], x[1] - (float)h01[1]}, f16x2);
+  const f16x2 l23 = __builtin_convertvector((f32x2){x[2] - (float)h23[0], x[3] - (float)h23[1]}, f16x2);
+  *hi = make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
+  *lo = make_uint2(__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23));
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -64,18 +129,21 @@ delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, 
   constexpr int LPR = D / 8;   // lanes per row (16 bytes each)
   constexpr int RPW = 64 / LPR;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t row = ((int64_t)blockIdx.x * 4 + w) * RPW + lane / LPR;
   const int chunk = lane % LPR;
-  float s = 0.f;
-  if (row < rows) {
-    const bf16x8 a = load_bf16x8(o + row * D + chunk * 8);
-    const bf16x8 c = load_bf16x8(dout + row * D + chunk * 8);
+  // workgroups loop over groups of 4 * RPW rows (the grid is capped)
+  for (int64_t g = blockIdx.x; g * 4 * RPW < rows; g += gridDim.x) {
+    const int64_t row = (g * 4 + w) * RPW + lane / LPR;
+    float s = 0.f;
+    if (row < rows) {
+      const bf16x8 a = load_bf16x8(o + row * D + chunk * 8);
+      const bf16x8 c = load_bf16x8(dout + row * D + chunk * 8);
 #pragma unroll
-    for (int e = 0; e < 8; e++) s += (float)a[e] * (float)c[e];
+      for (int e = 0; e < 8; e++) s += (float)a[e] * (float)c[e];
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (row < rows && chunk == 0) delta[row] = s;
   }
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if (row < rows && chunk == 0) delta[row] = s;
 }
 
 // d_sink[h] = -sum over tokens of 2^(sink_h log2 e - LSE) * Delta: the sink adds exp(sink_h) to
@@ -626,14 +694,14 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
   constexpr int SB = HB * T * 2;  // bytes of one [HB][T] bf16 buffer
   __shared__ __attribute__((aligned(16))) char tile0[C::TB];
   __shared__ __attribute__((aligned(16))) char tile1[C::TB];
-  // B operands of the dKV product, each [head][slot]. Staged: fp16 sm_scale * dS * 2^(sq - so),
-  // then fp16 P. Atomic (no kv_norm bound): the hi and lo bf16 parts of sm_scale * dS * 2^-so
-  // (lo = x - float(bf16(x)), rounded), then fp16 P.
-  constexpr int NB = STAGED ? 2 : 3;
+  // B operands of the dKV product, each [head][slot]: the hi and lo parts of the dS operand, then
+  // fp16 P. Staged: fp16 hi + lo of sm_scale * dS * 2^(sq - so). Atomic (no kv_norm bound): bf16
+  // hi + lo of sm_scale * dS * 2^-so (lo = x - float(bf16(x)), rounded).
+  constexpr int NB = 3;
   __shared__ __attribute__((aligned(16))) char pds[NB * SB];
-  __shared__ float red[3][NW];
+  __shared__ float red[4][NW];
   // Staging-store transpose. The dKV^T accumulator gives each lane one slot row and runs of four
-  // consecutive d; they go to this wave's [32 slots][SEGW d] fp16 buffer as 8-byte writes and come
+  // consecutive d; they go to this wave's [32 slots][SEGW d] int16 buffer as 8-byte writes and come
   // back as 16-byte pieces of whole row segments, so one store instruction covers LPR * 16
   // contiguous bytes of each of RPS rows. Rows are unpadded and their 16-byte chunks XOR-swizzled
   // by the row's low bits (obuf_chunk): the read-back is conflict-free and the writes (32 rows at
@@ -675,11 +743,10 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
   // bf16 value within 2^28 of the max converts exactly. Staged, Q is fp16 as well, scaled by 2^-sq
   // from max |q|, and the dS operand is sm_scale * dS * 2^(sq - so) in fp16, so both products
   // carry 2^-so, which the staged rows' exponents undo. so is raised where needed so that the dS
-  // operand stays inside the fp16 range: |sm_scale dS| <= sm_scale (|dP| + |Delta|) <= 2 sm_scale
-  // sqrt(D) max|dO| max_t |kv_t| (P <= 1, Cauchy-Schwarz, and |O| <= max_t |kv_t| as O is a
-  // convex combination of the token's kv rows), with max_t over the token's valid slots from the
-  // per-row norms in row_norm. The atomic variant has no row norms: Q stays bf16 and dS goes in as
-  // a hi + lo pair of bf16 (three MFMAs per k-step).
+  // operand stays inside the fp16 range (dS_operand_bound: P <= 1, Cauchy-Schwarz for dP, the
+  // block's largest |Delta|), with max_t |kv_t| over the token's valid slots from the per-row norms
+  // in row_norm. The dS operand is an fp16 hi + lo pair. The atomic variant has no row norms: Q
+  // stays bf16 and dS goes in as a hi + lo pair of bf16. Both run three MFMAs per k-step.
   constexpr int HH = C::TB / (D * 2);  // heads per tile buffer
   static_assert(HB <= 2 * HH && HH % 16 == 0, "staging copy must fit the tile buffers");
   constexpr int NPT = HB * D / 8 / (NW * 64);  // 16-byte pieces per thread
@@ -706,8 +773,9 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
         }
     };
     uint4 rq[NPT], rd[NPT];
-    float mq = 0.f, md = 0.f, mv = 0.f;
-    if constexpr (STAGED) {  // largest norm among this token's referenced kv rows
+    float mq = 0.f, md = 0.f, mv = 0.f, mdl = 0.f;
+    if constexpr (STAGED) {  // largest norm among this token's referenced kv rows; largest |Delta|
+      if (threadIdx.x < HB) mdl = fabsf(delta[token * H + (int64_t)hblk * HB + threadIdx.x]);
       const int32_t* it = idx + token * (int64_t)topk;
       const float* nb = row_norm + b * S_kv;
       constexpr int U = 8;  // independent index loads, then independent norm loads
@@ -742,11 +810,13 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
       mq = fmaxf(mq, __shfl_xor(mq, o));
       md = fmaxf(md, __shfl_xor(md, o));
       mv = fmaxf(mv, __shfl_xor(mv, o));
+      mdl = fmaxf(mdl, __shfl_xor(mdl, o));
     }
     if (lane == 0) {
       red[0][w] = mq;
       red[1][w] = md;
       red[2][w] = mv;
+      red[3][w] = mdl;
     }
     __syncthreads();
 #pragma unroll
@@ -754,13 +824,14 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
       mq = fmaxf(mq, red[0][k]);
       md = fmaxf(md, red[1][k]);
       mv = fmaxf(mv, red[2][k]);
+      mdl = fmaxf(mdl, red[3][k]);
     }
     // scaled maxima stay below 2^15
     const int sq = (STAGED && mq > 0.f && mq <= 3.4028235e38f) ? __builtin_amdgcn_frexp_expf(mq) - 15 : 0;
     if (md > 0.f && md <= 3.4028235e38f) {
       so = __builtin_amdgcn_frexp_expf(md) - 15;
       if constexpr (STAGED) {
-        const float bound = 2.f * sm_scale * sqrtf((float)D) * md * mv;
+        const float bound = dS_operand_bound(sm_scale, D, md, mv, mdl);
         if (bound > 0.f && bound <= 3.4028235e38f) {
           const int sd = __builtin_amdgcn_frexp_expf(bound) + sq - 15;
           so = so > sd ? so : sd;
@@ -934,9 +1005,7 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
         for (int r = 0; r < 4; r++)  // saturated to the fp16 range: only inputs outside the bound's assumptions reach it
           ds[r] = __builtin_amdgcn_fmed3f(
               __builtin_amdgcn_ldexpf(sm_scale * p[r] * (dpacc[mt][r] - delta_h), sqo), -65504.f, 65504.f);
-        const f16x2 d01 = __builtin_convertvector((f32x2){ds[0], ds[1]}, f16x2);
-        const f16x2 d23 = __builtin_convertvector((f32x2){ds[2], ds[3]}, f16x2);
-        *(uint2*)(wp) = make_uint2(__builtin_bit_cast(uint32_t, d01), __builtin_bit_cast(uint32_t, d23));
+        f16_hilo4(ds, (uint2*)(wp), (uint2*)(wp + SB));
       } else {
         float dslr[4];
 #pragma unroll
@@ -954,8 +1023,8 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
     lds_barrier();  // P/dS visible to all waves; the next tile's gather stays in flight
 
     // 2^-so dKV^T[d, slot] for this wave's d-range, DG tiles of 32 d at a time, k over the block's
-    // heads: (2^-sq Q)^T (2^(sq-so) sm_scale dS) + (2^-so dO)^T P staged, and
-    // Q^T dS_hi + Q^T dS_lo + (2^-so dO)^T P atomic.
+    // heads: Q^T dS_hi + Q^T dS_lo + (2^-so dO)^T P, with Q scaled by 2^-sq and dS by 2^(sq-so)
+    // (fp16) staged, Q and dS by 2^-so (bf16) atomic.
     // C layout: lane holds slot (lane & 31), d = w*DW + 32 dt + 8 (r >> 2) + 4 kg + (r & 3).
     // Masked slots store into this workgroup's spare row (after all staging rows of the chunk),
     // so the stores need no per-slot branches.
@@ -1030,29 +1099,15 @@ bwd_dkv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, 
         continue;
       }
       // one exponent per slot row segment (this lane and lane ^ 32 hold the row's values), then
-      // fp16 runs of four d into this wave's transpose buffer
-      float mx = 0.f;
+      // int16 runs of four d into this wave's transpose buffer
+      int es;
+      const float sc = bfp16_scale(c, so, &es);
 #pragma unroll
       for (int i = 0; i < DG; i++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) mx = fmaxf(mx, fabsf(c[i][r]));
-      const int e = stage_exponent(half_swap_max(mx));
-      int es = e + so;  // the stored exponent also undoes the dO scale
-      es = es < -127 ? -127 : (es > 127 ? 127 : es);
-      if (__ballot(e != 0)) {
-#pragma unroll
-        for (int i = 0; i < DG; i++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) c[i][r] = __builtin_amdgcn_ldexpf(c[i][r], -e);
-      }
-#pragma unroll
-      for (int i = 0; i < DG; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const f16x2 a = __builtin_convertvector((f32x2){c[i][4 * j], c[i][4 * j + 1]}, f16x2);
-          const f16x2 b2 = __builtin_convertvector((f32x2){c[i][4 * j + 2], c[i][4 * j + 3]}, f16x2);
-          *(i32x2*)(ob + obuf_chunk(lane & 31, 4 * i + j)) = i32x2{__builtin_bit_cast(int, a), __builtin_bit_cast(int, b2)};
-        }
+        for (int j = 0; j < 4; j++)
+          *(i32x2*)(ob + obuf_chunk(lane & 31, 4 * i + j)) =
+              i32x2{(int)bfp16_pair(c[i][4 * j], c[i][4 * j + 1], sc), (int)bfp16_pair(c[i][4 * j + 2], c[i][4 * j + 3], sc)};
       if constexpr (DEFER) {
         if (lane < T) obdst[w][lane] = dst_this;
         wait_all_mem();  // this wave's part of tile blk + 1
@@ -1118,10 +1173,11 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   constexpr int SB = HB * T * 2;  // bytes of one [HB][T] fp16 buffer
   __shared__ __attribute__((aligned(16))) char tile0[C::TB];
   __shared__ __attribute__((aligned(16))) char tile1[C::TB];
-  // dS operand then P of a block, each [head][slot] fp16; block j goes through pds<j & 1>
-  __shared__ __attribute__((aligned(16))) char pds0[2 * SB];
-  __shared__ __attribute__((aligned(16))) char pds1[2 * SB];
-  __shared__ float red[3][NWT];
+  // dS operand (hi, then lo) then P of a block, each [head][slot] fp16; block j goes through
+  // pds<j & 1>
+  __shared__ __attribute__((aligned(16))) char pds0[3 * SB];
+  __shared__ __attribute__((aligned(16))) char pds1[3 * SB];
+  __shared__ float red[4][NWT];
   // staging-store transpose per product wave, as in bwd_dkv_kernel (one exponent segment = DW)
   constexpr int SEGW = NDT * 32;
   constexpr int NSEG = D / SEGW;
@@ -1163,6 +1219,7 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   {
     const int64_t base = (token * H + (int64_t)hblk * HB) * D;
     float mq = 0.f, md = 0.f, mv = 0.f;
+    float mdl = threadIdx.x < HB ? fabsf(delta[token * H + (int64_t)hblk * HB + threadIdx.x]) : 0.f;
     const float* nb = row_norm + b * S_kv;
     constexpr int U = 8;  // independent index loads, then independent norm loads
     for (int t0 = threadIdx.x; t0 < topk; t0 += U * NWT * 64) {
@@ -1195,11 +1252,13 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
       mq = fmaxf(mq, __shfl_xor(mq, o));
       md = fmaxf(md, __shfl_xor(md, o));
       mv = fmaxf(mv, __shfl_xor(mv, o));
+      mdl = fmaxf(mdl, __shfl_xor(mdl, o));
     }
     if (lane == 0) {
       red[0][w] = mq;
       red[1][w] = md;
       red[2][w] = mv;
+      red[3][w] = mdl;
     }
     __syncthreads();
 #pragma unroll
@@ -1207,11 +1266,12 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
       mq = fmaxf(mq, red[0][k]);
       md = fmaxf(md, red[1][k]);
       mv = fmaxf(mv, red[2][k]);
+      mdl = fmaxf(mdl, red[3][k]);
     }
     const int sq = (mq > 0.f && mq <= 3.4028235e38f) ? __builtin_amdgcn_frexp_expf(mq) - 15 : 0;
     if (md > 0.f && md <= 3.4028235e38f) {
       so = __builtin_amdgcn_frexp_expf(md) - 15;
-      const float bound = 2.f * sm_scale * sqrtf((float)D) * md * mv;
+      const float bound = dS_operand_bound(sm_scale, D, md, mv, mdl);
       if (bound > 0.f && bound <= 3.4028235e38f) {
         const int sd = __builtin_amdgcn_frexp_expf(bound) + sq - 15;
         so = so > sd ? so : sd;
@@ -1307,15 +1367,13 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
             for (int r = 0; r < 4; r++)
               p[r] = ((vb >> (16 * mt + r)) & 1u) ? fast_exp2(sacc[mt][r] * scale_log2 - lse_h) : 0.f;
 #pragma unroll
-            for (int r = 0; r < 4; r++)
+            for (int r = 0; r < 4; r++)  // saturated to the fp16 range: only inputs outside the bound's assumptions reach it
               ds[r] = __builtin_amdgcn_fmed3f(
                   __builtin_amdgcn_ldexpf(sm_scale * p[r] * (dpacc[mt][r] - delta_h), sqo), -65504.f, 65504.f);
-            const f16x2 d01 = __builtin_convertvector((f32x2){ds[0], ds[1]}, f16x2);
-            const f16x2 d23 = __builtin_convertvector((f32x2){ds[2], ds[3]}, f16x2);
+            f16_hilo4(ds, (uint2*)(pw + 32 * mt), (uint2*)(pw + 32 * mt + SB));
             const f16x2 p01 = __builtin_convertvector((f32x2){p[0], p[1]}, f16x2);
             const f16x2 p23 = __builtin_convertvector((f32x2){p[2], p[3]}, f16x2);
-            *(uint2*)(pw + 32 * mt) = make_uint2(__builtin_bit_cast(uint32_t, d01), __builtin_bit_cast(uint32_t, d23));
-            *(uint2*)(pw + 32 * mt + SB) =
+            *(uint2*)(pw + 32 * mt + 2 * SB) =
                 make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
           }
         }
@@ -1372,7 +1430,7 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     int32_t idx_cur = load_idx(0), pos_cur = load_pos(0);
     __syncthreads();  // tile 0 is complete (the score waves' set-up)
 
-    // A block's products go to c; finish() then writes them out (exponent, fp16 transpose, staging
+    // A block's products go to c; finish() then writes them out (exponent, int16 transpose, staging
     // stores) before the stage ends. The stores thus share the vector memory path with the score
     // waves' softmax rather than with their gathers; finishing each block at the top of the next
     // stage instead (over the score waves' MFMAs and gathers) measured no faster, as that path
@@ -1385,31 +1443,17 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
       int ln = lane;
       asm volatile("" : "+v"(ln));
       // one exponent per slot row segment (this lane and lane ^ 32 hold the row's values)
-      float mx = 0.f;
-#pragma unroll
-      for (int i = 0; i < NDT; i++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) mx = fmaxf(mx, fabsf(c[i][r]));
-      const int e = stage_exponent(half_swap_max(mx));
-      int es = e + so;  // the stored exponent also undoes the dO scale
-      es = es < -127 ? -127 : (es > 127 ? 127 : es);
-      if (__ballot(e != 0)) {
-#pragma unroll
-        for (int i = 0; i < NDT; i++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) c[i][r] = __builtin_amdgcn_ldexpf(c[i][r], -e);
-      }
-      // fp16 runs of four d into this wave's transpose buffer (C layout: lane holds slot lane & 31,
+      int es;
+      const float sc = bfp16_scale(c, so, &es);
+      // int16 runs of four d into this wave's transpose buffer (C layout: lane holds slot lane & 31,
       // d = kw DW + 32 i + 8 (r >> 2) + 4 kg + (r & 3))
       char* ob = obuf[kw] + (ln & 31) * OP + 8 * (ln >> 5);
 #pragma unroll
       for (int i = 0; i < NDT; i++)
 #pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-          const f16x2 a = __builtin_convertvector((f32x2){c[i][4 * jj], c[i][4 * jj + 1]}, f16x2);
-          const f16x2 b2 = __builtin_convertvector((f32x2){c[i][4 * jj + 2], c[i][4 * jj + 3]}, f16x2);
-          *(i32x2*)(ob + obuf_chunk(ln & 31, 4 * i + jj)) = i32x2{__builtin_bit_cast(int, a), __builtin_bit_cast(int, b2)};
-        }
+        for (int jj = 0; jj < 4; jj++)
+          *(i32x2*)(ob + obuf_chunk(ln & 31, 4 * i + jj)) =
+              i32x2{(int)bfp16_pair(c[i][4 * jj], c[i][4 * jj + 1], sc), (int)bfp16_pair(c[i][4 * jj + 2], c[i][4 * jj + 3], sc)};
       // row read-back: lane covers d0 .. d0 + 7 of slot row n RPS + lane / LPR
       const int d0 = kw * DW + 8 * (ln % LPR);
 #pragma unroll
@@ -1444,28 +1488,30 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
             const char* p = pr + m * SB + ks * 16 * T * 2;
             return __builtin_bit_cast(f16x8, join_tr(lds_load_tr(p), lds_load_tr(p + 4 * T * 2)));
           };
-          // 2^-so dKV^T[d, slot] = (2^-sq Q)^T (2^(sq-so) sm_scale dS) + (2^-so dO)^T P
+          // 2^-so dKV^T[d, slot] = (2^-sq Q)^T (2^(sq-so) sm_scale (dS_hi + dS_lo)) + (2^-so dO)^T P
 #pragma unroll
           for (int i = 0; i < NDT; i++)
 #pragma unroll
             for (int r = 0; r < 16; r++) c[i][r] = 0.f;
-          f16x8 bcur[2], bnxt[2];
-          bcur[0] = bfrag(0, 0);
-          bcur[1] = bfrag(0, 1);
+          f16x8 bcur[3], bnxt[3];
+#pragma unroll
+          for (int m = 0; m < 3; m++) bcur[m] = bfrag(0, m);
 #pragma unroll
           for (int ks = 0; ks < KH; ks++) {
             __builtin_amdgcn_sched_barrier(0);
             if (ks + 1 < KH) {
-              bnxt[0] = bfrag(ks + 1, 0);
-              bnxt[1] = bfrag(ks + 1, 1);
+#pragma unroll
+              for (int m = 0; m < 3; m++) bnxt[m] = bfrag(ks + 1, m);
             }
 #pragma unroll
             for (int i = 0; i < NDT; i++) c[i] = mfma32h(qv[i][ks], bcur[0], c[i]);
 #pragma unroll
-            for (int i = 0; i < NDT; i++) c[i] = mfma32h(dov[i][ks], bcur[1], c[i]);
+            for (int i = 0; i < NDT; i++) c[i] = mfma32h(qv[i][ks], bcur[1], c[i]);
+#pragma unroll
+            for (int i = 0; i < NDT; i++) c[i] = mfma32h(dov[i][ks], bcur[2], c[i]);
             if (ks + 1 < KH) {
-              bcur[0] = bnxt[0];
-              bcur[1] = bnxt[1];
+#pragma unroll
+              for (int m = 0; m < 3; m++) bcur[m] = bnxt[m];
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -1512,33 +1558,38 @@ mark_kernel(const int32_t* __restrict__ idx, int2* __restrict__ bc, int64_t toke
             int64_t S_kv, int topk, int64_t nw, int64_t n_rows) {
   __shared__ uint32_t lb[MARK_ROWS];
   __shared__ int32_t lc[MARK_ROWS];
-  const int64_t w0 = blockIdx.x % nw;
-  const int64_t r0 = (int64_t)(blockIdx.x / nw) * MARK_ROWS;
-  const int nr = (int)(n_rows - r0 < MARK_ROWS ? n_rows - r0 : MARK_ROWS);
-  for (int r = threadIdx.x; r < nr; r += 256) {
-    lb[r] = 0u;
-    lc[r] = 0;
-  }
-  __syncthreads();
-  for (int j = 0; j < 32; j++) {
-    const int64_t ct = w0 + nw * j;
-    if (ct >= n_chunk) break;
-    const int64_t token = token0 + ct;
-    const int32_t* it = idx + token * topk;
-    const int64_t rb = (token / S) * S_kv - r0;  // this token's batch rows, relative to the tile
-    for (int t = threadIdx.x; t < topk; t += 256) {
-      const int32_t v = it[t];
-      if (slot_in_range(v, S_kv)) {
-        const int64_t r = rb + v;
-        if (r >= 0 && r < nr) {
-          atomicOr(lb + r, 1u << j);
-          atomicAdd(lc + r, 1);
+  const int64_t n_units = nw * ((n_rows + MARK_ROWS - 1) / MARK_ROWS);
+  for (int64_t u = blockIdx.x; u < n_units; u += gridDim.x) {  // the grid is capped
+    const int64_t w0 = u % nw;
+    const int64_t r0 = (u / nw) * MARK_ROWS;
+    const int nr = (int)(n_rows - r0 < MARK_ROWS ? n_rows - r0 : MARK_ROWS);
+    for (int r = threadIdx.x; r < nr; r += 256) {
+      lb[r] = 0u;
+      lc[r] = 0;
+    }
+    __syncthreads();
+    for (int j = 0; j < 32; j++) {
+      const int64_t ct = w0 + nw * j;
+      if (ct >= n_chunk) break;
+      const int64_t token = token0 + ct;
+      const int64_t rb = (token / S) * S_kv - r0;  // this token's batch rows, relative to the tile
+      if (rb >= nr || rb + S_kv <= 0) continue;    // the token's batch has no row in this tile
+      const int32_t* it = idx + token * topk;
+      for (int t = threadIdx.x; t < topk; t += 256) {
+        const int32_t v = it[t];
+        if (slot_in_range(v, S_kv)) {
+          const int64_t r = rb + v;
+          if (r >= 0 && r < nr) {
+            atomicOr(lb + r, 1u << j);
+            atomicAdd(lc + r, 1);
+          }
         }
       }
     }
+    __syncthreads();
+    for (int r = threadIdx.x; r < nr; r += 256) bc[(r0 + r) * nw + w0] = make_int2((int)lb[r], lc[r]);
+    __syncthreads();  // lb and lc are cleared for the next unit
   }
-  __syncthreads();
-  for (int r = threadIdx.x; r < nr; r += 256) bc[(r0 + r) * nw + w0] = make_int2((int)lb[r], lc[r]);
 }
 
 // pos[ct, slot] = the slot's first staging row, or -1 for a masked slot. Workgroup unit u covers
@@ -1643,78 +1694,88 @@ template <int D>
 __global__ void __launch_bounds__(256)
 reduce_rows_kernel(const uint16_t* __restrict__ stage, const int8_t* __restrict__ stage_exp, int nseg,
                    const int32_t* __restrict__ offset, int64_t stride, f32x4* __restrict__ acc,
-                   uint4* __restrict__ out_bf16, int accumulate) {
-  // the row's segment is [offset[row * stride], offset[(row + 1) * stride])
+                   uint4* __restrict__ out_bf16, int accumulate, int64_t n_rows) {
+  // Workgroups loop over kv rows (the grid is capped); a row's segment is
+  // [offset[row * stride], offset[(row + 1) * stride]).
   // Thread c of a group takes values 8c .. 8c+7 of every NG-th staging row of the segment.
-  constexpr int F8 = D / 8;         // 16-byte pieces of fp16 per row
+  constexpr int F8 = D / 8;         // 16-byte pieces of int16 per row
   constexpr int NG = 256 / F8;      // thread groups
   static_assert(NG >= 1 && 256 % F8 == 0, "row width");
   __shared__ f32x4 part[NG][F8][2];
-  const int64_t row = blockIdx.x;
   const int g = threadIdx.x / F8, c = threadIdx.x % F8;
-  const int32_t beg = offset[row * stride], end = offset[(row + 1) * stride];
-  f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
+  f32x4 lo, hi;
+  // values 8c .. 8c+7 of a row: int16 pairs (the lower value in the low half) times 2^e
+  auto lo16 = [](int x) { return (float)(int)(int16_t)(uint16_t)(uint32_t)x; };
+  auto hi16 = [](int x) { return (float)(x >> 16); };
   auto add = [&](const i32x4& raw, int e) {
-    const f16x8 h = __builtin_bit_cast(f16x8, raw);
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
-      lo[k] += __builtin_amdgcn_ldexpf((float)h[k], e);
-      hi[k] += __builtin_amdgcn_ldexpf((float)h[4 + k], e);
+    for (int k = 0; k < 2; k++) {
+      lo[2 * k] += __builtin_amdgcn_ldexpf(lo16(raw[k]), e);
+      lo[2 * k + 1] += __builtin_amdgcn_ldexpf(hi16(raw[k]), e);
+      hi[2 * k] += __builtin_amdgcn_ldexpf(lo16(raw[2 + k]), e);
+      hi[2 * k + 1] += __builtin_amdgcn_ldexpf(hi16(raw[2 + k]), e);
     }
   };
   auto ld = [&](int32_t i) { return __builtin_nontemporal_load((const i32x4*)(stage + (int64_t)i * D) + c); };
   const int seg = 8 * c * nseg / D;  // exponent segment of this thread's 8 values
   auto lde = [&](int32_t i) { return (int)stage_exp[(int64_t)i * nseg + seg]; };
-  int32_t i = beg + g;
-  // eight rows in flight per thread, then four, then one (the order of the sums stays row order)
-  for (; i + 7 * NG < end; i += 8 * NG) {
-    i32x4 r[8];
-    int e[8];
+  for (int64_t row = blockIdx.x; row < n_rows; row += gridDim.x) {
+    const int32_t beg = offset[row * stride], end = offset[(row + 1) * stride];
+    lo = f32x4{0.f, 0.f, 0.f, 0.f};
+    hi = lo;
+    int32_t i = beg + g;
+    // eight rows in flight per thread, then four, then one (the order of the sums stays row order)
+    for (; i + 7 * NG < end; i += 8 * NG) {
+      i32x4 r[8];
+      int e[8];
 #pragma unroll
-    for (int k = 0; k < 8; k++) r[k] = ld(i + k * NG);
+      for (int k = 0; k < 8; k++) r[k] = ld(i + k * NG);
 #pragma unroll
-    for (int k = 0; k < 8; k++) e[k] = lde(i + k * NG);
+      for (int k = 0; k < 8; k++) e[k] = lde(i + k * NG);
 #pragma unroll
-    for (int k = 0; k < 8; k++) add(r[k], e[k]);
-  }
-  for (; i + 3 * NG < end; i += 4 * NG) {
-    const i32x4 r0 = ld(i), r1 = ld(i + NG), r2 = ld(i + 2 * NG), r3 = ld(i + 3 * NG);
-    const int e0 = lde(i), e1 = lde(i + NG), e2 = lde(i + 2 * NG), e3 = lde(i + 3 * NG);
-    add(r0, e0);
-    add(r1, e1);
-    add(r2, e2);
-    add(r3, e3);
-  }
-  for (; i < end; i += NG) add(ld(i), lde(i));
-  part[g][c][0] = lo;
-  part[g][c][1] = hi;
-  __syncthreads();
-  if (g == 0) {
-    f32x4 t0 = part[0][c][0], t1 = part[0][c][1];
-    for (int k = 1; k < NG; k++) {
-      t0 += part[k][c][0];
-      t1 += part[k][c][1];
+      for (int k = 0; k < 8; k++) add(r[k], e[k]);
     }
-    if (accumulate) {
-      t0 += acc[row * (D / 4) + 2 * c];
-      t1 += acc[row * (D / 4) + 2 * c + 1];
+    for (; i + 3 * NG < end; i += 4 * NG) {
+      const i32x4 r0 = ld(i), r1 = ld(i + NG), r2 = ld(i + 2 * NG), r3 = ld(i + 3 * NG);
+      const int e0 = lde(i), e1 = lde(i + NG), e2 = lde(i + 2 * NG), e3 = lde(i + 3 * NG);
+      add(r0, e0);
+      add(r1, e1);
+      add(r2, e2);
+      add(r3, e3);
     }
-    if (acc) {
-      acc[row * (D / 4) + 2 * c] = t0;
-      acc[row * (D / 4) + 2 * c + 1] = t1;
+    for (; i < end; i += NG) add(ld(i), lde(i));
+    part[g][c][0] = lo;
+    part[g][c][1] = hi;
+    __syncthreads();
+    if (g == 0) {
+      f32x4 t0 = part[0][c][0], t1 = part[0][c][1];
+      for (int k = 1; k < NG; k++) {
+        t0 += part[k][c][0];
+        t1 += part[k][c][1];
+      }
+      if (accumulate) {
+        t0 += acc[row * (D / 4) + 2 * c];
+        t1 += acc[row * (D / 4) + 2 * c + 1];
+      }
+      if (acc) {
+        acc[row * (D / 4) + 2 * c] = t0;
+        acc[row * (D / 4) + 2 * c + 1] = t1;
+      }
+      if (out_bf16) {
+        const uint2 a = pack4_bf16(t0[0], t0[1], t0[2], t0[3]), b = pack4_bf16(t1[0], t1[1], t1[2], t1[3]);
+        out_bf16[row * F8 + c] = make_uint4(a.x, a.y, b.x, b.y);
+      }
     }
-    if (out_bf16) {
-      const uint2 a = pack4_bf16(t0[0], t0[1], t0[2], t0[3]), b = pack4_bf16(t1[0], t1[1], t1[2], t1[3]);
-      out_bf16[row * F8 + c] = make_uint4(a.x, a.y, b.x, b.y);
-    }
+    __syncthreads();  // part is rewritten for the next row
   }
 }
 
 // ---------------------------------------------------------------------------------------------
 hipError_t launch_bwd_preprocess(const void* o, const void* d_o, float* delta, int64_t rows, int64_t D,
                                  hipStream_t st) {
-  const int64_t rpb = 4 * (64 / (D / 8));  // rows per 256-thread block
-  const dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(256);
+  const int64_t rpb = 4 * (64 / (D / 8));  // rows per 256-thread block and pass
+  const int64_t groups = (rows + rpb - 1) / rpb;
+  const dim3 grid((unsigned)(groups < (1 << 20) ? groups : (1 << 20))), block(256);
   if (D == 512)
     hipLaunchKernelGGL(delta_kernel<512>, grid, block, 0, st, (const uint16_t*)o, (const uint16_t*)d_o, delta, rows);
   else if (D == 256)
@@ -1854,10 +1915,9 @@ hipError_t launch_dkv_prepare(const int32_t* idx, uint32_t* plan, int32_t* offse
   int32_t* cur = (int32_t*)(plan + 2 * n);  // cursors of words with duplicate pairs
   hipError_t e = launch_fill_zero_f32((float*)cur, (n + 3) / 4 * 4, st);
   if (e != hipSuccess) return e;
-  const int64_t mark_groups = nw * ((n_rows + MARK_ROWS - 1) / MARK_ROWS);
-  if (mark_groups > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mark_kernel, dim3((unsigned)mark_groups), dim3(256), 0, st, idx, bc, token0, n_chunk, S, S_kv,
-                     (int)topk, nw, n_rows);
+  const int64_t mark_units = nw * ((n_rows + MARK_ROWS - 1) / MARK_ROWS);
+  hipLaunchKernelGGL(mark_kernel, dim3(grid_for(mark_units, 1, 1 << 20)), dim3(256), 0, st, idx, bc, token0, n_chunk,
+                     S, S_kv, (int)topk, nw, n_rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t tiles = scan_tiles(n);
   hipLaunchKernelGGL(scan_tiles_kernel, dim3((unsigned)tiles), dim3(256), 0, st, (const int2*)bc, offset, tile_sum,
@@ -1876,18 +1936,19 @@ hipError_t launch_dkv_prepare(const int32_t* idx, uint32_t* plan, int32_t* offse
 hipError_t launch_reduce_rows(const uint16_t* stage, const int8_t* stage_exp, int nseg, const int32_t* offset,
                               int64_t stride, float* acc, void* out_bf16, int accumulate, int64_t n_rows, int64_t D,
                               hipStream_t st) {
+  const dim3 grid((unsigned)(n_rows < (1 << 22) ? n_rows : (1 << 22)));
   if (D == 512)
-    hipLaunchKernelGGL(reduce_rows_kernel<512>, dim3((unsigned)n_rows), dim3(256), 0, st, stage, stage_exp, nseg,
-                       offset, stride, (f32x4*)acc, (uint4*)out_bf16, accumulate);
+    hipLaunchKernelGGL(reduce_rows_kernel<512>, grid, dim3(256), 0, st, stage, stage_exp, nseg, offset, stride,
+                       (f32x4*)acc, (uint4*)out_bf16, accumulate, n_rows);
   else if (D == 256)
-    hipLaunchKernelGGL(reduce_rows_kernel<256>, dim3((unsigned)n_rows), dim3(256), 0, st, stage, stage_exp, nseg,
-                       offset, stride, (f32x4*)acc, (uint4*)out_bf16, accumulate);
+    hipLaunchKernelGGL(reduce_rows_kernel<256>, grid, dim3(256), 0, st, stage, stage_exp, nseg, offset, stride,
+                       (f32x4*)acc, (uint4*)out_bf16, accumulate, n_rows);
   else if (D == 128)
-    hipLaunchKernelGGL(reduce_rows_kernel<128>, dim3((unsigned)n_rows), dim3(256), 0, st, stage, stage_exp, nseg,
-                       offset, stride, (f32x4*)acc, (uint4*)out_bf16, accumulate);
+    hipLaunchKernelGGL(reduce_rows_kernel<128>, grid, dim3(256), 0, st, stage, stage_exp, nseg, offset, stride,
+                       (f32x4*)acc, (uint4*)out_bf16, accumulate, n_rows);
   else if (D == 64)
-    hipLaunchKernelGGL(reduce_rows_kernel<64>, dim3((unsigned)n_rows), dim3(256), 0, st, stage, stage_exp, nseg,
-                       offset, stride, (f32x4*)acc, (uint4*)out_bf16, accumulate);
+    hipLaunchKernelGGL(reduce_rows_kernel<64>, grid, dim3(256), 0, st, stage, stage_exp, nseg, offset, stride,
+                       (f32x4*)acc, (uint4*)out_bf16, accumulate, n_rows);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
