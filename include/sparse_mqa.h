@@ -83,8 +83,9 @@ int sparse_mqa_fwd(const void* q, const void* kv, const float* attn_sink, const 
  * with one power-of-two exponent per segment of up to 128 values -- block floating point -- summed
  * in fp32).
  * sparse_mqa_bwd_workspace_bytes is the size for one pass over all tokens (an upper bound that
- * assumes every slot valid); any size >= sparse_mqa_bwd_workspace_min_bytes also works, and the
- * tokens are then processed in chunks with an fp32 running sum. Both return 0 for invalid sizes. */
+ * assumes every slot valid); any size >= sparse_mqa_bwd_workspace_min_bytes also works (the smaller
+ * of that and token chunks of one with an fp32 running sum), and the tokens are then processed in
+ * the largest chunks that fit. Both return 0 for invalid sizes. */
 size_t sparse_mqa_bwd_workspace_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D,
                                       int64_t topk);
 size_t sparse_mqa_bwd_workspace_min_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D,
@@ -108,6 +109,29 @@ int sparse_mqa_bwd(const void* q, const void* kv, const float* attn_sink, const 
                    const void* d_o, const int32_t* topk_idxs, const float* lse, void* dq, void* dkv,
                    int dkv_fp32, void* workspace, size_t workspace_bytes, int64_t B, int64_t S,
                    int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale, void* stream);
+
+/* Size of the static scratch of sparse_mqa_bwd_noalloc: 128 MiB per device. */
+#define SMQA_BWD_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* sparse_mqa_bwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same computation and results, with
+ * the workspace taken from a static device array of SMQA_BWD_SCRATCH_BYTES that the library holds
+ * on each device it runs on until the process ends. The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); the caller still passes every input and output.
+ * - Sizes whose smallest workspace (sparse_mqa_bwd_workspace_min_bytes) exceeds
+ *   SMQA_BWD_SCRATCH_BYTES are refused with SMQA_ERR_WORKSPACE before anything is enqueued; sizes
+ *   whose one-pass workspace (sparse_mqa_bwd_workspace_bytes) exceeds it run in token chunks, so
+ *   dkv may differ from sparse_mqa_bwd's one-pass result in fp32 summation order.
+ * - The stream must belong to the current device (else SMQA_ERR_ARG); the first call on a device
+ *   looks up that device's copy of the array (hipGetSymbolAddress).
+ * - Every call on one device shares that device's array: calls that overlap in time on one device
+ *   (different streams, or different threads without ordering) race and give wrong results. The
+ *   kernels clear what they need, so the array's contents from an earlier call do not matter.
+ * Other arguments, statuses and results as for sparse_mqa_bwd. */
+int sparse_mqa_bwd_noalloc(const void* q, const void* kv, const float* attn_sink, const void* o,
+                           const void* d_o, const int32_t* topk_idxs, const float* lse, void* dq,
+                           void* dkv, int dkv_fp32, int64_t B, int64_t S, int64_t S_kv, int64_t H,
+                           int64_t D, int64_t topk, float sm_scale, void* stream);
 
 /* Stage: Delta[b,s,h] = sum_d O*dO in fp32 (bwd page, preprocess factory). */
 int sparse_mqa_bwd_preprocess(const void* o, const void* d_o, float* delta, int64_t B, int64_t S,

@@ -142,6 +142,11 @@ def test_workspace_bytes(lib):
     assert dkv_layout_bytes(B, S_kv, H, D, K, B * S, False) > 6.4e9
     low = lib.sparse_mqa_bwd_workspace_min_bytes(B, S, S_kv, H, D, K)
     assert low == r256(B * S * H * 4) + dkv_layout_bytes(B, S_kv, H, D, K, 1, True)
+    # few tokens over many rows: a single pass (no fp32 running sum) is the smaller layout
+    b, s_, skv, h, d, k = 1, 8, 1 << 20, 64, 512, 4
+    assert lib.sparse_mqa_bwd_workspace_min_bytes(b, s_, skv, h, d, k) == r256(b * s_ * h * 4) + min(
+        dkv_layout_bytes(b, skv, h, d, k, 1, True), dkv_layout_bytes(b, skv, h, d, k, b * s_, False))
+    assert dkv_layout_bytes(b, skv, h, d, k, b * s_, False) < dkv_layout_bytes(b, skv, h, d, k, 1, True)
     # H = 128 runs two 64-head workgroups per token: two staging rows per slot (and two spare rows)
     for (b, s_, skv, h, d, k) in ((1, 8, 16, 128, 512, 4), (2, 40, 33, 16, 64, 7), (1, 100, 70, 192, 256, 9)):
         assert lib.sparse_mqa_bwd_workspace_bytes(b, s_, skv, h, d, k) == (
@@ -175,6 +180,39 @@ def test_bwd_validation(lib):
     assert bwd(lib, dkv=0x71000000 + 64) == ALIAS
     assert bwd(lib, ws=0x72000000) == ALIAS
     assert bwd(lib, scale=-math.inf) == ARG
+
+
+def bwd_noalloc(lib, dkv_fp32=0, dq=0x71000000, dkv=0x72000000, o=E, B=1, S=8, S_kv=16, H=64, D=512, topk=4,
+                scale=NAN):
+    return lib.sparse_mqa_bwd_noalloc(A, Bp, C, o, 0x11000000, Dp, F_, dq, dkv, dkv_fp32, B, S, S_kv, H, D, topk,
+                                      scale, None)
+
+
+def test_bwd_noalloc_validation(lib):
+    """Every argument check of the allocation-free backward runs before its scratch lookup, with
+    the statuses of sparse_mqa_bwd; sizes whose smallest workspace exceeds the static scratch are
+    refused with SMQA_ERR_WORKSPACE."""
+    assert bwd_noalloc(lib, dq=None) == NULL
+    assert bwd_noalloc(lib, S=0) == SHAPE
+    assert bwd_noalloc(lib, H=8) == UNSUP
+    assert bwd_noalloc(lib, dq=0x71000000 + 8) == ALIGN
+    assert bwd_noalloc(lib, scale=math.inf) == ARG
+    assert bwd_noalloc(lib, dq=A) == ALIAS
+    assert bwd_noalloc(lib, dkv=0x71000000 + 64) == ALIAS
+    # 2^20 kv rows, 4096 tokens, bf16 output: one pass needs 8 GiB of staging rows and token chunks
+    # the fp32 running sum (2 GiB), both beyond the scratch
+    scratch = 128 << 20
+    assert lib.sparse_mqa_bwd_workspace_min_bytes(1, 4096, 1 << 20, 64, 512, 2048) > scratch
+    assert bwd_noalloc(lib, S=4096, S_kv=1 << 20, topk=2048) == WORKSPACE
+    # with 8 tokens one pass (no running sum) takes ~24 MiB: that is the minimum, and it fits
+    assert lib.sparse_mqa_bwd_workspace_min_bytes(1, 8, 1 << 20, 64, 512, 4) <= scratch
+    assert bwd_noalloc(lib, S_kv=1 << 20, dq=A) == ALIAS
+    # the headline shape fits in token chunks (its one-pass workspace does not)
+    assert lib.sparse_mqa_bwd_workspace_min_bytes(1, 4096, 4096, 64, 512, 2048) <= scratch
+    assert lib.sparse_mqa_bwd_workspace_bytes(1, 4096, 4096, 64, 512, 2048) > scratch
+    assert bwd_noalloc(lib, S=4096, S_kv=4096, topk=2048, dq=A) == ALIAS
+    header = HEADER.read_text()
+    assert "#define SMQA_BWD_SCRATCH_BYTES ((size_t)128 << 20)" in header
 
 
 def test_stage_validation(lib):

@@ -27,6 +27,7 @@ _SIGS = {
     "sparse_mqa_bwd_workspace_min_bytes": [_i64] * 6,
     "sparse_mqa_bwd": [_c_void_p] * 9 + [ctypes.c_int, _c_void_p, ctypes.c_size_t] + [_i64] * 6
     + [ctypes.c_float, _c_void_p],
+    "sparse_mqa_bwd_noalloc": [_c_void_p] * 9 + [ctypes.c_int] + [_i64] * 6 + [ctypes.c_float, _c_void_p],
     "sparse_mqa_bwd_preprocess": [_c_void_p] * 3 + [_i64] * 4 + [_c_void_p],
     "sparse_mqa_bwd_dsink": [_c_void_p] * 4 + [_i64] * 3 + [_c_void_p],
     "sparse_mqa_bwd_main": [_c_void_p] * 8 + [_i64] * 6 + [ctypes.c_float, _c_void_p],

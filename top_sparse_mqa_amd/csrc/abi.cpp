@@ -3,8 +3,10 @@
 #include "../../include/sparse_mqa.h"
 #include "launch.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 namespace {
 
@@ -161,15 +163,21 @@ size_t dkv_layout(int64_t B, int64_t S_kv, int64_t H, int64_t D, int64_t topk, i
 // Lay out the dKV part of the workspace starting at `base`: one pass over all tokens if it fits,
 // else the largest token chunk that fits, with an fp32 running sum; false if `bytes` cannot hold
 // even one token's staging.
+// Most tokens one dKV pass may take: staging row indices are 32-bit, and the scan of the bitmap
+// words runs one workgroup per 4096 words (a launch holds fewer than 2^24 workgroups of 256
+// threads). 0 if not even one token fits.
+int64_t max_chunk_tokens(int64_t B, int64_t S_kv, int64_t H, int64_t topk) {
+  int64_t max_chunk = (int64_t)(INT32_MAX / ((topk + 1) * smqa::bwd_hblocks(H)));
+  const int64_t max_nw = (((int64_t)1 << 24) - 1) * 4096 / (B * S_kv);
+  if (max_nw * 32 < max_chunk) max_chunk = max_nw * 32;
+  return max_chunk < 0 ? 0 : max_chunk;
+}
+
 bool plan_dkv(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, bool dkv_fp32, size_t base,
               size_t bytes, DkvPlan* p) {
   const int64_t tokens = B * S;
-  // staging row indices are 32-bit; the scan of the bitmap words runs one workgroup per 4096
-  // words, and a launch holds fewer than 2^24 workgroups of 256 threads
-  int64_t max_chunk = (int64_t)(INT32_MAX / ((topk + 1) * smqa::bwd_hblocks(H)));
-  const int64_t max_nw = (((int64_t)1 << 24) - 1) * 4096 / (B * S_kv);
-  if (max_nw < 1) return false;
-  if (max_nw * 32 < max_chunk) max_chunk = max_nw * 32;
+  const int64_t max_chunk = max_chunk_tokens(B, S_kv, H, topk);
+  if (max_chunk < 1) return false;
   if (tokens <= max_chunk && dkv_layout(B, S_kv, H, D, topk, tokens, false, base, p) <= bytes) return true;
   const bool use_acc = !dkv_fp32;
   if (dkv_layout(B, S_kv, H, D, topk, 1, use_acc, base, p) > bytes) return false;
@@ -231,6 +239,83 @@ int check_bwd_inputs(const void* q, const void* kv, const void* d_o, const int32
   return resolve_scale(sm_scale, D, scale);
 }
 
+// Argument checks of the full backward on a workspace of workspace_bytes at `workspace` (which may be
+// null when check_ws_ptr is false: the allocation-free entry point learns its address only after
+// the checks, and its scratch overlaps no caller buffer). Fills the scale and the dKV plan.
+int bwd_validate(const void* q, const void* kv, const float* attn_sink, const void* o, const void* d_o,
+                 const int32_t* topk_idxs, const float* lse, void* dq, void* dkv, int dkv_fp32, void* workspace,
+                 size_t workspace_bytes, bool check_ws_ptr, int64_t B, int64_t S, int64_t S_kv, int64_t H,
+                 int64_t D, int64_t topk, float sm_scale, float* scale, DkvPlan* p) {
+  int st = check_bwd_inputs(q, kv, d_o, topk_idxs, lse, B, S, S_kv, H, D, topk, sm_scale, scale);
+  if (st) return st;
+  if (!attn_sink || !o || !dq || !dkv) return SMQA_ERR_NULL;
+  if (check_ws_ptr && !workspace) return SMQA_ERR_WORKSPACE;
+  if (!aligned16(o) || !aligned16(dq) || !aligned16(dkv) || !aligned4(attn_sink) || !aligned16(workspace))
+    return SMQA_ERR_ALIGN;
+  const size_t dbytes = delta_bytes(B, S, H);
+  if (workspace_bytes < dbytes || !plan_dkv(B, S, S_kv, H, D, topk, dkv_fp32 != 0, dbytes, workspace_bytes, p))
+    return SMQA_ERR_WORKSPACE;
+  const int64_t qb = count({B, S, H, D}) * 2, nkv = count({B, S_kv, D});
+  const Span sdq{dq, qb}, sdkv{dkv, nkv * (dkv_fp32 ? 4 : 2)}, sws{workspace, (int64_t)p->end};
+  const Span ins[] = {{q, qb}, {kv, nkv * 2}, {attn_sink, H * 4}, {o, qb}, {d_o, qb},
+                      {topk_idxs, count({B, S, topk}) * 4}, {lse, count({B, S, H}) * 4}};
+  for (const Span& s : ins)
+    if (overlap(sdq, s) || overlap(sdkv, s) || overlap(sws, s)) return SMQA_ERR_ALIAS;
+  if (overlap(sdq, sdkv) || overlap(sdq, sws) || overlap(sdkv, sws)) return SMQA_ERR_ALIAS;
+  return SMQA_OK;
+}
+
+// The full backward (preprocess, staged dKV in as many token chunks as the plan says, dQ) on a
+// validated workspace; sparse_mqa_bwd and sparse_mqa_bwd_noalloc differ only in where it comes from.
+int bwd_launch(const void* q, const void* kv, const void* o, const void* d_o, const int32_t* topk_idxs,
+               const float* lse, void* dq, void* dkv, int dkv_fp32, void* workspace, const DkvPlan& p, int64_t B,
+               int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, float scale, void* stream) {
+  hipStream_t hs = (hipStream_t)stream;
+  float* delta = (float*)workspace;
+  if (smqa::launch_bwd_preprocess(o, d_o, delta, count({B, S, H}), D, hs) != hipSuccess) return SMQA_ERR_HIP;
+  const int st = run_dkv(q, kv, d_o, topk_idxs, lse, delta, dkv, dkv_fp32, (char*)workspace, p, B, S, S_kv, H, D,
+                         topk, scale, hs);
+  if (st) return st;
+  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, nullptr, nullptr, nullptr, nullptr, nullptr, B, S, S_kv, H,
+                      D, topk, scale, 0, B * S};
+  return smqa::launch_bwd_main(a, 1, hs) == hipSuccess ? SMQA_OK : SMQA_ERR_HIP;
+}
+
+// Workspace of sparse_mqa_bwd_noalloc, for callers that cannot allocate device memory: one
+// SMQA_BWD_SCRATCH_BYTES array per device, created with the library's code object on each device it
+// runs on and held until the process ends. Host code never passes this name to a kernel (on the host
+// it is only a stand-in for the symbol): the device address of each device's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) char scratch[SMQA_BWD_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];  // device address of `scratch` per device, once known
+std::mutex g_scratch_mu;
+
+// Device address of the scratch array of the device `stream` runs on, which must be the current
+// device (hipGetSymbolAddress resolves the symbol for the current device).
+int scratch_for_stream(hipStream_t stream, void** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return SMQA_ERR_HIP;
+  if (stream) {
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return SMQA_ERR_HIP;
+    if ((int)sd != cur) return SMQA_ERR_ARG;
+  }
+  if (cur < 0 || cur >= kMaxDevices) return SMQA_ERR_UNSUPPORTED;
+  void* p = g_scratch_addr[cur].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[cur].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SMQA_ERR_HIP;
+      g_scratch_addr[cur].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SMQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -243,8 +328,18 @@ size_t sparse_mqa_bwd_workspace_bytes(int64_t B, int64_t S, int64_t S_kv, int64_
 
 size_t sparse_mqa_bwd_workspace_min_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk) {
   if (!sizes_ok(B, S, S_kv, H, D, topk)) return 0;
+  const int64_t max_chunk = max_chunk_tokens(B, S_kv, H, topk);
+  if (max_chunk < 1) return 0;
   DkvPlan p;
-  return delta_bytes(B, S, H) + dkv_layout(B, S_kv, H, D, topk, 1, true, 0, &p);
+  // token chunks of one (with the fp32 running sum), or a single pass over all tokens when that
+  // takes less (few tokens over many kv rows)
+  const size_t chunked = dkv_layout(B, S_kv, H, D, topk, 1, true, 0, &p);
+  size_t low = chunked;
+  if (B * S <= max_chunk) {
+    const size_t one_pass = dkv_layout(B, S_kv, H, D, topk, B * S, false, 0, &p);
+    if (one_pass < low) low = one_pass;
+  }
+  return delta_bytes(B, S, H) + low;
 }
 
 int sparse_mqa_bwd_preprocess(const void* o, const void* d_o, float* delta, int64_t B, int64_t S, int64_t H,
@@ -431,33 +526,29 @@ int sparse_mqa_bwd(const void* q, const void* kv, const float* attn_sink, const 
                    size_t workspace_bytes, int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk,
                    float sm_scale, void* stream) {
   float scale;
-  int st = check_bwd_inputs(q, kv, d_o, topk_idxs, lse, B, S, S_kv, H, D, topk, sm_scale, &scale);
-  if (st) return st;
-  if (!attn_sink || !o || !dq || !dkv) return SMQA_ERR_NULL;
-  if (!workspace) return SMQA_ERR_WORKSPACE;
-  if (!aligned16(o) || !aligned16(dq) || !aligned16(dkv) || !aligned4(attn_sink) || !aligned16(workspace))
-    return SMQA_ERR_ALIGN;
-  const size_t dbytes = delta_bytes(B, S, H);
   DkvPlan p;
-  if (workspace_bytes < dbytes || !plan_dkv(B, S, S_kv, H, D, topk, dkv_fp32 != 0, dbytes, workspace_bytes, &p))
-    return SMQA_ERR_WORKSPACE;
-  const int64_t qb = count({B, S, H, D}) * 2, nkv = count({B, S_kv, D});
-  const Span sdq{dq, qb}, sdkv{dkv, nkv * (dkv_fp32 ? 4 : 2)}, sws{workspace, (int64_t)p.end};
-  const Span ins[] = {{q, qb}, {kv, nkv * 2}, {attn_sink, H * 4}, {o, qb}, {d_o, qb},
-                      {topk_idxs, count({B, S, topk}) * 4}, {lse, count({B, S, H}) * 4}};
-  for (const Span& s : ins)
-    if (overlap(sdq, s) || overlap(sdkv, s) || overlap(sws, s)) return SMQA_ERR_ALIAS;
-  if (overlap(sdq, sdkv) || overlap(sdq, sws) || overlap(sdkv, sws)) return SMQA_ERR_ALIAS;
+  const int st = bwd_validate(q, kv, attn_sink, o, d_o, topk_idxs, lse, dq, dkv, dkv_fp32, workspace, workspace_bytes,
+                              true, B, S, S_kv, H, D, topk, sm_scale, &scale, &p);
+  if (st) return st;
+  return bwd_launch(q, kv, o, d_o, topk_idxs, lse, dq, dkv, dkv_fp32, workspace, p, B, S, S_kv, H, D, topk, scale,
+                    stream);
+}
 
-  hipStream_t hs = (hipStream_t)stream;
-  float* delta = (float*)workspace;
-  if (smqa::launch_bwd_preprocess(o, d_o, delta, count({B, S, H}), D, hs) != hipSuccess) return SMQA_ERR_HIP;
-  if ((st = run_dkv(q, kv, d_o, topk_idxs, lse, delta, dkv, dkv_fp32, (char*)workspace, p, B, S, S_kv, H, D, topk,
-                    scale, hs)))
-    return st;
-  smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, nullptr, nullptr, nullptr, nullptr, nullptr, B, S, S_kv, H,
-                      D, topk, scale, 0, B * S};
-  return smqa::launch_bwd_main(a, 1, hs) == hipSuccess ? SMQA_OK : SMQA_ERR_HIP;
+int sparse_mqa_bwd_noalloc(const void* q, const void* kv, const float* attn_sink, const void* o, const void* d_o,
+                           const int32_t* topk_idxs, const float* lse, void* dq, void* dkv, int dkv_fp32, int64_t B,
+                           int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale,
+                           void* stream) {
+  // every argument check first, against a workspace of the scratch's size; then the scratch's
+  // address (the only HIP calls before the launches: device queries and, once per device, the
+  // symbol lookup)
+  float scale;
+  DkvPlan p;
+  int st = bwd_validate(q, kv, attn_sink, o, d_o, topk_idxs, lse, dq, dkv, dkv_fp32, nullptr,
+                        (size_t)SMQA_BWD_SCRATCH_BYTES, false, B, S, S_kv, H, D, topk, sm_scale, &scale, &p);
+  if (st) return st;
+  void* ws = nullptr;
+  if ((st = scratch_for_stream((hipStream_t)stream, &ws))) return st;
+  return bwd_launch(q, kv, o, d_o, topk_idxs, lse, dq, dkv, dkv_fp32, ws, p, B, S, S_kv, H, D, topk, scale, stream);
 }
 
 }  // extern "C"
