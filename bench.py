@@ -36,12 +36,13 @@ import torch
 METRIC = "sparse-MQA fwd/bwd TFLOP/s and % bf16 MFMA peak @ H=64 D=512 topk=2048"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
-KERNELS = ("fwd", "bwd_preprocess", "bwd_dq", "bwd_dkv_prepare", "bwd_dkv_partials", "bwd_dkv_reduce")
+KERNELS = ("fwd", "bwd_preprocess", "bwd_dkv_prepare", "bwd_dkv_partials", "bwd_dkv_dq", "bwd_dkv_reduce")
 # single-kernel steps: rocprofv3 kernel name prefix, source files, algorithmic flops per valid pair / (H*D)
 SINGLE = {
     "fwd": ("smqa::fwd_", ("fwd.hip", "device_common.h"), 4),  # fwd_ws_kernel at H=64k D=512
-    "bwd_dq": ("smqa::bwd_dq_", ("bwd.hip", "device_common.h"), 6),  # _ws_kernel at H=64k D=512
-    "bwd_dkv_partials": ("smqa::bwd_dkv_", ("bwd.hip", "device_common.h"), 8),  # _ws_kernel at H=64 D=512
+    # bwd_dkv_ws_kernel: S and dP recompute, dS^T Q and P^T dO
+    "bwd_dkv_partials": ("smqa::bwd_dkv_", ("bwd.hip", "device_common.h"), 8),
+    "bwd_dkv_dq": ("smqa::bwd_dq_ds_", ("bwd.hip", "device_common.h"), 2),  # dS K from the stored dS
 }
 CALIB_BYTES = 1 << 30        # the calibration copy reads and writes this many bytes
 CALIB_KERNEL = "MulFunctor"  # part of the name of the kernel torch.mul(src, 1.0, out=dst) runs
@@ -105,8 +106,8 @@ class Step:
             "fwd": lambda h: L.sparse_mqa_fwd(p(self.q), p(self.kv), p(self.sink), p(self.idx), p(self.o),
                                             p(self.lse), B, S, S_kv, H, D, K, self.nan, 0, h),
             "bwd_preprocess": lambda h: L.sparse_mqa_bwd_preprocess(p(self.o), p(self.do), p(self.delta), B, S, H, D, h),
-            "bwd_dq": lambda h: L.sparse_mqa_bwd_dq(p(self.q), p(self.kv), p(self.do), p(self.idx), p(self.lse),
-                                                  p(self.delta), p(self.dq), B, S, S_kv, H, D, K, self.nan, h),
+            "bwd_dkv_dq": lambda h: L.sparse_mqa_bwd_dkv_dq(p(self.kv), p(self.idx), p(self.dq), p(self.ws),
+                                                          self.ws_bytes, B, S, S_kv, H, D, K, self.nan, h),
             "bwd_dkv_prepare": lambda h: L.sparse_mqa_bwd_dkv_prepare(p(self.idx), p(self.ws), self.ws_bytes,
                                                                     B, S, S_kv, H, D, K, h),
             "bwd_dkv_partials": lambda h: L.sparse_mqa_bwd_dkv_partials(
@@ -136,10 +137,10 @@ class Step:
             launch("bwd_dkv_prepare", self.side)
             ready = torch.cuda.Event()
             ready.record(self.side)
-            for k in ("fwd", "bwd_preprocess", "bwd_dq"):
+            for k in ("fwd", "bwd_preprocess"):
                 launch(k, self.stream)
             self.stream.wait_event(ready)
-            for k in ("bwd_dkv_partials", "bwd_dkv_reduce"):
+            for k in ("bwd_dkv_partials", "bwd_dkv_dq", "bwd_dkv_reduce"):
                 launch(k, self.stream)
         if timed:
             self.events.append(ev)

@@ -159,18 +159,21 @@ int sparse_mqa_bwd_dkv(const void* q, const void* kv, const void* d_o, const int
                        size_t workspace_bytes, int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D,
                        int64_t topk, float sm_scale, void* stream);
 
-/* The three steps of sparse_mqa_bwd_dkv for a single pass, for callers that schedule or time them
- * separately (bwd page, bwd factory: the dKV scatter-add). They need a workspace that holds every
- * token (at least sparse_mqa_bwd_workspace_bytes minus Delta's bytes; SMQA_ERR_WORKSPACE otherwise)
- * and must run in this order with the same workspace and sizes:
+/* The steps of sparse_mqa_bwd's staged pass over all tokens, for callers that schedule or time them
+ * separately (bwd page, bwd factory: the dKV scatter-add, and dQ). They need a workspace that holds
+ * every token (at least sparse_mqa_bwd_workspace_bytes minus Delta's bytes; SMQA_ERR_WORKSPACE
+ * otherwise) and must run in this order with the same workspace and sizes:
  *   prepare   marks every valid (token, kv row) pair in a bitmap and gives each valid slot its
  *             staging row: a kv row's rows are contiguous, in an order fixed by the
  *             token indices;
- *   partials  computes every valid slot's dKV contribution row into the staging rows;
+ *   partials  computes every valid slot's dKV contribution row into the staging rows; at D = 512
+ *             with H a multiple of 64 it also stores dS = P (dP - Delta) (bf16) in the workspace;
+ *   dq        (sparse_mqa_bwd_dkv_dq; D = 512 with H a multiple of 64, else SMQA_ERR_UNSUPPORTED)
+ *             writes dq [B,S,H,D] bf16 = sm_scale * sum_t dS_t kv_i from that dS and the kv rows;
  *   reduce    sums each kv row's staging rows and writes dkv (bf16, or fp32 if dkv_fp32).
- * prepare reads only topk_idxs, so it may run on another stream, e.g. beside the forward, as
- * long as the caller orders it after the workspace's previous use and before partials (events);
- * partials and reduce go on one stream. */
+ * dq and reduce may run in either order after partials. prepare reads only topk_idxs, so it may
+ * run on another stream, e.g. beside the forward, as long as the caller orders it after the
+ * workspace's previous use and before partials (events); the other steps go on one stream. */
 int sparse_mqa_bwd_dkv_prepare(const int32_t* topk_idxs, void* workspace, size_t workspace_bytes,
                                int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk,
                                void* stream);
@@ -179,6 +182,9 @@ int sparse_mqa_bwd_dkv_partials(const void* q, const void* kv, const void* d_o,
                                 void* workspace, size_t workspace_bytes, int64_t B, int64_t S,
                                 int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale,
                                 void* stream);
+int sparse_mqa_bwd_dkv_dq(const void* kv, const int32_t* topk_idxs, void* dq, void* workspace,
+                          size_t workspace_bytes, int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D,
+                          int64_t topk, float sm_scale, void* stream);
 int sparse_mqa_bwd_dkv_reduce(void* dkv, int dkv_fp32, void* workspace, size_t workspace_bytes,
                               int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk,
                               void* stream);

@@ -116,14 +116,17 @@ def r256(n):
     return (n + 255) // 256 * 256
 
 
-def dkv_layout_bytes(B, S_kv, H, D, K, chunk, acc):
+def dkv_layout_bytes(B, S_kv, H, D, K, chunk, acc, ds=None):
     """The dKV workspace layout restated: kv row norms, the selection bitmap (one bit per kv row and
     chunk token, in 32-bit words) with a pair count and a cursor per word (cleared together as whole
     16-byte pieces), the scanned offsets (+ total),
     the scan's tile sums, the fp32 accumulator when chunked with bf16 output, the slots' positions,
-    and the staging rows (one per slot and 64-head block plus one spare per token and head block; a
+    the staging rows (one per slot and 64-head block plus one spare per token and head block; a
     row is D int16 values and one int8 exponent per segment of min(128, D / (heads per workgroup /
-    16)) values)."""
+    16)) values), and, for the full backward at D = 512 with H a multiple of 64 (ds=None picks it by
+    shape), the stored dS: [chunk][H / 64][ceil(K / 32)][64][32] bf16."""
+    if ds is None:
+        ds = D == 512 and H % 64 == 0
     n_rows = B * S_kv
     words = n_rows * ((chunk + 31) // 32)
     hb = max(1, H // 64)
@@ -131,7 +134,7 @@ def dkv_layout_bytes(B, S_kv, H, D, K, chunk, acc):
     rows = chunk * (K + 1) * hb
     return (r256(n_rows * 4) + r256((3 * words + 4) * 4) + r256((words + 1) * 4) + r256(((words + 4095) // 4096) * 4)
             + (r256(n_rows * D * 4) if acc else 0) + r256(chunk * K * 4) + r256(rows * D * 2)
-            + r256(rows * (D // seg)))
+            + r256(rows * (D // seg)) + (r256(chunk * (H // 64) * ((K + 31) // 32) * 64 * 32 * 2) if ds else 0))
 
 
 def test_workspace_bytes(lib):

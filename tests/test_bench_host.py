@@ -47,7 +47,7 @@ def test_pmc_summary_scales_by_the_calibration_copy(tmp_path):
     assert k["fetch_bytes"] == round(1001.0 * 1024 * 2.0)  # mean of the two dispatches, scaled
     assert k["write_bytes"] == round(3000.0 * 1024)
     assert block["kernels"]["fwd"]["fetch_bytes"] == round(10.0 * 1024 * 2.0)
-    assert "bwd_dq" not in block["kernels"]  # no dispatch of it in the files
+    assert "bwd_dkv_dq" not in block["kernels"]  # no dispatch of it in the files
 
 
 def test_traffic_is_null_once_the_kernel_source_changes(tmp_path, monkeypatch):

@@ -331,7 +331,8 @@ def test_explicit_scale_and_int64_indices(gpu_lib):
 
 def test_dkv_paths_agree(gpu_lib):
     """Staged dKV in one pass, in forced token chunks (bf16 and fp32 outputs), and the atomic
-    stage all match the oracle."""
+    stage all match the oracle; the separately enqueued steps reproduce the one-call dKV, and their
+    dQ step (from the stored dS) the recompute dQ kernel."""
     w = syn.WORKLOADS["mid_h64_d512_k300"]
     say("case", w.name, "dKV paths")
     x = syn.workload_inputs(w)
@@ -364,10 +365,16 @@ def test_dkv_paths_agree(gpu_lib):
     steps = smqa.DkvSteps(*args)
     steps.prepare()
     steps.partials()
+    dq_steps = steps.dq()
     split = steps.reduce()
     torch.cuda.synchronize()
     check_bf16("dKV steps", split.view(-1, w.D), dkv_ref)
     assert torch.equal(split, one)
+    # dQ from the dS the partials step stored equals the recompute kernel's bit for bit (same bf16 dS,
+    # same order of the dQ products)
+    dq_recompute = smqa.bwd_dq(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(dq_steps, dq_recompute), "dQ from stored dS differs from the recompute kernel"
 
 
 def test_backward_is_deterministic(gpu_lib):

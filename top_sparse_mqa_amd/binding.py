@@ -36,6 +36,7 @@ _SIGS = {
     + [ctypes.c_float, _c_void_p],
     "sparse_mqa_bwd_dkv_prepare": [_c_void_p] * 2 + [ctypes.c_size_t] + [_i64] * 6 + [_c_void_p],
     "sparse_mqa_bwd_dkv_partials": [_c_void_p] * 7 + [ctypes.c_size_t] + [_i64] * 6 + [ctypes.c_float, _c_void_p],
+    "sparse_mqa_bwd_dkv_dq": [_c_void_p] * 4 + [ctypes.c_size_t] + [_i64] * 6 + [ctypes.c_float, _c_void_p],
     "sparse_mqa_bwd_dkv_reduce": [_c_void_p, ctypes.c_int, _c_void_p, ctypes.c_size_t] + [_i64] * 6 + [_c_void_p],
     "sparse_mqa_bwd_postprocess": [_c_void_p] * 2 + [_i64] * 3 + [_c_void_p],
     "sparse_mqa_status_string": [ctypes.c_int],
@@ -332,8 +333,9 @@ def bwd_dkv(q: torch.Tensor, kv: torch.Tensor, do: torch.Tensor, topk_idxs: torc
 
 
 class DkvSteps:
-    """The three steps of a single-pass dKV stage (prepare, partials, reduce) over one workspace,
-    for callers that time or schedule them separately; together they equal bwd_dkv."""
+    """The steps of a single-pass staged backward (prepare, partials, dq, reduce) over one workspace,
+    for callers that time or schedule them separately; prepare, partials and reduce together equal
+    bwd_dkv, and dq (D = 512 with H a multiple of 64) equals bwd_dq."""
 
     def __init__(self, q: torch.Tensor, kv: torch.Tensor, do: torch.Tensor, topk_idxs: torch.Tensor,
                  lse: torch.Tensor, delta: torch.Tensor, sm_scale: Optional[float] = None, dkv_fp32: bool = False):
@@ -363,6 +365,14 @@ class DkvSteps:
         _check("sparse_mqa_bwd_dkv_partials", load_library().sparse_mqa_bwd_dkv_partials(
             _ptr(self.q), _ptr(self.kv), _ptr(self.do), _ptr(self.idx), _ptr(self.lse), _ptr(self.delta),
             _ptr(self.workspace), self.workspace.numel(), *self._dims(), self.scale, _stream()))
+
+    def dq(self) -> torch.Tensor:
+        """dQ from the dS that partials stored (D = 512 with H a multiple of 64)."""
+        out = torch.empty((self.B, self.S, self.H, self.D), dtype=torch.bfloat16, device=self.q.device)
+        _check("sparse_mqa_bwd_dkv_dq", load_library().sparse_mqa_bwd_dkv_dq(
+            _ptr(self.kv), _ptr(self.idx), _ptr(out), _ptr(self.workspace), self.workspace.numel(), *self._dims(),
+            self.scale, _stream()))
+        return out
 
     def reduce(self) -> torch.Tensor:
         _check("sparse_mqa_bwd_dkv_reduce", load_library().sparse_mqa_bwd_dkv_reduce(

@@ -123,7 +123,7 @@ int sparse_mqa_fwd(const void* q, const void* kv, const float* attn_sink, const 
 namespace {
 
 struct DkvPlan {
-  size_t kvn, bits, offset, tiles, acc, pos, stage, stage_exp;  // byte offsets into the workspace
+  size_t kvn, bits, offset, tiles, acc, pos, stage, stage_exp, ds;  // byte offsets into the workspace
   int64_t chunk;                                               // tokens per chunk
   bool use_acc;                                                // a separate fp32 accumulator in the workspace
   size_t end;                                                  // bytes used
@@ -132,7 +132,7 @@ struct DkvPlan {
 // Lay out the dKV part of the workspace from `base` for token chunks of `chunk` tokens; returns the
 // end offset.
 size_t dkv_layout(int64_t B, int64_t S_kv, int64_t H, int64_t D, int64_t topk, int64_t chunk, bool use_acc,
-                  size_t base, DkvPlan* p) {
+                  bool with_ds, size_t base, DkvPlan* p) {
   const int64_t n_rows = B * S_kv, words = smqa::dkv_bitmap_words(n_rows, chunk);
   size_t o = base;
   p->kvn = o;  // kv row norms
@@ -155,6 +155,9 @@ size_t dkv_layout(int64_t B, int64_t S_kv, int64_t H, int64_t D, int64_t topk, i
   o += round256(rows * D * 2);
   p->stage_exp = o;
   o += round256(rows * smqa::stage_segments(H, D));
+  // the dS the dKV kernel stores for the dQ kernel (full backward at D = 512, 64-head blocks)
+  p->ds = with_ds ? o : 0;
+  if (with_ds) o += round256((size_t)smqa::ds_bytes(chunk, H, topk));
   p->chunk = chunk;
   p->end = o;
   return o;
@@ -173,21 +176,21 @@ int64_t max_chunk_tokens(int64_t B, int64_t S_kv, int64_t H, int64_t topk) {
   return max_chunk < 0 ? 0 : max_chunk;
 }
 
-bool plan_dkv(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, bool dkv_fp32, size_t base,
-              size_t bytes, DkvPlan* p) {
+bool plan_dkv(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, bool dkv_fp32, bool with_ds,
+              size_t base, size_t bytes, DkvPlan* p) {
   const int64_t tokens = B * S;
   const int64_t max_chunk = max_chunk_tokens(B, S_kv, H, topk);
   if (max_chunk < 1) return false;
-  if (tokens <= max_chunk && dkv_layout(B, S_kv, H, D, topk, tokens, false, base, p) <= bytes) return true;
+  if (tokens <= max_chunk && dkv_layout(B, S_kv, H, D, topk, tokens, false, with_ds, base, p) <= bytes) return true;
   const bool use_acc = !dkv_fp32;
-  if (dkv_layout(B, S_kv, H, D, topk, 1, use_acc, base, p) > bytes) return false;
+  if (dkv_layout(B, S_kv, H, D, topk, 1, use_acc, with_ds, base, p) > bytes) return false;
   int64_t lo = 1, hi = tokens < max_chunk ? tokens : max_chunk;
   while (lo < hi) {  // the largest chunk that fits (the layout grows with the chunk)
     const int64_t mid = lo + (hi - lo + 1) / 2;
-    if (dkv_layout(B, S_kv, H, D, topk, mid, use_acc, base, p) <= bytes) lo = mid;
+    if (dkv_layout(B, S_kv, H, D, topk, mid, use_acc, with_ds, base, p) <= bytes) lo = mid;
     else hi = mid - 1;
   }
-  dkv_layout(B, S_kv, H, D, topk, lo, use_acc, base, p);
+  dkv_layout(B, S_kv, H, D, topk, lo, use_acc, with_ds, base, p);
   return true;
 }
 
@@ -197,10 +200,11 @@ bool sizes_ok(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t 
   return check_shapes(B, S, S_kv, H, D, topk) == SMQA_OK;
 }
 
-// The staged dKV pass over all tokens, chunked as the plan says. dkv: bf16 or fp32 output.
+// The staged dKV pass over all tokens, chunked as the plan says. dkv: bf16 or fp32 output. When the
+// plan has a dS region, the dKV kernel also stores dS and dQ (dq) is computed from it chunk by chunk.
 int run_dkv(const void* q, const void* kv, const void* d_o, const int32_t* idx, const float* lse, const float* delta,
-            void* dkv, int dkv_fp32, char* ws, const DkvPlan& p, int64_t B, int64_t S, int64_t S_kv, int64_t H,
-            int64_t D, int64_t topk, float scale, hipStream_t st) {
+            void* dkv, int dkv_fp32, void* dq, char* ws, const DkvPlan& p, int64_t B, int64_t S, int64_t S_kv,
+            int64_t H, int64_t D, int64_t topk, float scale, hipStream_t st) {
   const int64_t tokens = B * S, n_rows = B * S_kv;
   uint32_t* bits = (uint32_t*)(ws + p.bits);
   int32_t* offset = (int32_t*)(ws + p.offset);
@@ -216,9 +220,10 @@ int run_dkv(const void* q, const void* kv, const void* d_o, const int32_t* idx, 
     if (smqa::launch_dkv_prepare(idx, bits, offset, tiles, pos, B, S, S_kv, topk, smqa::bwd_hblocks(H), t0, n, st) !=
         hipSuccess)
       return SMQA_ERR_HIP;
-    smqa::BwdMainArgs a{q, kv, d_o, idx, lse, delta, nullptr, nullptr, pos, stage, stage_exp, kvn, B, S, S_kv, H,
-                        D, topk, scale, t0, n};
+    smqa::BwdMainArgs a{q, kv, d_o, idx, lse, delta, dq, nullptr, pos, stage, stage_exp, kvn, B, S, S_kv, H,
+                        D, topk, scale, t0, n, p.ds ? (uint16_t*)(ws + p.ds) : nullptr};
     if (smqa::launch_bwd_main(a, 2, st) != hipSuccess) return SMQA_ERR_HIP;
+    if (p.ds && smqa::launch_bwd_dq_ds(a, st) != hipSuccess) return SMQA_ERR_HIP;
     const bool last = t0 + n >= tokens;
     void* out16 = (!dkv_fp32 && last) ? dkv : nullptr;
     if (smqa::launch_reduce_rows(stage, stage_exp, smqa::stage_segments(H, D), offset,
@@ -253,7 +258,8 @@ int bwd_validate(const void* q, const void* kv, const float* attn_sink, const vo
   if (!aligned16(o) || !aligned16(dq) || !aligned16(dkv) || !aligned4(attn_sink) || !aligned16(workspace))
     return SMQA_ERR_ALIGN;
   const size_t dbytes = delta_bytes(B, S, H);
-  if (workspace_bytes < dbytes || !plan_dkv(B, S, S_kv, H, D, topk, dkv_fp32 != 0, dbytes, workspace_bytes, p))
+  if (workspace_bytes < dbytes ||
+      !plan_dkv(B, S, S_kv, H, D, topk, dkv_fp32 != 0, smqa::dq_from_ds(H, D), dbytes, workspace_bytes, p))
     return SMQA_ERR_WORKSPACE;
   const int64_t qb = count({B, S, H, D}) * 2, nkv = count({B, S_kv, D});
   const Span sdq{dq, qb}, sdkv{dkv, nkv * (dkv_fp32 ? 4 : 2)}, sws{workspace, (int64_t)p->end};
@@ -273,9 +279,10 @@ int bwd_launch(const void* q, const void* kv, const void* o, const void* d_o, co
   hipStream_t hs = (hipStream_t)stream;
   float* delta = (float*)workspace;
   if (smqa::launch_bwd_preprocess(o, d_o, delta, count({B, S, H}), D, hs) != hipSuccess) return SMQA_ERR_HIP;
-  const int st = run_dkv(q, kv, d_o, topk_idxs, lse, delta, dkv, dkv_fp32, (char*)workspace, p, B, S, S_kv, H, D,
-                         topk, scale, hs);
+  const int st = run_dkv(q, kv, d_o, topk_idxs, lse, delta, dkv, dkv_fp32, dq, (char*)workspace, p, B, S, S_kv, H,
+                         D, topk, scale, hs);
   if (st) return st;
+  if (p.ds) return SMQA_OK;  // dQ came from the stored dS
   smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, dq, nullptr, nullptr, nullptr, nullptr, nullptr, B, S, S_kv, H,
                       D, topk, scale, 0, B * S};
   return smqa::launch_bwd_main(a, 1, hs) == hipSuccess ? SMQA_OK : SMQA_ERR_HIP;
@@ -323,7 +330,7 @@ extern "C" {
 size_t sparse_mqa_bwd_workspace_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk) {
   if (!sizes_ok(B, S, S_kv, H, D, topk)) return 0;
   DkvPlan p;
-  return delta_bytes(B, S, H) + dkv_layout(B, S_kv, H, D, topk, B * S, false, 0, &p);
+  return delta_bytes(B, S, H) + dkv_layout(B, S_kv, H, D, topk, B * S, false, smqa::dq_from_ds(H, D), 0, &p);
 }
 
 size_t sparse_mqa_bwd_workspace_min_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk) {
@@ -333,10 +340,11 @@ size_t sparse_mqa_bwd_workspace_min_bytes(int64_t B, int64_t S, int64_t S_kv, in
   DkvPlan p;
   // token chunks of one (with the fp32 running sum), or a single pass over all tokens when that
   // takes less (few tokens over many kv rows)
-  const size_t chunked = dkv_layout(B, S_kv, H, D, topk, 1, true, 0, &p);
+  const bool with_ds = smqa::dq_from_ds(H, D);
+  const size_t chunked = dkv_layout(B, S_kv, H, D, topk, 1, true, with_ds, 0, &p);
   size_t low = chunked;
   if (B * S <= max_chunk) {
-    const size_t one_pass = dkv_layout(B, S_kv, H, D, topk, B * S, false, 0, &p);
+    const size_t one_pass = dkv_layout(B, S_kv, H, D, topk, B * S, false, with_ds, 0, &p);
     if (one_pass < low) low = one_pass;
   }
   return delta_bytes(B, S, H) + low;
@@ -401,7 +409,7 @@ int sparse_mqa_bwd_dkv(const void* q, const void* kv, const void* d_o, const int
   if (!workspace) return SMQA_ERR_WORKSPACE;
   if (!aligned4(delta) || !aligned16(dkv) || !aligned16(workspace)) return SMQA_ERR_ALIGN;
   DkvPlan p;
-  if (!plan_dkv(B, S, S_kv, H, D, topk, dkv_fp32 != 0, 0, workspace_bytes, &p)) return SMQA_ERR_WORKSPACE;
+  if (!plan_dkv(B, S, S_kv, H, D, topk, dkv_fp32 != 0, false, 0, workspace_bytes, &p)) return SMQA_ERR_WORKSPACE;
   const int64_t qb = count({B, S, H, D}) * 2, nkv = count({B, S_kv, D});
   const Span sdkv{dkv, nkv * (dkv_fp32 ? 4 : 2)}, sws{workspace, (int64_t)p.end};
   const Span ins[] = {{q, qb}, {kv, nkv * 2}, {d_o, qb}, {topk_idxs, count({B, S, topk}) * 4},
@@ -409,7 +417,7 @@ int sparse_mqa_bwd_dkv(const void* q, const void* kv, const void* d_o, const int
   for (const Span& s : ins)
     if (overlap(sdkv, s) || overlap(sws, s)) return SMQA_ERR_ALIAS;
   if (overlap(sdkv, sws)) return SMQA_ERR_ALIAS;
-  return run_dkv(q, kv, d_o, topk_idxs, lse, delta, dkv, dkv_fp32, (char*)workspace, p, B, S, S_kv, H, D, topk, scale,
+  return run_dkv(q, kv, d_o, topk_idxs, lse, delta, dkv, dkv_fp32, nullptr, (char*)workspace, p, B, S, S_kv, H, D, topk, scale,
                  (hipStream_t)stream);
 }
 
@@ -420,7 +428,8 @@ static int single_pass_plan(void* workspace, size_t workspace_bytes, int64_t B, 
                             int64_t D, int64_t topk, int dkv_fp32, DkvPlan* p) {
   if (!workspace) return SMQA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return SMQA_ERR_ALIGN;
-  if (!plan_dkv(B, S, S_kv, H, D, topk, dkv_fp32 != 0, 0, workspace_bytes, p) || p->chunk != B * S)
+  if (!plan_dkv(B, S, S_kv, H, D, topk, dkv_fp32 != 0, smqa::dq_from_ds(H, D), 0, workspace_bytes, p) ||
+      p->chunk != B * S)
     return SMQA_ERR_WORKSPACE;
   return SMQA_OK;
 }
@@ -464,9 +473,32 @@ int sparse_mqa_bwd_dkv_partials(const void* q, const void* kv, const void* d_o, 
   if (smqa::launch_kv_row_norm(kv, B * S_kv, D, kvn, (hipStream_t)stream) != hipSuccess) return SMQA_ERR_HIP;
   smqa::BwdMainArgs a{q, kv, d_o, topk_idxs, lse, delta, nullptr, nullptr, (const int32_t*)(ws + p.pos),
                       (uint16_t*)(ws + p.stage), (int8_t*)(ws + p.stage_exp), kvn, B, S, S_kv, H, D, topk, scale, 0,
-                      B * S};
+                      B * S, p.ds ? (uint16_t*)(ws + p.ds) : nullptr};
   if (smqa::launch_bwd_main(a, 2, (hipStream_t)stream) != hipSuccess) return SMQA_ERR_HIP;
   return SMQA_OK;
+}
+
+int sparse_mqa_bwd_dkv_dq(const void* kv, const int32_t* topk_idxs, void* dq, void* workspace, size_t workspace_bytes,
+                          int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, float sm_scale,
+                          void* stream) {
+  int st = check_shapes(B, S, S_kv, H, D, topk);
+  if (st) return st;
+  if (!smqa::dq_from_ds(H, D)) return SMQA_ERR_UNSUPPORTED;
+  if (!kv || !topk_idxs || !dq) return SMQA_ERR_NULL;
+  if (!aligned16(kv) || !aligned4(topk_idxs) || !aligned16(dq)) return SMQA_ERR_ALIGN;
+  float scale;
+  if ((st = resolve_scale(sm_scale, D, &scale))) return st;
+  DkvPlan p;
+  if ((st = single_pass_plan(workspace, workspace_bytes, B, S, S_kv, H, D, topk, 0, &p))) return st;
+  const Span sdq{dq, count({B, S, H, D}) * 2};
+  const Span others[] = {{kv, count({B, S_kv, D}) * 2}, {topk_idxs, count({B, S, topk}) * 4},
+                         {workspace, (int64_t)p.end}};
+  for (const Span& s : others)
+    if (overlap(sdq, s)) return SMQA_ERR_ALIAS;
+  char* ws = (char*)workspace;
+  smqa::BwdMainArgs a{nullptr, kv, nullptr, topk_idxs, nullptr, nullptr, dq, nullptr, nullptr, nullptr, nullptr,
+                      nullptr, B, S, S_kv, H, D, topk, scale, 0, B * S, (uint16_t*)(ws + p.ds)};
+  return smqa::launch_bwd_dq_ds(a, (hipStream_t)stream) == hipSuccess ? SMQA_OK : SMQA_ERR_HIP;
 }
 
 int sparse_mqa_bwd_dkv_reduce(void* dkv, int dkv_fp32, void* workspace, size_t workspace_bytes, int64_t B,

@@ -101,6 +101,12 @@ __device__ __forceinline__ float bfp16_scale(f32x16 (&c)[NT], int so, int* es_ou
   *es_out = es > 127 ? 127 : es;
   return sc;
 }
+// Offset (in bf16 elements, within one 64-head x 32-slot block) of dS[head][slot] in the stored dS:
+// the dQ kernel's MFMA B fragments in order, fragment f = 2 (slot >> 4) + (head >> 5) of 64 lanes x 8
+// values, lane (head & 31) + 32 ((slot >> 3) & 1) holding slots 8 (slot >> 3) .. +7 of its head.
+__device__ __forceinline__ int ds_fragment_offset(int head, int slot) {
+  return (2 * (slot >> 4) + (head >> 5)) * 512 + ((head & 31) + 32 * ((slot >> 3) & 1)) * 8 + (slot & 7);
+}
 // Bound on |sm_scale * dS| over a token's valid slots and a block of heads, for the scale of the dS
 // operand of the dKV product: with P <= 1 (the LSE passed in is at least the log of each head's
 // softmax denominator, as the forward's is), |dS| <= |dP| + |Delta|, and |dP| = |<dO_h, kv_t>| <=
@@ -671,6 +677,160 @@ bwd_dq_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv
 }
 
 // ---------------------------------------------------------------------------------------------
+// dQ from the dS that the staged dKV kernel stores (D = 512, blocks of 64 heads): per (token, head
+// block), dQ^T[d, head] = sm_scale * sum over blocks of K^T[d, slot] dS^T[slot, head]. No S or dP
+// recompute: the kernel only gathers the kv tiles and copies dS (bf16, as bwd_dq_ws_kernel rounds it,
+// so the two give the same dQ bit for bit).
+// Eight waves, two per SIMD. Wave w owns d-columns 64 w .. 64 w + 63 of all 64 heads (dQ^T
+// accumulators) and gathers rows w, w + 8, w + 16, w + 24 of every tile; waves 0-3 also copy one
+// 1 KiB fragment each of the block's dS (stored in B-fragment order) into LDS, so dS crosses the
+// vector memory path once per workgroup instead of once per wave. Three buffers of each: during
+// block j the copies for blocks j + 1 and j + 2 are in flight. Every stage issues its vector memory
+// instructions in one fixed order (masked rows and tiles past the end read the zero row; dS copies
+// past the end repeat the last block), so one fixed vmcnt wait per wave at the top of a stage finds
+// that wave's copies for block j complete while later ones stay in flight; the copies are issued so
+// that the compiler adds no waits of its own (dma16_buf_unordered).
+template <int D>
+__global__ void __launch_bounds__(512)
+bwd_dq_ds_kernel(const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx, const uint16_t* __restrict__ ds,
+                 uint16_t* __restrict__ dq, int S, int64_t S_kv, int H, int topk, float sm_scale, int n_hblk,
+                 int token0, int n_tokens) {
+  constexpr int T = 32, HB = 64, NWV = 8;
+  constexpr int ROWB = D * 2, CPR = D / 8, TB = T * ROWB;
+  constexpr int DSB = HB * T * 2;  // bytes of one block's dS
+  constexpr int DW = D / NWV;      // d-columns per wave
+  constexpr int NDT = DW / 32;     // 32-wide d tiles per wave
+  constexpr int NP = T / NWV;      // gather rows per wave and tile
+  static_assert(ROWB == 1024 && NDT * 32 == DW && NP == 4, "one kv row per gather instruction, four per wave");
+  __shared__ __attribute__((aligned(16))) char tile0[TB];
+  __shared__ __attribute__((aligned(16))) char tile1[TB];
+  __shared__ __attribute__((aligned(16))) char tile2[TB];
+  __shared__ __attribute__((aligned(16))) char dsb0[DSB];
+  __shared__ __attribute__((aligned(16))) char dsb1[DSB];
+  __shared__ __attribute__((aligned(16))) char dsb2[DSB];
+
+  const int lane = threadIdx.x & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int item = blockIdx.x;
+  const int64_t ctok = (int64_t)n_tokens - 1 - item / n_hblk;  // heavier (later) tokens first
+  const int64_t token = token0 + ctok;
+  const int hblk = item % n_hblk;
+  const int64_t b = token / S;
+  const int nblk = (topk + T - 1) / T;
+  const int32_t* idx_tok = idx + token * (int64_t)topk;
+  const uint16_t* ds_tok = ds + (ctok * n_hblk + hblk) * (int64_t)nblk * (HB * T);
+  auto load_idx = [&](int blk) -> int32_t {
+    const int t = blk * T + lane;
+    return (blk < nblk && lane < T && t < topk) ? idx_tok[t] : -1;
+  };
+  auto tile_at = [&](int k) -> char* { return k == 0 ? tile0 : (k == 1 ? tile1 : tile2); };
+  auto dsb_at = [&](int k) -> char* { return k == 0 ? dsb0 : (k == 1 ? dsb1 : dsb2); };
+  const char* kv_b = (const char*)(kv + b * S_kv * D);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv_b, (int)(uint32_t)(S_kv * ROWB));
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(g_zero_row_bwd, ROWB);
+  // this wave's NP rows of tile blk's buffer (always NP instructions: masked rows read the zero row),
+  // then (waves 0-3) fragment w of block blk's dS
+  auto copy_block = [&](int blk, int32_t my_idx, char* tile, char* dsbuf) {
+    const uint64_t mask = __ballot(slot_in_range(my_idx, S_kv));
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int k = 0; k < NP; k++) {
+      const int r = wu + NWV * k;
+      const int32_t ri = __builtin_amdgcn_readlane(my_idx, r);
+      const uint32_t voff = (uint32_t)((ln ^ (bwd_swz(r) & (CPR - 1))) << 4);
+      const bool v = (mask >> r) & 1ull;
+      dma16_buf_unordered(v ? rk : rz, voff, v ? (uint32_t)ri * ROWB : 0u, tile + r * ROWB);
+    }
+    if (wu < 4) {
+      const uint16_t* src = ds_tok + (int64_t)(blk < nblk ? blk : nblk - 1) * (HB * T);
+      dma16_buf_unordered(make_rsrc(src, DSB), (uint32_t)(ln << 4), (uint32_t)(wu * 1024), dsbuf + wu * 1024);
+    }
+  };
+  // K^T A fragments: for k-step kk (slots 16 kk .. +15) lane l gets d = 64 w + 32 dt + (l & 31) and
+  // slots 16 kk + 8 (l >> 5) .. +7, from two transposing reads four rows apart
+  const int krow = 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int kch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int hoff = 8 * (lane & 1);
+
+  f32x16 acc[NDT][2];
+#pragma unroll
+  for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[dt][hh][r] = 0.f;
+
+  // indices of blocks j, j + 1, j + 2 at the top of stage j
+  int32_t ia = load_idx(0), ib = load_idx(1), ic = load_idx(2);
+  copy_block(0, ia, tile0, dsb0);
+  __builtin_amdgcn_sched_barrier(0);
+  copy_block(1, ib, tile1, dsb1);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Stage j issues, in this order: the index of block j + 3 (none past the end), then the copies of
+  // block j + 2. At the top of stage j the copies of block j (stage j - 2) are needed; issued after
+  // them are the index of block j + 2 (needed too) and the copies of block j + 1: four row copies and,
+  // on waves 0-3, one dS copy.
+  auto stage = [&](auto buf_tag, int j) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    if (wu < 4) __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5); lgkmcnt and expcnt at their maxima
+    else __builtin_amdgcn_s_waitcnt(0x0F74);         // vmcnt(4)
+    lds_barrier();  // every wave's copies of block j; every wave done with the buffers of block j - 1
+    const uint64_t mask = __ballot(slot_in_range(ia, S_kv));
+    const int32_t id = load_idx(j + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    copy_block(j + 2, ic, tile_at((BUF + 2) % 3), dsb_at((BUF + 2) % 3));  // into the buffers of block j - 1
+    __builtin_amdgcn_sched_barrier(0);
+    if (mask) {
+      const char* tile = tile_at(BUF);
+      const char* dsp = dsb_at(BUF) + 16 * lane;
+#pragma unroll
+      for (int kk = 0; kk < 2; kk++) {
+        bf16x8 ka[NDT], dv[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) dv[hh] = lds_load16(dsp + (2 * kk + hh) * 1024);
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt++) {
+          const int r0 = 16 * kk + krow, c = wu * (DW / 8) + 4 * dt + kch;
+          const char* p0 = tile + r0 * ROWB + ((c ^ (bwd_swz(r0) & (CPR - 1))) << 4) + hoff;
+          const char* p1 = tile + (r0 + 4) * ROWB + ((c ^ (bwd_swz(r0 + 4) & (CPR - 1))) << 4) + hoff;
+          ka[dt] = join_tr(lds_load_tr(p0), lds_load_tr(p1));
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt++) {
+          acc[dt][0] = mfma32(ka[dt], dv[0], acc[dt][0]);
+          acc[dt][1] = mfma32(ka[dt], dv[1], acc[dt][1]);
+        }
+      }
+    }
+    ia = ib;
+    ib = ic;
+    ic = id;
+  };
+  for (int j = 0; j < nblk; j += 3) {
+    stage(IntTag<0>{}, j);
+    if (j + 1 < nblk) stage(IntTag<1>{}, j + 1);
+    if (j + 2 < nblk) stage(IntTag<2>{}, j + 2);
+  }
+  wait_all_mem();  // no copy may still write LDS when the workgroup ends
+  // dQ = sm_scale * (dS K), bf16; dQ^T C layout: lane holds head 32 hh + (lane & 31),
+  // d = 64 w + 32 dt + 8 (r >> 2) + 4 (lane >> 5) + (r & 3)
+#pragma unroll
+  for (int hh = 0; hh < 2; hh++) {
+    uint16_t* row = dq + (token * H + hblk * HB + 32 * hh + (lane & 31)) * (int64_t)D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; r4++) {
+        const int d = wu * DW + 32 * dt + 8 * r4 + 4 * (lane >> 5);
+        *(uint2*)(row + d) = pack4_bf16(acc[dt][hh][4 * r4] * sm_scale, acc[dt][hh][4 * r4 + 1] * sm_scale,
+                                        acc[dt][hh][4 * r4 + 2] * sm_scale, acc[dt][hh][4 * r4 + 3] * sm_scale);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // STAGED: every valid slot's dKV row goes to its staging row (pos, stage, stage_exp); otherwise it
 // is added into the fp32 accumulator dkv_acc with fp32 atomics (the workspace-free variant).
 template <int D, int NW, bool STAGED>
@@ -1158,7 +1318,7 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
                   const int32_t* __restrict__ idx, const float* __restrict__ lse, const float* __restrict__ delta,
                   const int32_t* __restrict__ pos, uint16_t* __restrict__ stage, int8_t* __restrict__ stage_exp,
                   const float* __restrict__ row_norm, int S, int64_t S_kv, int H, int topk, float sm_scale,
-                  float scale_log2, int n_hblk, int token0, int n_tokens) {
+                  float scale_log2, int n_hblk, int token0, int n_tokens, uint16_t* __restrict__ ds_out) {
   using C = BwdCommon<D, NW>;
   using G = BwdGather<D, NW>;
   constexpr int T = C::T;
@@ -1326,6 +1486,11 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     int sc_off[C::KSJ];
     bwd_score_offsets<D>(lane, sc_off);
     const int pw_off = (hrow * T + 4 * g) * 2;  // P/dS writes: head hrow, slots 16 mt + 4 g .. +3
+    // dS output, per (chunk token, head block, 32-slot block) in the order of the dQ kernel's MFMA B
+    // fragments: fragment f = 2 kk + hh is 64 lanes x 8 values, lane l holding head 32 hh + (l & 31)
+    // and slots 16 kk + 8 (l >> 5) .. +7 (ds_fragment_offset). This lane's values (head hrow, slots
+    // 16 mt + 4 g .. +3) are 8 contiguous bytes of fragment 2 mt + (hrow >> 5).
+    const int64_t ds_off = (ctok * n_hblk + hblk) * (int64_t)nblk * (HB * T) + ds_fragment_offset(hrow, 4 * g);
     const G gather((const char*)(kv + b * S_kv * D), S_kv);
     int32_t idx_cur = load_idx(0);
     uint64_t mask_cur = __ballot(slot_in_range(idx_cur, S_kv));
@@ -1371,6 +1536,10 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
               ds[r] = __builtin_amdgcn_fmed3f(
                   __builtin_amdgcn_ldexpf(sm_scale * p[r] * (dpacc[mt][r] - delta_h), sqo), -65504.f, 65504.f);
             f16_hilo4(ds, (uint2*)(pw + 32 * mt), (uint2*)(pw + 32 * mt + SB));
+            if (ds_out)  // dS = P (dP - Delta) in bf16 for the dQ kernel (bwd_dq_ds_kernel)
+              *(uint2*)(ds_out + ds_off + (int64_t)blk * (HB * T) + mt * 1024) =
+                  pack4_bf16(p[0] * (dpacc[mt][0] - delta_h), p[1] * (dpacc[mt][1] - delta_h),
+                             p[2] * (dpacc[mt][2] - delta_h), p[3] * (dpacc[mt][3] - delta_h));
             const f16x2 p01 = __builtin_convertvector((f32x2){p[0], p[1]}, f16x2);
             const f16x2 p23 = __builtin_convertvector((f32x2){p[2], p[3]}, f16x2);
             *(uint2*)(pw + 32 * mt + 2 * SB) =
@@ -1861,7 +2030,7 @@ static hipError_t launch_bwd_main_t(const BwdMainArgs& a, int which, hipStream_t
       hipLaunchKernelGGL((bwd_dkv_ws_kernel<D, NW>), dim3((unsigned)(a.n_chunk * n_hblk)), dim3(NW * 128), 0, st,
                          (const uint16_t*)a.q, (const uint16_t*)a.kv, (const uint16_t*)a.d_o, a.idx, a.lse, a.delta,
                          a.pos, a.stage, a.stage_exp, a.row_norm, (int)a.S, a.S_kv, (int)a.H, (int)a.topk, a.sm_scale,
-                         sl2, n_hblk, (int)a.token0, (int)a.n_chunk);
+                         sl2, n_hblk, (int)a.token0, (int)a.n_chunk, a.ds);
     else
       hipLaunchKernelGGL((bwd_dkv_kernel<D, NW, true>), dim3((unsigned)(a.n_chunk * n_hblk)), dim3(NW * 64), 0, st,
                          (const uint16_t*)a.q, (const uint16_t*)a.kv, (const uint16_t*)a.d_o, a.idx, a.lse, a.delta,
@@ -1873,6 +2042,15 @@ static hipError_t launch_bwd_main_t(const BwdMainArgs& a, int which, hipStream_t
                        a.dkv_accum, nullptr, nullptr, nullptr, nullptr, (int)a.S, a.S_kv, (int)a.H, (int)a.topk,
                        a.sm_scale, sl2, n_hblk, (int)a.token0, (int)a.n_chunk);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_ds(const BwdMainArgs& a, hipStream_t st) {
+  if (!dq_from_ds(a.H, a.D) || !a.ds) return hipErrorInvalidValue;
+  const int n_hblk = (int)(a.H / 64);
+  hipLaunchKernelGGL((bwd_dq_ds_kernel<512>), dim3((unsigned)(a.n_chunk * n_hblk)), dim3(512), 0, st,
+                     (const uint16_t*)a.kv, a.idx, (const uint16_t*)a.ds, (uint16_t*)a.dq, (int)a.S, a.S_kv,
+                     (int)a.H, (int)a.topk, a.sm_scale, n_hblk, (int)a.token0, (int)a.n_chunk);
   return hipGetLastError();
 }
 

@@ -73,6 +73,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, char* lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SMQA_LDS void*)(SMQA_LDS char*)lds_base, 16, voff, soff, 0, 0);
 }
+// dma16_buf whose LDS destination the compiler cannot trace to an LDS variable. The compiler then
+// adds no wait of its own before later LDS reads (it cannot tell which reads the copy feeds), so the
+// caller must order every read of the destination after the copy itself: an explicit vmcnt wait for
+// the copy, then a barrier for the other waves' copies. Used where several tiles are in flight.
+__device__ __forceinline__ void dma16_buf_unordered(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                                    char* lds_base) {
+  uint32_t a = (uint32_t)(uintptr_t)(SMQA_LDS char*)lds_base;
+  asm volatile("" : "+s"(a));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SMQA_LDS void*)(uintptr_t)a, 16, voff, soff, 0, 0);
+}
 // Workgroup barrier that publishes this wave's LDS writes only. __syncthreads() also waits for
 // every outstanding global access, including tile gathers still in flight for a later block; this
 // waits for the LDS counter alone, and the empty asm statements keep the compiler from moving

@@ -29,14 +29,24 @@ struct BwdMainArgs {
   void* dq;
   float* dkv_accum;       // atomic mode: pre-zeroed fp32 accumulator [B,S_kv,D]
   const int32_t* pos;     // staging mode: staging row of each slot of the chunk (-1 if masked)
-  uint16_t* stage;        // staging mode: contribution rows (fp16); nullptr selects atomic mode
+  uint16_t* stage;        // staging mode: contribution rows (int16 block floating point); nullptr: atomic mode
   int8_t* stage_exp;      // staging mode: one power-of-two exponent per row segment (stage_segments)
   const float* row_norm;  // staging mode: |kv_r| of every kv row (launch_kv_row_norm)
   int64_t B, S, S_kv, H, D, topk;
   float sm_scale;
   int64_t token0;         // first token of the chunk (dKV kernel)
   int64_t n_chunk;        // tokens in the chunk (dKV kernel)
+  uint16_t* ds = nullptr; // staging mode at D = 512 with 64-head blocks: the dKV kernel also stores
+                          // dS (bf16, [chunk token][head block][32-slot block][64][32]) here
 };
+
+// The dS store and the dQ kernel that reads it (bwd_dq_ds_kernel) serve D = 512 with H a multiple of
+// 64; other shapes compute dQ with the recompute kernel.
+inline bool dq_from_ds(int64_t H, int64_t D) { return D == 512 && H % 64 == 0; }
+// Bytes of the dS store for n_chunk tokens.
+inline int64_t ds_bytes(int64_t n_chunk, int64_t H, int64_t topk) {
+  return n_chunk * (H / 64) * ((topk + 31) / 32) * 64 * 32 * 2;
+}
 
 // Heads handled by one backward workgroup, and workgroups per token.
 inline int bwd_heads_per_wg(int64_t H) { return H >= 64 ? 64 : (int)H; }
@@ -58,6 +68,9 @@ hipError_t launch_bwd_dsink(const float* lse, const float* delta, const float* s
                             int64_t H, hipStream_t st);
 // which: 1 = dQ kernel (all tokens), 2 = dKV kernel (chunk; atomic or staging mode), 3 = both.
 hipError_t launch_bwd_main(const BwdMainArgs& a, int which, hipStream_t st);
+// dQ of the chunk's tokens [a.token0, a.token0 + a.n_chunk) from the dS the dKV kernel stored in a.ds
+// (dq_from_ds shapes only).
+hipError_t launch_bwd_dq_ds(const BwdMainArgs& a, hipStream_t st);
 // Staging-row assignment for the tokens [token0, token0 + n_chunk). `plan` holds 3 *
 // dkv_bitmap_words 32-bit words: {bitmap word, pair count} per word, then the cursors (written or
 // cleared here). Marks every valid
