@@ -18,9 +18,17 @@ dS^T Q and P^T dO). `traffic` is that kernel's HBM bytes per launch from the roc
 and WRITE_SIZE summary under profiles/, scaled by the same counters' reading for a copy of known
 size, and null once the kernel source differs from the one the counters were taken on.
 
+Beside the headline line's warm-cache step time it reports a cold-cache step time (each step
+preceded by a 1 GiB write that evicts L2 and the Infinity Cache), the rate counted over all
+B*S*topk slots (nominal) next to the valid pairs, and, as `gather_bound`, the same step timed on
+the batched gather workload (B=4, S=2048, S_kv=65536, uniform indices with masked slots) with each
+gathering kernel's row-gather rate against the HBM peak.
+
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                  [--calibration-copy]
+                  [--calibration-copy] [--cold-steps C] [--gather-workload NAME] [--gather-steps G]
   python bench.py --summarize-pmc FETCH.csv WRITE.csv --out profiles/hbm_traffic_<workload>.md
+  python bench.py --summarize-trace KERNEL_STATS.csv --out profiles/kernel_trace_<workload>.md
+  python bench.py --summarize-counters PASS1.csv [PASS2.csv ...] --out profiles/counters_<workload>.md
 """
 from __future__ import annotations
 
@@ -44,9 +52,16 @@ SINGLE = {
     "bwd_dkv_partials": ("smqa::bwd_dkv_", ("bwd.hip", "device_common.h"), 8),
     "bwd_dkv_dq": ("smqa::bwd_dq_ds_", ("bwd.hip", "device_common.h"), 2),  # dS K from the stored dS
 }
+GATHER_KERNELS = ("fwd", "bwd_dkv_partials", "bwd_dkv_dq")  # each gathers one kv row per valid pair
+FLUSH_BYTES = 1 << 30        # written before each cold-cache step (L2 4 MiB per XCD, Infinity Cache 256 MiB)
 CALIB_BYTES = 1 << 30        # the calibration copy reads and writes this many bytes
 CALIB_KERNEL = "MulFunctor"  # part of the name of the kernel torch.mul(src, 1.0, out=dst) runs
 REPO = os.path.dirname(os.path.abspath(__file__))
+# bench arguments of every profiled run (a short run: two timed steps of the one workload)
+PROFILE_ARGS = "--steps 2 --warmup 1 --no-cpu-baseline --cold-steps 0 --gather-steps 0"
+# kernels the counter summary reports, in this order
+COUNTER_KERNELS = ("fwd_ws_kernel", "bwd_dkv_ws_kernel", "bwd_dq_ds_kernel", "reduce_rows_kernel", "delta_kernel",
+                   "mark_kernel", "position_kernel")
 
 
 def parse():
@@ -60,9 +75,18 @@ def parse():
                    help="run one 1 GiB copy kernel before the warmup (reference for the HBM byte counters)")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write the HBM traffic summary from two rocprofv3 --pmc counter_collection.csv files")
-    p.add_argument("--out", help="output file of --summarize-pmc")
+    p.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
+                   help="write the kernel-time summary from a rocprofv3 --kernel-trace --stats kernel_stats.csv")
+    p.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                   help="write the counter summary from rocprofv3 --pmc counter_collection.csv files (one per pass)")
+    p.add_argument("--out", help="output file of --summarize-*")
     p.add_argument("--serial", action="store_true",
                    help="run every kernel on one stream (default: the dKV staging plan on a side stream)")
+    p.add_argument("--cold-steps", type=int, default=5,
+                   help="steps timed after a cache-evicting write each (0: none)")
+    p.add_argument("--gather-workload", default="gather_b4_skv64k",
+                   help="workload of the gather_bound object ('none': skip it)")
+    p.add_argument("--gather-steps", type=int, default=5)
     return p.parse_args()
 
 
@@ -200,9 +224,9 @@ def summarize_pmc(fetch_csv: str, write_csv: str, out_path: str, workload: str) 
              f"each scaled by the same counter's reading for a copy kernel that reads and writes {CALIB_BYTES} bytes.",
              "", "Commands (from the repository root on one MI355X; `<out>` an output directory):", "", "```",
              f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/fetch -o pmc -- python bench.py --workload "
-             f"{workload} --steps 2 --warmup 1 --no-cpu-baseline --calibration-copy",
+             f"{workload} {PROFILE_ARGS} --calibration-copy",
              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/write -o pmc -- python bench.py --workload "
-             f"{workload} --steps 2 --warmup 1 --no-cpu-baseline --calibration-copy",
+             f"{workload} {PROFILE_ARGS} --calibration-copy",
              "python bench.py --summarize-pmc <out>/fetch/pmc_counter_collection.csv "
              f"<out>/write/pmc_counter_collection.csv --workload {workload} --out <this file>", "```", "",
              "| step | kernel | fetch (GB) | write (GB) |", "|---|---|---|---|"]
@@ -230,6 +254,133 @@ def traffic_for(step: str, workload: str):
     if k["source_sha256"] != source_sha256(SINGLE[step][1]):
         return None
     return k["fetch_bytes"] + k["write_bytes"]
+
+
+def summarize_trace(stats_csv: str, out_path: str, workload: str) -> None:
+    """Kernel times of a rocprofv3 --kernel-trace --stats run as a table (average over dispatches)."""
+    import csv
+
+    rows = list(csv.DictReader(open(stats_csv)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [f"# Kernel trace: {workload}", "",
+             "rocprofv3 kernel-trace statistics of a short bench run (warmup and timed steps; every dispatch).", "",
+             "Command (from the repository root on one MI355X; `<out>` an output directory):", "", "```",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o trace -- python bench.py "
+             f"--workload {workload} {PROFILE_ARGS}",
+             f"python bench.py --workload {workload} --summarize-trace <out>/trace_kernel_stats.csv --out <this file>",
+             "```", "", "| kernel | calls | avg (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].split("(")[0].replace("void ", "")
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    lines += ["", "Library steps to kernels: fwd = `fwd_ws_kernel`; bwd_preprocess = `delta_kernel`;",
+              "bwd_dkv_prepare = `fill_zero_kernel` + `mark_kernel` + three scan kernels + `position_kernel`;",
+              "bwd_dkv_partials = `kv_row_norm_kernel` + `bwd_dkv_ws_kernel`; bwd_dkv_dq = `bwd_dq_ds_kernel`;",
+              "bwd_dkv_reduce = `reduce_rows_kernel`. The staging plan (bwd_dkv_prepare) runs on a second stream",
+              "beside the forward and the preprocess, so their durations include that overlap."]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def counter_table(paths):
+    """{kernel: {counter: mean over dispatches}} and {kernel: mean duration ns} from --pmc csv files."""
+    import csv
+    from collections import defaultdict
+
+    vals = defaultdict(lambda: defaultdict(list))
+    dur = defaultdict(list)
+    passes = []
+    for p in paths:
+        names = []
+        for r in csv.DictReader(open(p)):
+            k = next((k for k in COUNTER_KERNELS if k in r["Kernel_Name"]), None)
+            if r["Counter_Name"] not in names:
+                names.append(r["Counter_Name"])
+            if k is None:
+                continue
+            vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            dur[k].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        passes.append(names)
+    mean = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in vals.items()}
+    return mean, {k: sum(v) / len(v) for k, v in dur.items()}, passes
+
+
+def derived_counters(a: dict, dur_ns: float) -> dict:
+    """Utilisations from raw counter means of one kernel. GRBM_GUI_ACTIVE is summed over the 8 XCDs,
+    so a kernel's clock count is a eighth of it; per-CU counters (TA, TD, TCP, SQ_LDS_*) are summed over
+    256 CUs and SQ_VALU_MFMA_BUSY_CYCLES over their 1024 SIMDs."""
+    out = {}
+    if "GRBM_GUI_ACTIVE" not in a:
+        return out
+    cyc = a["GRBM_GUI_ACTIVE"] / 8
+    out["clock_GHz"] = cyc / dur_ns
+    per_cu = lambda c: a[c] / (cyc * 256)  # noqa: E731
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in a:
+        out["mfma_busy"] = a["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * 1024)
+    if "VmemLatency" in a:
+        out["vmem_latency_cycles"] = a["VmemLatency"]
+    if "SQ_WAVE_CYCLES" in a and "SQ_WAIT_INST_ANY" in a:
+        out["wave_wait_dependency"] = a["SQ_WAIT_INST_ANY"] / a["SQ_WAVE_CYCLES"]
+    if "SQ_WAVE_CYCLES" in a and "SQ_ACTIVE_INST_ANY" in a:
+        out["wave_issuing"] = a["SQ_ACTIVE_INST_ANY"] / a["SQ_WAVE_CYCLES"]
+    for c, n in (("TA_TA_BUSY_sum", "ta_busy"), ("TA_ADDR_STALLED_BY_TC_CYCLES_sum", "ta_stalled_by_tc"),
+                 ("TD_TD_BUSY_sum", "td_busy"), ("TD_TC_STALL_sum", "td_tc_stall"),
+                 ("SQ_LDS_IDX_ACTIVE", "lds_active")):
+        if c in a:
+            out[n] = per_cu(c)
+    if "TCC_HIT_sum" in a and "TCC_MISS_sum" in a:
+        out["l2_hit"] = a["TCC_HIT_sum"] / max(a["TCC_HIT_sum"] + a["TCC_MISS_sum"], 1.0)
+    if "SQ_LDS_BANK_CONFLICT" in a and "SQ_LDS_IDX_ACTIVE" in a:
+        out["lds_bank_conflict"] = a["SQ_LDS_BANK_CONFLICT"] / max(a["SQ_LDS_IDX_ACTIVE"], 1.0)
+    if "TCP_TCC_READ_REQ_LATENCY_sum" in a and "TCP_TCC_READ_REQ_sum" in a:
+        out["l1_l2_read_latency_cycles"] = a["TCP_TCC_READ_REQ_LATENCY_sum"] / max(a["TCP_TCC_READ_REQ_sum"], 1.0)
+    if "TCP_UTCL1_TRANSLATION_MISS_sum" in a and "TCP_UTCL1_REQUEST_sum" in a:
+        out["utcl1_miss"] = a["TCP_UTCL1_TRANSLATION_MISS_sum"] / max(a["TCP_UTCL1_REQUEST_sum"], 1.0)
+    return out
+
+
+DERIVED_DOC = {
+    "clock_GHz": "GRBM_GUI_ACTIVE / 8 over the dispatch duration",
+    "mfma_busy": "SQ_VALU_MFMA_BUSY_CYCLES / (clocks x 1024 SIMDs)",
+    "vmem_latency_cycles": "VmemLatency (derived: average vector-memory instruction latency)",
+    "wave_wait_dependency": "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES",
+    "wave_issuing": "SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES",
+    "ta_busy": "TA_TA_BUSY_sum / (clocks x 256 CUs)",
+    "ta_stalled_by_tc": "TA_ADDR_STALLED_BY_TC_CYCLES_sum / (clocks x 256)",
+    "td_busy": "TD_TD_BUSY_sum / (clocks x 256)",
+    "td_tc_stall": "TD_TC_STALL_sum / (clocks x 256)",
+    "lds_active": "SQ_LDS_IDX_ACTIVE / (clocks x 256)",
+    "lds_bank_conflict": "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE",
+    "l2_hit": "TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)",
+    "l1_l2_read_latency_cycles": "TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum",
+    "utcl1_miss": "TCP_UTCL1_TRANSLATION_MISS_sum / TCP_UTCL1_REQUEST_sum",
+}
+
+
+def summarize_counters(paths, out_path: str, workload: str) -> None:
+    """Per-kernel utilisation table from rocprofv3 --pmc passes over the same short bench run."""
+    mean, dur, passes = counter_table(paths)
+    lines = [f"# Hardware counters: {workload}", "",
+             "rocprofv3 --pmc passes (one run each, counters averaged over every dispatch of a kernel), over the",
+             "same short bench run. Commands (from the repository root on one MI355X; `<out>` an output directory):",
+             "", "```"]
+    for i, names in enumerate(passes):
+        lines.append(f"rocprofv3 --pmc {' '.join(names)} --output-format csv -d <out>/p{i} -o pmc -- "
+                     f"python bench.py --workload {workload} {PROFILE_ARGS}")
+    lines.append("python bench.py --workload " + workload + " --summarize-counters "
+                 + " ".join(f"<out>/p{i}/pmc_counter_collection.csv" for i in range(len(passes))) + " --out <this file>")
+    lines += ["```", ""]
+    table = {k: derived_counters(mean[k], dur[k]) for k in COUNTER_KERNELS if k in mean}
+    cols = [c for c in DERIVED_DOC if any(c in v for v in table.values())]
+    lines += ["| kernel | avg (us) | " + " | ".join(cols) + " |", "|---|---|" + "---|" * len(cols)]
+    for k, v in table.items():
+        cells = [(f"{v[c]:.0f}" if c.endswith("cycles") else f"{v[c]:.3f}") if c in v else "" for c in cols]
+        lines.append(f"| `{k}` | {dur[k] / 1e3:.0f} | " + " | ".join(cells) + " |")
+    lines += ["", "Columns:", ""] + [f"- `{c}`: {DERIVED_DOC[c]}" for c in cols]
+    lines += ["", "Raw means per dispatch:", "", "```json",
+              json.dumps({k: {c: round(x, 1) for c, x in sorted(mean[k].items())} for k in table}, indent=1), "```"]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
 
 
 def cpu_baseline(x, w, valid_per_token):
@@ -263,9 +414,84 @@ def cpu_baseline(x, w, valid_per_token):
     flops = 4 * w.H * w.D * pairs + 6 * w.H * w.D * pairs + 10 * w.H * w.D * refs
     secs = t3 - t0
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            **cpu_info(),
             "sample": (f"fp32 oracle: forward + dQ for the last {n_tok} tokens ({pairs} valid pairs) and dKV for "
                        f"kv rows 0..{len(rows) - 1} ({refs} references); {secs:.1f} s "
                        f"(fwd {t1 - t0:.1f} s, dQ {t2 - t1:.1f} s, dKV {t3 - t2:.1f} s)")}
+
+
+def cpu_info():
+    """CPU model and the cores this process may run on (its affinity mask)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    aff = sorted(os.sched_getaffinity(0))
+    return {"cpu_model": model, "affinity_cores": len(aff), "affinity": f"{aff[0]}-{aff[-1]}" if aff else ""}
+
+
+def measure(smqa, w, x, steps, warmup, overlap=True, cold_steps=0, calibration_copy=False):
+    """Warm step time and per-kernel event times over `steps` steps (after `warmup`), then, if
+    cold_steps, the step time with a cache-evicting write before each step (outside the timed span)."""
+    step = Step(smqa, w, x, overlap=overlap)
+    if calibration_copy:
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(warmup):
+        step.run(timed=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        step.run(timed=True)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    res = {"ms_step": start.elapsed_time(end) / steps, "ms": step.kernel_ms(), "wall": wall}
+    if cold_steps > 0:
+        flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        step.events = []
+        tot = 0.0
+        for _ in range(cold_steps):
+            flush.zero_()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            step.run(timed=True)
+            b.record()
+            torch.cuda.synchronize()
+            tot += a.elapsed_time(b)
+        res["cold_ms_step"] = tot / cold_steps
+        res["cold_ms"] = step.kernel_ms()
+        del flush
+    del step
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def gather_rates(w, n_valid, ms):
+    """Row-gather rate of each gathering kernel (one D-wide bf16 kv row per valid pair) and the staging
+    rows the reduce reads (D int16 values per valid pair and 64-head block), in GB/s and as a fraction
+    of the HBM peak. Rows served from L2 or the Infinity Cache count the same, so a fraction above 1
+    is possible."""
+    row = w.D * 2
+    out = {}
+    for k in GATHER_KERNELS:
+        gbs = n_valid * row / (ms[k] * 1e-3) / 1e9
+        out[k] = {"GBps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    gbs = n_valid * max(1, w.H // 64) * row / (ms["bwd_dkv_reduce"] * 1e-3) / 1e9
+    out["bwd_dkv_reduce"] = {"GBps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                             "bytes": "staging rows read"}
+    return out
 
 
 def main():
@@ -274,6 +500,14 @@ def main():
         if not args.out:
             raise SystemExit("--summarize-pmc needs --out")
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.out, args.workload)
+        return
+    if args.summarize_trace or args.summarize_counters:
+        if not args.out:
+            raise SystemExit("--summarize-trace / --summarize-counters need --out")
+        if args.summarize_trace:
+            summarize_trace(args.summarize_trace, args.out, args.workload)
+        else:
+            summarize_counters(args.summarize_counters, args.out, args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU (got --gpus {args.gpus}): the kernels run on a single device and "
@@ -290,28 +524,10 @@ def main():
     x = syn.workload_inputs(w)
     valid = ((x["topk_idxs"] >= 0) & (x["topk_idxs"] < w.S_kv)).sum(-1).view(-1)
     n_valid = int(valid.sum())
-    step = Step(smqa, w, x, overlap=not args.serial)
-    if args.calibration_copy:
-        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
-    for _ in range(args.warmup):
-        step.run(timed=False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        step.run(timed=True)
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    # per-kernel event times (each kernel bracketed on the stream it runs on)
-    ms = step.kernel_ms()
-    ms_step = total_ms / args.steps
+    n_nominal = w.B * w.S * w.topk
+    r = measure(smqa, w, x, args.steps, args.warmup, overlap=not args.serial, cold_steps=args.cold_steps,
+                calibration_copy=args.calibration_copy)
+    ms, ms_step = r["ms"], r["ms_step"]
 
     HD = w.H * w.D
     fl_fwd = 4 * HD * n_valid
@@ -333,9 +549,14 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
+        "operand_dtypes": ("bf16 inputs, outputs and MFMA operands; fp16 (hi + lo split) P and dS operands in the "
+                           "dKV products; fp32 accumulation; int16 block floating point dKV staging rows"),
         "data": "synthetic",
         "config": dict(w.describe(), valid_pairs=n_valid, step="forward + backward",
                        schedule="serial" if args.serial else "dkv prepare on a side stream"),
+        "flops_per_valid_pair": {"fwd": 4 * HD, "bwd": 10 * HD},
+        "nominal_pairs": n_nominal,
+        "nominal_tflops": round((fl_fwd + fl_bwd) / n_valid * n_nominal / (ms_step * 1e-3) / 1e12, 3),
         "fwd_ms": round(ms_fwd, 4),
         "bwd_ms": round(ms_bwd, 4),
         "fwd_tflops": round(fl_fwd / (ms_fwd * 1e-3) / 1e12, 2),
@@ -346,7 +567,7 @@ def main():
         "fwd_gather_GBps": round(n_valid * 2 * w.D / (ms_fwd * 1e-3) / 1e9, 1),
         "fwd_gather_frac_hbm": round(n_valid * 2 * w.D / (ms_fwd * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "kernel_ms": {k: round(v, 4) for k, v in ms.items()},
-        "wall_s_timed": round(wall, 3),
+        "wall_s_timed": round(r["wall"], 3),
         "roofline": {
             "kernel": dom,
             "bound": "mfma",
@@ -357,9 +578,30 @@ def main():
             "traffic": traffic_for(dom, args.workload),
         },
     }
-    # staged dKV rows written by the partials kernel: D fp16 values per valid pair and head block
+    if "cold_ms_step" in r:
+        out["cold_cache"] = {"steps": args.cold_steps, "ms_per_step": round(r["cold_ms_step"], 4),
+                             "tflops": round((fl_fwd + fl_bwd) / (r["cold_ms_step"] * 1e-3) / 1e12, 3),
+                             "kernel_ms": {k: round(v, 4) for k, v in r["cold_ms"].items()},
+                             "flush": f"{FLUSH_BYTES >> 20} MiB write before each step, outside the timed span"}
+    # staged dKV rows written by the partials kernel: D int16 values per valid pair and head block
     out["dkv_staging_write_TBps"] = round(n_valid * (w.H // min(w.H, 64)) * 2 * w.D / (ms["bwd_dkv_partials"] * 1e-3)
                                           / 1e12, 3)
+    if args.gather_workload != "none" and args.gather_steps > 0:
+        wg = syn.WORKLOADS[args.gather_workload]
+        xg = syn.workload_inputs(wg)
+        ng = int(((xg["topk_idxs"] >= 0) & (xg["topk_idxs"] < wg.S_kv)).sum())
+        rg = measure(smqa, wg, xg, args.gather_steps, 1, overlap=not args.serial)
+        del xg
+        HDg = wg.H * wg.D
+        out["gather_bound"] = {
+            "config": dict(wg.describe(), valid_pairs=ng, nominal_pairs=wg.B * wg.S * wg.topk),
+            "steps": args.gather_steps, "warmup": 1,
+            "ms_per_step": round(rg["ms_step"], 4),
+            "tflops": round(14 * HDg * ng / (rg["ms_step"] * 1e-3) / 1e12, 3),
+            "kernel_ms": {k: round(v, 4) for k, v in rg["ms"].items()},
+            "gather": gather_rates(wg, ng, rg["ms"]),
+            "hbm_peak_GBps": PEAK_HBM_GBS,
+        }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, w, valid)
     print(json.dumps(out), flush=True)

@@ -708,6 +708,7 @@ bwd_dq_ds_kernel(const uint16_t* __restrict__ kv, const int32_t* __restrict__ id
   __shared__ __attribute__((aligned(16))) char dsb0[DSB];
   __shared__ __attribute__((aligned(16))) char dsb1[DSB];
   __shared__ __attribute__((aligned(16))) char dsb2[DSB];
+  __shared__ int last_s[NWV];
 
   const int lane = threadIdx.x & 63;
   const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -716,9 +717,34 @@ bwd_dq_ds_kernel(const uint16_t* __restrict__ kv, const int32_t* __restrict__ id
   const int64_t token = token0 + ctok;
   const int hblk = item % n_hblk;
   const int64_t b = token / S;
-  const int nblk = (topk + T - 1) / T;
+  const int nblk_all = (topk + T - 1) / T;  // blocks of the dS store layout
   const int32_t* idx_tok = idx + token * (int64_t)topk;
-  const uint16_t* ds_tok = ds + (ctok * n_hblk + hblk) * (int64_t)nblk * (HB * T);
+  const uint16_t* ds_tok = ds + (ctok * n_hblk + hblk) * (int64_t)nblk_all * (HB * T);
+  // The stages run over the blocks up to the last one holding a valid slot (a selection shorter than
+  // topk is padded with masked slots at its end; the dKV kernel stores no dS for blocks past it). The
+  // index scan's loads go out first, so the wait for them covers nothing else.
+  int last = -1;
+  {
+    constexpr int U = 4;
+    for (int t0 = threadIdx.x; t0 < topk; t0 += U * NWV * 64) {
+      int32_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int t = t0 + u * NWV * 64;
+        v[u] = t < topk ? idx_tok[t] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++)
+        if (slot_in_range(v[u], S_kv)) last = max(last, t0 + u * NWV * 64);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) last = max(last, __shfl_xor(last, o));
+    if (lane == 0) last_s[wu] = last;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int k = 0; k < NWV; k++) last = max(last, last_s[k]);
+  const int nblk = __builtin_amdgcn_readfirstlane((last + T) / T);
   auto load_idx = [&](int blk) -> int32_t {
     const int t = blk * T + lane;
     return (blk < nblk && lane < T && t < topk) ? idx_tok[t] : -1;
@@ -743,7 +769,7 @@ bwd_dq_ds_kernel(const uint16_t* __restrict__ kv, const int32_t* __restrict__ id
       dma16_buf_unordered(v ? rk : rz, voff, v ? (uint32_t)ri * ROWB : 0u, tile + r * ROWB);
     }
     if (wu < 4) {
-      const uint16_t* src = ds_tok + (int64_t)(blk < nblk ? blk : nblk - 1) * (HB * T);
+      const uint16_t* src = ds_tok + (int64_t)(blk < nblk_all ? blk : nblk_all - 1) * (HB * T);
       dma16_buf_unordered(make_rsrc(src, DSB), (uint32_t)(ln << 4), (uint32_t)(wu * 1024), dsbuf + wu * 1024);
     }
   };
@@ -1338,6 +1364,7 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   __shared__ __attribute__((aligned(16))) char pds0[3 * SB];
   __shared__ __attribute__((aligned(16))) char pds1[3 * SB];
   __shared__ float red[4][NWT];
+  __shared__ int red_last[NWT];
   // staging-store transpose per product wave, as in bwd_dkv_kernel (one exponent segment = DW)
   constexpr int SEGW = NDT * 32;
   constexpr int NSEG = D / SEGW;
@@ -1354,7 +1381,10 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   const int64_t token = token0 + ctok;
   const int hblk = item % n_hblk;
   const int64_t b = token / S;
-  const int nblk = (topk + T - 1) / T;
+  const int nblk_all = (topk + T - 1) / T;  // blocks of the dS store layout
+  // blocks processed: those up to the last one holding a valid slot (set after the index scan below;
+  // a selection shorter than topk is padded with masked slots at its end)
+  int nblk = nblk_all;
   const int32_t* idx_tok = idx + token * (int64_t)topk;
   auto load_idx = [&](int blk) -> int32_t {
     const int t = blk * T + lane;
@@ -1380,6 +1410,7 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     const int64_t base = (token * H + (int64_t)hblk * HB) * D;
     float mq = 0.f, md = 0.f, mv = 0.f;
     float mdl = threadIdx.x < HB ? fabsf(delta[token * H + (int64_t)hblk * HB + threadIdx.x]) : 0.f;
+    int last = -1;  // last valid slot
     const float* nb = row_norm + b * S_kv;
     constexpr int U = 8;  // independent index loads, then independent norm loads
     for (int t0 = threadIdx.x; t0 < topk; t0 += U * NWT * 64) {
@@ -1391,7 +1422,10 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
       }
 #pragma unroll
       for (int u = 0; u < U; u++)
-        if (slot_in_range(v[u], S_kv)) mv = fmaxf(mv, nb[v[u]]);
+        if (slot_in_range(v[u], S_kv)) {
+          mv = fmaxf(mv, nb[v[u]]);
+          last = max(last, t0 + u * NWT * 64);
+        }
     }
 #pragma unroll
     for (int k = 0; k < NPT; k++) {
@@ -1413,8 +1447,10 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
       md = fmaxf(md, __shfl_xor(md, o));
       mv = fmaxf(mv, __shfl_xor(mv, o));
       mdl = fmaxf(mdl, __shfl_xor(mdl, o));
+      last = max(last, __shfl_xor(last, o));
     }
     if (lane == 0) {
+      red_last[w] = last;
       red[0][w] = mq;
       red[1][w] = md;
       red[2][w] = mv;
@@ -1427,7 +1463,9 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
       md = fmaxf(md, red[1][k]);
       mv = fmaxf(mv, red[2][k]);
       mdl = fmaxf(mdl, red[3][k]);
+      last = max(last, red_last[k]);
     }
+    nblk = __builtin_amdgcn_readfirstlane((last + T) / T);
     const int sq = (mq > 0.f && mq <= 3.4028235e38f) ? __builtin_amdgcn_frexp_expf(mq) - 15 : 0;
     if (md > 0.f && md <= 3.4028235e38f) {
       so = __builtin_amdgcn_frexp_expf(md) - 15;
@@ -1490,7 +1528,7 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     // fragments: fragment f = 2 kk + hh is 64 lanes x 8 values, lane l holding head 32 hh + (l & 31)
     // and slots 16 kk + 8 (l >> 5) .. +7 (ds_fragment_offset). This lane's values (head hrow, slots
     // 16 mt + 4 g .. +3) are 8 contiguous bytes of fragment 2 mt + (hrow >> 5).
-    const int64_t ds_off = (ctok * n_hblk + hblk) * (int64_t)nblk * (HB * T) + ds_fragment_offset(hrow, 4 * g);
+    const int64_t ds_off = (ctok * n_hblk + hblk) * (int64_t)nblk_all * (HB * T) + ds_fragment_offset(hrow, 4 * g);
     const G gather((const char*)(kv + b * S_kv * D), S_kv);
     int32_t idx_cur = load_idx(0);
     uint64_t mask_cur = __ballot(slot_in_range(idx_cur, S_kv));

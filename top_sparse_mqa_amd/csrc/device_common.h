@@ -83,6 +83,48 @@ __device__ __forceinline__ void dma16_buf_unordered(__amdgpu_buffer_rsrc_t r, ui
   asm volatile("" : "+s"(a));
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SMQA_LDS void*)(uintptr_t)a, 16, voff, soff, 0, 0);
 }
+// dma16 (global_load_lds_dwordx4) whose LDS destination the compiler cannot trace, with the same
+// contract as dma16_buf_unordered: the caller orders every read of the destination after the copy.
+__device__ __forceinline__ void dma16_unordered(const void* gsrc, char* lds_base) {
+  uint32_t a = (uint32_t)(uintptr_t)(SMQA_LDS char*)lds_base;
+  asm volatile("" : "+s"(a));
+  __builtin_amdgcn_global_load_lds(gsrc, (SMQA_LDS void*)(uintptr_t)a, 16, 0, 0);
+}
+// A token's top-k indices staged in LDS in blocks of 32 slots, 32 blocks at a time, in a ring of 64
+// blocks. Reading a block's indices from global memory inside a block loop puts one memory latency
+// into every stage (each block's indices are a fresh cache line, and a stage that ends waiting for
+// its gathers waits for that load too); from the ring the read is an LDS access. Four waves (256
+// lanes, wave number w4 = 0..3) fetch blocks c .. c + 31 with four coalesced loads a lane (-1 past
+// topk) and write them in once a wait of their own has covered the loads, so a fetch issued at the
+// top of a stage lands at its end. The slots of blocks c .. c + 31 are those of blocks c - 64 ..
+// c - 33, and, for a refill at c = blk + 32 issued in stage blk, of blocks blk - 32 .. blk - 1.
+struct IdxRing {
+  static constexpr int T = 32;
+  static constexpr int SLOTS = 64 * T;
+  int32_t* ring;         // SLOTS ints of LDS
+  const int32_t* src;    // the token's topk indices
+  int topk;
+  __device__ __forceinline__ void fetch(int c, int w4, int lane, int32_t (&v)[4]) const {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const int t = c * T + 256 * k + 64 * w4 + lane;
+      v[k] = t < topk ? src[t] : -1;
+    }
+  }
+  __device__ __forceinline__ void store(int c, int w4, int lane, const int32_t (&v)[4]) const {
+#pragma unroll
+    for (int k = 0; k < 4; k++) ring[(c * T + 256 * k + 64 * w4 + lane) & (SLOTS - 1)] = v[k];
+  }
+  // block blk's index of this lane (lanes >= 32 and slots past topk: -1)
+  __device__ __forceinline__ int32_t read(int blk, int lane) const {
+    const int32_t v = ring[(blk * T + (lane & (T - 1))) & (SLOTS - 1)];
+    return (lane < T && blk * T + lane < topk) ? v : -1;
+  }
+  // whether stage blk refills blocks blk + 32 .. blk + 63 (the first 64 blocks are fetched up front)
+  __device__ __forceinline__ static bool refill_at(int blk, int nblk) {
+    return blk >= 32 && (blk & 31) == 0 && blk + 32 < nblk;
+  }
+};
 // Workgroup barrier that publishes this wave's LDS writes only. __syncthreads() also waits for
 // every outstanding global access, including tile gathers still in flight for a later block; this
 // waits for the LDS counter alone, and the empty asm statements keep the compiler from moving

@@ -342,7 +342,7 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
   constexpr int KS = D / 32;      // k-steps of S^T
   constexpr int NF = 2 * KS;      // score fragments (k-step, 16-slot half)
   constexpr int PF = 6;           // score fragment reads in flight
-  constexpr int NP = T / 8;       // gather instructions per wave (all eight waves gather)
+  constexpr int NP = T / 8;       // gather instructions per wave and tile
   constexpr int DW = D / 4;       // O^T d-columns per O wave
   constexpr int NDT = DW / 32;    // its 32-wide d tiles
   constexpr int PB = HB * T * 2;  // bytes of one P buffer
@@ -358,6 +358,8 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
   __shared__ __attribute__((aligned(16))) char pbuf2[PB];
   __shared__ float alpha_s[3][HB];
   __shared__ float fin_l[HB];
+  __shared__ __attribute__((aligned(16))) int32_t idx_ring[IdxRing::SLOTS];  // the token's indices
+  __shared__ int last_s[4];  // last valid slot seen by each score wave
 
   const int lane = threadIdx.x & 63;
   const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -365,35 +367,40 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
   const int64_t token = (int64_t)n_tokens - 1 - item / n_hblk;  // heavier (later) tokens first
   const int hblk = item % n_hblk;
   const int64_t b = token / S;
-  const int nblk = (topk + T - 1) / T;
+  // Blocks after the last one holding a valid slot are skipped (when the ring holds every block):
+  // a selection shorter than topk is padded with masked slots at its end.
+  int nblk = (topk + T - 1) / T;
   const int32_t* idx_tok = idx + token * (int64_t)topk;
   auto load_idx = [&](int blk) -> int32_t {
     const int t = blk * T + lane;
     return (lane < T && t < topk) ? idx_tok[t] : -1;
   };
+  // the score waves fill the ring; both roles read it
+  const IdxRing ring{idx_ring, idx_tok, topk};
+  auto read_idx = [&](int blk) -> int32_t { return ring.read(blk, lane); };
   auto tile_at = [&](int k) -> char* { return k == 0 ? tile0 : (k == 1 ? tile1 : tile2); };
   auto pbuf_at = [&](int k) -> char* { return k == 0 ? pbuf0 : (k == 1 ? pbuf1 : pbuf2); };
-  // Tile gathers are shared by all eight waves: part k of wave wu is row wu + 8 k (one kv row per
-  // instruction; masked rows read the zero row). The buffer a stage gathers into is read by neither
-  // role during that stage, so the O waves issue their parts at once and the score waves spread
-  // theirs over the score loop.
+  // The score waves gather the tiles, spreading their parts over the score loop: part k of wave wu
+  // is row wu + 4 k, one kv row per instruction (masked rows read the zero row). The buffer a stage
+  // gathers into is read by neither role during that stage. The O waves gather nothing: their
+  // stage (all of the PV products) is the longer one, and a burst of gather instructions at its
+  // start waited for the texture unit.
   const char* kv_b = (const char*)(kv + b * S_kv * D);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv_b, (int)(uint32_t)(S_kv * ROWB));
-  const __amdgpu_buffer_rsrc_t rz = make_rsrc(g_zero_row, ROWB);
-  auto gpart = [&](int k, int32_t my_idx, uint64_t mask, char* tile) {
-    const int r = wu + 8 * k;
+  auto gpart = [&](int r, int32_t my_idx, uint64_t mask, char* tile) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int32_t ri = __builtin_amdgcn_readlane(my_idx, r);
     const uint32_t voff = (uint32_t)((ln ^ (fws_swz(r) & (CPR - 1))) << 4);
     const bool v = (mask >> r) & 1ull;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv_b, (int)(uint32_t)(S_kv * ROWB));
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(g_zero_row, ROWB);
     dma16_buf(v ? rk : rz, voff, v ? (uint32_t)ri * ROWB : 0u, tile + r * ROWB);
   };
   const int32_t idx0 = load_idx(0);
   const uint64_t mask0 = __ballot(slot_in_range(idx0, S_kv));
-  if (mask0) {
+  if (mask0) {  // tile 0: all eight waves, rows wu + 8 k
 #pragma unroll
-    for (int k = 0; k < NP; k++) gpart(k, idx0, mask0, tile0);
+    for (int k = 0; k < T / 8; k++) gpart(wu + 8 * k, idx0, mask0, tile0);
   }
 
   if (wu < 4) {
@@ -423,10 +430,27 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
       for (int j = 0; j < 4; j++) sc_off[j] = row * ROWB + (((4 * j + g) ^ (fws_swz(row) & (CPR - 1))) << 4);
     }
     uint64_t mask_cur = mask0;
-    int32_t idx_nxt = nblk > 1 ? load_idx(1) : -1;
-    wait_all_mem();
+    {
+      int32_t v0[4], v1[4];
+      ring.fetch(0, wu, lane, v0);
+      if (nblk > 32) ring.fetch(32, wu, lane, v1);
+      wait_all_mem();
+      ring.store(0, wu, lane, v0);
+      if (nblk > 32) ring.store(32, wu, lane, v1);
+      int last = -1;
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        if (slot_in_range(v0[k], S_kv)) last = max(last, 256 * k + 64 * wu + lane);
+        if (nblk > 32 && slot_in_range(v1[k], S_kv)) last = max(last, 1024 + 256 * k + 64 * wu + lane);
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) last = max(last, __shfl_xor(last, o));
+      if (lane == 0) last_s[wu] = last;
+    }
+    __syncthreads();  // tile 0 and the first index blocks are in LDS
+    if (nblk <= 64) nblk = __builtin_amdgcn_readfirstlane((max(max(last_s[0], last_s[1]), max(last_s[2], last_s[3])) + T) / T);
+    int32_t idx_nxt = read_idx(1);
     uint64_t mask_nxt = __ballot(slot_in_range(idx_nxt, S_kv));
-    __syncthreads();  // tile 0 is complete
 
     auto sblock = [&](auto buf_tag, int blk) {
       constexpr int BUF = decltype(buf_tag)::value;
@@ -436,11 +460,16 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
       if (blk < nblk) {
         const uint64_t mask = mask_cur, mask_g = mask_nxt;
         const int32_t idx_g = idx_nxt;
-        const int32_t idx_new = blk + 2 < nblk ? load_idx(blk + 2) : -1;
+        const int32_t idx_new = read_idx(blk + 2);
+        // blocks blk + 32 .. blk + 63 go where blocks blk - 32 .. blk - 1 were (read by neither role
+        // from here on); they land in the ring at the end of this stage
+        const bool refill = IdxRing::refill_at(blk, nblk);
+        int32_t iv[4];
+        if (refill) ring.fetch(blk + 32, wu, lane, iv);
         if (mask == 0) {
           if (mask_g) {
 #pragma unroll
-            for (int k = 0; k < NP; k++) gpart(k, idx_g, mask_g, nxt);
+            for (int k = 0; k < NP; k++) gpart(wu + 8 * k, idx_g, mask_g, nxt);
           }
         } else {
           // S^T for the block: fragment i = (k-step i / 2, half i % 2); PF reads run ahead, every
@@ -464,7 +493,7 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (i + PF < NF) fr[(i + PF) % NB] = frag(i + PF);
             sacc[i & 1] = mfma16(fr[i % NB], qb[i >> 1], sacc[i & 1]);
-            if constexpr (i % (NF / NP) == NF / NP / 2) gpart(i / (NF / NP), idx_g, mask_g, nxt);
+            if constexpr (i % (NF / NP) == NF / NP / 2) gpart(wu + 8 * (i / (NF / NP)), idx_g, mask_g, nxt);
           });
           __builtin_amdgcn_sched_barrier(0);
           // online softmax (log2 units, or natural units under RR); this lane holds head hrow,
@@ -499,11 +528,11 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
             *(uint2*)(pw + 32 * mt) = pack4_bf16(p[4 * mt], p[4 * mt + 1], p[4 * mt + 2], p[4 * mt + 3]);
           if (g == 0) alpha_s[BUF][hrow] = alpha;
         }
-        // the next indices are used here, so that later waits never include this stage's gathers
         mask_cur = mask_g;
         mask_nxt = __ballot(slot_in_range(idx_new, S_kv));
         idx_nxt = idx_new;
         wait_all_mem();  // this wave's part of tile blk + 1
+        if (refill) ring.store(blk + 32, wu, lane, iv);
       }
       lds_barrier();
     };
@@ -532,27 +561,29 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
       for (int hh = 0; hh < 2; hh++)
 #pragma unroll
         for (int r = 0; r < 16; r++) oacc[dt][hh][r] = 0.f;
-    // indices of blocks j - 1 (products), j and j + 1 (gather) at the top of stage j
-    int32_t idx_m1 = -1, idx_0 = idx0, idx_p1 = nblk > 1 ? load_idx(1) : -1;
+    // masks of the blocks in flight, slot k holding blocks k, k + 3, ...: at the top of stage j the
+    // mask of block j - 1 (products) is in slot (j + 2) % 3, and stage j sets slot (j + 1) % 3 (gather)
+    uint64_t mask_s[3];
+    mask_s[0] = mask0;
+    mask_s[2] = 0;
     wait_all_mem();
-    __syncthreads();  // tile 0 is complete
+    __syncthreads();  // tile 0 and the first index blocks are in LDS
+    if (nblk <= 64) nblk = __builtin_amdgcn_readfirstlane((max(max(last_s[0], last_s[1]), max(last_s[2], last_s[3])) + T) / T);
 
     auto oblock = [&](auto buf_tag, int j) {
       constexpr int BUF = decltype(buf_tag)::value;
       constexpr int PBUF = (BUF + 2) % 3;  // block j - 1 went through buffers (j - 1) % 3
-      const int32_t idx_this = idx_m1;
       if (j + 1 < nblk) {  // this wave's rows of tile j + 1
-        const uint64_t mask_g = __ballot(slot_in_range(idx_p1, S_kv));
+        const int32_t idx_g = read_idx(j + 1);
+        const uint64_t mask_g = __ballot(slot_in_range(idx_g, S_kv));
+        mask_s[(BUF + 1) % 3] = mask_g;
         if (mask_g) {
 #pragma unroll
-          for (int k = 0; k < NP; k++) gpart(k, idx_p1, mask_g, tile_at((BUF + 1) % 3));
+          for (int k = 0; k < NP; k++) gpart(wu + 8 * k, idx_g, mask_g, tile_at((BUF + 1) % 3));
         }
       }
-      idx_m1 = idx_0;
-      idx_0 = idx_p1;
-      idx_p1 = j + 2 < nblk ? load_idx(j + 2) : -1;
       if (j >= 1 && j <= nblk) {
-        const uint64_t mask = __ballot(slot_in_range(idx_this, S_kv));
+        const uint64_t mask = mask_s[(BUF + 2) % 3];
         if (mask) {
           int ln = lane;
           asm volatile("" : "+v"(ln));
