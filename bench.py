@@ -57,8 +57,9 @@ FLUSH_BYTES = 1 << 30        # written before each cold-cache step (L2 4 MiB per
 CALIB_BYTES = 1 << 30        # the calibration copy reads and writes this many bytes
 CALIB_KERNEL = "MulFunctor"  # part of the name of the kernel torch.mul(src, 1.0, out=dst) runs
 REPO = os.path.dirname(os.path.abspath(__file__))
-# bench arguments of every profiled run (a short run: two timed steps of the one workload)
-PROFILE_ARGS = "--steps 2 --warmup 1 --no-cpu-baseline --cold-steps 0 --gather-steps 0"
+# bench arguments of every profiled run (a short run of the one workload)
+PROFILE_STEPS, PROFILE_WARMUP = 8, 2
+PROFILE_ARGS = f"--steps {PROFILE_STEPS} --warmup {PROFILE_WARMUP} --no-cpu-baseline --cold-steps 0 --gather-steps 0"
 # kernels the counter summary reports, in this order
 COUNTER_KERNELS = ("fwd_ws_kernel", "bwd_dkv_ws_kernel", "bwd_dq_ds_kernel", "reduce_rows_kernel", "delta_kernel",
                    "mark_kernel", "position_kernel")
@@ -257,21 +258,37 @@ def traffic_for(step: str, workload: str):
 
 
 def summarize_trace(stats_csv: str, out_path: str, workload: str) -> None:
-    """Kernel times of a rocprofv3 --kernel-trace --stats run as a table (average over dispatches)."""
+    """Kernel times of a rocprofv3 --kernel-trace --stats run as a table: the statistics over every
+    dispatch, and, from the per-dispatch trace beside it, the mean over the timed steps' dispatches
+    (the last PROFILE_STEPS of each kernel), which is what the bench line's event times cover."""
     import csv
 
     rows = list(csv.DictReader(open(stats_csv)))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    timed = {}
+    trace_csv = stats_csv.replace("_kernel_stats.csv", "_kernel_trace.csv")
+    if os.path.exists(trace_csv):
+        per = {}
+        for r in csv.DictReader(open(trace_csv)):
+            per.setdefault(r["Kernel_Name"], []).append(
+                (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        for k, v in per.items():
+            v.sort()
+            last = [d for _, d in v[-PROFILE_STEPS:]]
+            timed[k] = sum(last) / len(last)
     lines = [f"# Kernel trace: {workload}", "",
-             "rocprofv3 kernel-trace statistics of a short bench run (warmup and timed steps; every dispatch).", "",
+             f"rocprofv3 kernel-trace statistics of a short bench run ({PROFILE_WARMUP} warmup and {PROFILE_STEPS} timed "
+             "steps): every dispatch, and the mean over the timed steps' dispatches.", "",
              "Command (from the repository root on one MI355X; `<out>` an output directory):", "", "```",
              f"rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o trace -- python bench.py "
              f"--workload {workload} {PROFILE_ARGS}",
              f"python bench.py --workload {workload} --summarize-trace <out>/trace_kernel_stats.csv --out <this file>",
-             "```", "", "| kernel | calls | avg (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+             "```", "", "| kernel | calls | avg (us) | timed-step avg (us) | min (us) | max (us) | share |",
+             "|---|---|---|---|---|---|---|"]
     for r in rows:
         name = r["Name"].split("(")[0].replace("void ", "")
-        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+        t = f"{timed[r['Name']] / 1e3:.1f}" if r["Name"] in timed else ""
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {t} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
     lines += ["", "Library steps to kernels: fwd = `fwd_ws_kernel`; bwd_preprocess = `delta_kernel`;",
               "bwd_dkv_prepare = `fill_zero_kernel` + `mark_kernel` + three scan kernels + `position_kernel`;",
