@@ -113,6 +113,7 @@ EDGE = [
     ("h16_d256_k70", 2, 3, 90, 16, 256, 70),
     ("h32_d128_k40", 1, 7, 60, 32, 128, 40),
     ("h128_d128_k33", 1, 4, 40, 128, 128, 33),
+    ("h64_d512_k2200", 1, 3, 2500, 64, 512, 2200),  # more than 64 blocks: the forward's index ring refills
 ]
 
 
@@ -151,6 +152,31 @@ def test_edge_shapes_full(gpu_lib, case):
     l0 = lse[0, 0].cpu()
     assert l0[0] == -math.inf
     torch.testing.assert_close(l0[1:].double(), x["attn_sink"][1:].double() / math.log(2), rtol=0, atol=1e-5)
+
+
+def test_trailing_masked_slots_64_head_kernels(gpu_lib):
+    """Selections shorter than topk, padded with masked slots at the end (as causal top-k picks of
+    early tokens are): the 64-head D = 512 kernels stop after the last block holding a valid slot.
+    topk = 1100 spans 35 blocks; the tokens keep 1100, 1025 (one slot into block 32), 700, 33, 32
+    and 0 valid slots, and the padding mixes -1 with out-of-range values."""
+    B, S, S_kv, H, D, topk = 1, 6, 1500, 64, 512, 1100
+    keep = [1100, 1025, 700, 33, 32, 0]
+    say("case", "trailing masked slots", dict(topk=topk, keep=keep))
+    g = torch.Generator().manual_seed(77)
+    x = {
+        "q": torch.randn(B, S, H, D, generator=g).to(torch.bfloat16),
+        "kv": torch.randn(B, S_kv, D, generator=g).to(torch.bfloat16),
+        "attn_sink": torch.randn(H, generator=g),
+        "do": torch.randn(B, S, H, D, generator=g).to(torch.bfloat16),
+    }
+    idx = torch.full((B, S, topk), -1, dtype=torch.int64)
+    for s_, n in enumerate(keep):
+        idx[0, s_, :n] = torch.randperm(S_kv, generator=g)[:n]
+        pad = torch.rand(topk - n, generator=g)
+        tail = torch.where(pad < 0.5, torch.full_like(pad, -1), torch.full_like(pad, S_kv + 7)).long()
+        idx[0, s_, n:] = tail
+    x["topk_idxs"] = idx.to(torch.int32)
+    full_parity(x, tag="trailing masked")
 
 
 @pytest.mark.parametrize("H", [64, 128])
@@ -226,6 +252,34 @@ def test_negative_and_zero_scale(gpu_lib, scale):
         n = valid_mask(x["topk_idxs"], w.S_kv).sum(-1).double().view(-1, 1)
         expect = torch.log2(n + torch.exp(x["attn_sink"].double()).view(1, -1))
         torch.testing.assert_close(lse.view(-1, w.H).double().cpu(), expect, rtol=0, atol=1e-5)
+
+
+def test_negative_scale_large_do_64_head_kernels(gpu_lib):
+    """A negative sm_scale through the 64-head D = 512 kernels with q x 4 (peaked rows) and dO x 2^16,
+    so that dS = P (dP - Delta) sm_scale reaches ~10^5: the dKV kernel's fp16 dS operand scale must
+    take |sm_scale| into its bound, or dS saturates at the fp16 maximum. The gradients are linear in
+    dO, so they are compared after dividing both sides by 2^16 (the elementwise bar of the unscaled
+    problem)."""
+    w = syn.WORKLOADS["mid_h64_d512_k300"]
+    scale = -1.0 / math.sqrt(w.D)
+    say("case", w.describe(), "q x 4, dO x 2^16, sm_scale", scale)
+    x = syn.workload_inputs(w)
+    x["q"] = (x["q"].float() * 4).to(torch.bfloat16)
+    x["do"] = (x["do"].float() * 65536.0).to(torch.bfloat16)
+    B, S, H, D = x["q"].shape
+    xg = gpu(x)
+    o, lse = fwd_gpu(xg, scale)
+    o_ref, lse_ref = oracle.fwd(x["q"], x["kv"], x["attn_sink"], x["topk_idxs"], sm_scale=scale)
+    check_bf16("neg O", o.view(-1, H, D), o_ref)
+    check_lse("neg LSE", lse.view(-1, H), lse_ref)
+    ob = o_ref.view(B, S, H, D).to(torch.bfloat16)
+    lb = lse_ref.view(B, S, H)
+    dq_ref, _ = oracle.dq(x["q"], x["kv"], ob, x["do"], x["topk_idxs"], lb, sm_scale=scale)
+    dkv_ref = oracle.dkv(x["q"], x["kv"], ob, x["do"], x["topk_idxs"], lb, sm_scale=scale)
+    for fp32 in (False, True):
+        dq, dkv = bwd_gpu(xg, ob.cuda(), lb.cuda(), scale, fp32=fp32)
+        check_bf16(f"neg dQ / 2^16 (fp32 dkv {fp32})", dq.view(-1, H, D).float() / 65536.0, dq_ref / 65536.0)
+        check_bf16(f"neg dKV / 2^16 (fp32 dkv {fp32})", dkv.view(-1, D).float() / 65536.0, dkv_ref / 65536.0)
 
 
 def test_sharp_scores_mid(gpu_lib):
