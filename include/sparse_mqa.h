@@ -91,9 +91,10 @@ size_t sparse_mqa_bwd_workspace_bytes(int64_t B, int64_t S, int64_t S_kv, int64_
 size_t sparse_mqa_bwd_workspace_min_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D,
                                           int64_t topk);
 
-/* Backward (bwd page, sparse_mqa_bwd_interface): preprocess (Delta), the dQ kernel, and the dKV
- * kernel with its segmented scatter-add and per-row reduction (which also performs the fp32 ->
- * bf16 postprocess). dq [B,S,H,D] bf16. dkv [B,S_kv,D]: bf16 if dkv_fp32 == 0, else fp32 (the
+/* Backward (bwd page, sparse_mqa_bwd_interface): preprocess (Delta), the dKV kernel with its
+ * segmented scatter-add and per-row reduction (which also performs the fp32 -> bf16
+ * postprocess), and dQ: at D = 512 with H a multiple of 64 from the dS the dKV kernel stores in
+ * the workspace, otherwise from a kernel that recomputes S and dP. dq [B,S,H,D] bf16. dkv [B,S_kv,D]: bf16 if dkv_fp32 == 0, else fp32 (the
  * fp32 sums themselves). The call overwrites dq and dkv; it never accumulates into them. Rows no
  * valid slot references come out exactly 0. attn_sink is accepted for the documented signature;
  * the LSE already includes the sink, so dQ and dKV do not read it. Results are bitwise

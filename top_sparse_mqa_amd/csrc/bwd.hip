@@ -16,11 +16,16 @@
 //                block floating point (one exponent per segment of up to 128 values).
 //   bwd_dkv_ws   the staged bwd_dkv at 64 heads per workgroup and D = 512, with specialised
 //                waves: score waves (gather, S^T, dP^T, P, dS) and product waves (dKV^T, staging
-//                stores) share each SIMD, one block apart
+//                stores) share each SIMD, one block apart; the score waves also store dS (bf16,
+//                in the dQ kernel's MFMA operand order) for bwd_dq_ds
+//   bwd_dq_ds    at D = 512 with 64-head blocks: dQ = sm_scale dS K from that dS, gathering the
+//                same kv rows (2HD flops per pair instead of the recompute's 6HD)
 //   postprocess  fp32 accumulator -> bf16 (round to nearest even)
 // dQ and dKV run as two kernels: the per-token state both need (Q and dO in two layouts plus
-// the dQ accumulator) does not fit one workgroup's registers at H = 64, D = 512.
-// Both kernels gather a block of 32 slots into LDS with direct-to-LDS loads, double-buffered.
+// the dQ accumulator) does not fit one workgroup's registers at H = 64, D = 512. Where the dS
+// store exists the dQ kernel reads it; elsewhere (other shapes, and the standalone dQ stage) it
+// recomputes S and dP. Every kernel gathers a block of 32 slots into LDS with direct-to-LDS loads
+// and stops after the token's last block that holds a valid slot.
 #include <type_traits>
 
 #include "device_common.h"
