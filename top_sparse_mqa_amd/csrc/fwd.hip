@@ -569,72 +569,96 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
     wait_all_mem();
     __syncthreads();  // tile 0 and the first index blocks are in LDS
     if (nblk <= 64) nblk = __builtin_amdgcn_readfirstlane((max(max(last_s[0], last_s[1]), max(last_s[2], last_s[3])) + T) / T);
+    // indices of the block gathered in the next stage (read one stage ahead, so that no stage waits
+    // on an index read before its gather)
+    int32_t idx_nx = read_idx(1);
 
+    // V^T A fragments of a block run one stage ahead: stage j reads block j's (its tile landed at
+    // the end of stage j - 1) into register set j % 2 while its MFMAs use block j - 1's from the
+    // other set, so only the P^T fragments' LDS round trip stays in front of the stage's products.
+    // For k-step kk (slots 16 kk .. +15) lane l gets d = dbase + (l & 31) and slots s0 .. s0 + 7,
+    // s0 = 16 kk + 8 (l >> 5), from two transposing reads four rows apart.
+    bf16x8 va_s[2][2][NDT];
+    auto read_v = [&](const char* tile, bf16x8 (&va)[2][NDT]) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int vrow = 8 * (ln >> 5) + ((ln & 15) >> 2);
+      const int vch = 2 * ((ln >> 4) & 1) + ((ln & 3) >> 1);
+      const int hoff = 8 * (ln & 1);
+#pragma unroll
+      for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt++) {
+          const int r0 = 16 * kk + vrow, c = ow * (DW / 8) + 4 * dt + vch;
+          const char* p0 = tile + r0 * ROWB + ((c ^ (fws_swz(r0) & (CPR - 1))) << 4) + hoff;
+          const char* p1 = tile + (r0 + 4) * ROWB + ((c ^ (fws_swz(r0 + 4) & (CPR - 1))) << 4) + hoff;
+          va[kk][dt] = join_tr(lds_load_tr(p0), lds_load_tr(p1));
+        }
+    };
     auto oblock = [&](auto buf_tag, int j) {
-      constexpr int BUF = decltype(buf_tag)::value;
+      constexpr int J = decltype(buf_tag)::value;
+      constexpr int BUF = J % 3;
       constexpr int PBUF = (BUF + 2) % 3;  // block j - 1 went through buffers (j - 1) % 3
+      constexpr int VS = J % 2;            // register set of block j's V^T fragments
+      // the tile gather first (its indices were read a stage ahead), then the LDS reads: the P^T B
+      // fragments of block j - 1 and its rescale factors (lane holds head 32 hh + (l & 31), slots
+      // 16 kk + 8 (l >> 5) .. +7), block j's V^T fragments and the next stage's indices
       if (j + 1 < nblk) {  // this wave's rows of tile j + 1
-        const int32_t idx_g = read_idx(j + 1);
-        const uint64_t mask_g = __ballot(slot_in_range(idx_g, S_kv));
+        const uint64_t mask_g = __ballot(slot_in_range(idx_nx, S_kv));
         mask_s[(BUF + 1) % 3] = mask_g;
         if (mask_g) {
 #pragma unroll
-          for (int k = 0; k < NP; k++) gpart(wu + 8 * k, idx_g, mask_g, tile_at((BUF + 1) % 3));
+          for (int k = 0; k < NP; k++) gpart(wu + 8 * k, idx_nx, mask_g, tile_at((BUF + 1) % 3));
         }
       }
-      if (j >= 1 && j <= nblk) {
-        const uint64_t mask = mask_s[(BUF + 2) % 3];
-        if (mask) {
-          int ln = lane;
-          asm volatile("" : "+v"(ln));
-          const char* tile = tile_at(PBUF);
-          const char* pp = pbuf_at(PBUF);
-          const float a0 = alpha_s[PBUF][ln & 31], a1 = alpha_s[PBUF][32 + (ln & 31)];
-          if (__any(a0 != 1.f || a1 != 1.f)) {
+      __builtin_amdgcn_sched_barrier(0);
+      const uint64_t mask = (j >= 1 && j <= nblk) ? mask_s[(BUF + 2) % 3] : 0ull;
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      bf16x8 pv[2][2];
+      float a0 = 1.f, a1 = 1.f;
+      if (mask) {
+        const char* pp = pbuf_at(PBUF);
+        a0 = alpha_s[PBUF][ln & 31];
+        a1 = alpha_s[PBUF][32 + (ln & 31)];
 #pragma unroll
-            for (int dt = 0; dt < NDT; dt++)
+        for (int kk = 0; kk < 2; kk++)
 #pragma unroll
-              for (int r = 0; r < 16; r++) {
-                oacc[dt][0][r] *= a0;
-                oacc[dt][1][r] *= a1;
-              }
-          }
-          // V^T A fragments: for k-step kk (slots 16 kk .. +15), lane l gets d = dbase + (l & 31) and
-          // slots s0 .. s0 + 7, s0 = 16 kk + 8 (l >> 5), from two transposing reads four rows apart
-          const int vrow = 8 * (ln >> 5) + ((ln & 15) >> 2);
-          const int vch = 2 * ((ln >> 4) & 1) + ((ln & 3) >> 1);
-          const int hoff = 8 * (ln & 1);
-          auto vfrag = [&](int kk, int dt) {
-            const int r0 = 16 * kk + vrow, c = ow * (DW / 8) + 4 * dt + vch;
-            const char* p0 = tile + r0 * ROWB + ((c ^ (fws_swz(r0) & (CPR - 1))) << 4) + hoff;
-            const char* p1 = tile + (r0 + 4) * ROWB + ((c ^ (fws_swz(r0 + 4) & (CPR - 1))) << 4) + hoff;
-            return join_tr(lds_load_tr(p0), lds_load_tr(p1));
-          };
+          for (int hh = 0; hh < 2; hh++)
+            pv[kk][hh] = lds_load16(pp + ((32 * hh + (ln & 31)) * T + 16 * kk + 8 * (ln >> 5)) * 2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (j < nblk && mask_s[BUF] != 0ull) read_v(tile_at(BUF), va_s[VS]);  // block j's V^T
+      idx_nx = read_idx(j + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (mask) {
+        if (__any(a0 != 1.f || a1 != 1.f)) {
 #pragma unroll
-          for (int kk = 0; kk < 2; kk++) {
-            // P^T B fragments: lane holds head 32 hh + (l & 31), slots 16 kk + 8 (l >> 5) .. +7
-            bf16x8 pv[2];
+          for (int dt = 0; dt < NDT; dt++)
 #pragma unroll
-            for (int hh = 0; hh < 2; hh++)
-              pv[hh] = lds_load16(pp + ((32 * hh + (ln & 31)) * T + 16 * kk + 8 * (ln >> 5)) * 2);
-            bf16x8 va[NDT];
-#pragma unroll
-            for (int dt = 0; dt < NDT; dt++) va[dt] = vfrag(kk, dt);
-#pragma unroll
-            for (int dt = 0; dt < NDT; dt++) {
-              oacc[dt][0] = mfma32(va[dt], pv[0], oacc[dt][0]);
-              oacc[dt][1] = mfma32(va[dt], pv[1], oacc[dt][1]);
+            for (int r = 0; r < 16; r++) {
+              oacc[dt][0][r] *= a0;
+              oacc[dt][1][r] *= a1;
             }
-          }
         }
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+          for (int dt = 0; dt < NDT; dt++) {
+            oacc[dt][0] = mfma32(va_s[1 - VS][kk][dt], pv[kk][0], oacc[dt][0]);
+            oacc[dt][1] = mfma32(va_s[1 - VS][kk][dt], pv[kk][1], oacc[dt][1]);
+          }
       }
       wait_all_mem();  // this wave's rows of tile j + 1
       lds_barrier();
     };
-    for (int j = 0; j <= nblk; j += 3) {
+    for (int j = 0; j <= nblk; j += 6) {
       oblock(IntTag<0>{}, j);
       if (j + 1 <= nblk) oblock(IntTag<1>{}, j + 1);
       if (j + 2 <= nblk) oblock(IntTag<2>{}, j + 2);
+      if (j + 3 <= nblk) oblock(IntTag<3>{}, j + 3);
+      if (j + 4 <= nblk) oblock(IntTag<4>{}, j + 4);
+      if (j + 5 <= nblk) oblock(IntTag<5>{}, j + 5);
     }
     __syncthreads();  // the denominators are in LDS
     // epilogue: normalise and store O (bf16), four consecutive d per 8-byte store
