@@ -117,6 +117,7 @@ class Step:
         # priority) beside the forward, preprocess and dQ kernels; the partials wait for it.
         self.side = torch.cuda.Stream(device=dev) if overlap else None
         self.events = []  # one {kernel: (start, end)} per timed step
+        self.step_events = []  # one (start, end) per timed step, on the main stream
         self.nan = float("nan")
 
     def _check(self, name, st):
@@ -151,6 +152,9 @@ class Step:
             if timed:
                 ev[k][1].record(st)
 
+        if timed:
+            st_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            st_ev[0].record(self.stream)
         if self.side is None:
             for k in KERNELS:
                 launch(k, self.stream)
@@ -168,7 +172,13 @@ class Step:
             for k in ("bwd_dkv_partials", "bwd_dkv_dq", "bwd_dkv_reduce"):
                 launch(k, self.stream)
         if timed:
+            st_ev[1].record(self.stream)  # the side stream joined the main one before the partials
             self.events.append(ev)
+            self.step_events.append(st_ev)
+
+    def step_ms_median(self):
+        import statistics
+        return statistics.median(a.elapsed_time(b) for a, b in self.step_events)
 
     def kernel_ms(self):
         """Average event-timed duration of each kernel over the timed steps."""
@@ -473,7 +483,8 @@ def measure(smqa, w, x, steps, warmup, overlap=True, cold_steps=0, calibration_c
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    res = {"ms_step": start.elapsed_time(end) / steps, "ms": step.kernel_ms(), "wall": wall}
+    res = {"ms_step": start.elapsed_time(end) / steps, "ms": step.kernel_ms(), "wall": wall,
+           "ms_step_median": step.step_ms_median()}
     if cold_steps > 0:
         flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
         step.events = []
@@ -509,6 +520,17 @@ def gather_rates(w, n_valid, ms):
     out["bwd_dkv_reduce"] = {"GBps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
                              "bytes": "staging rows read"}
     return out
+
+
+def algorithmic_bytes(w, n_valid):
+    """HBM bytes of one step by the method's own accounting, per valid pair and per token/row: two
+    row gathers (forward, backward) of 2D bytes and a 4D-byte dKV scatter per pair; per token the q
+    and O streams of the forward, O and dO of the preprocess, q, dO and dQ of the backward (2HD
+    bytes each), the indices (4 per slot, read by the forward and the backward); per kv row the
+    accumulator's zero and postprocess (10D)."""
+    tokens, HD = w.B * w.S, w.H * w.D
+    return (n_valid * (2 * 2 * w.D + 4 * w.D) + tokens * 7 * 2 * HD + 2 * tokens * w.topk * 4
+            + w.B * w.S_kv * 10 * w.D)
 
 
 def main():
@@ -562,6 +584,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(r["ms_step_median"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -617,6 +640,10 @@ def main():
             "tflops": round(14 * HDg * ng / (rg["ms_step"] * 1e-3) / 1e12, 3),
             "kernel_ms": {k: round(v, 4) for k, v in rg["ms"].items()},
             "gather": gather_rates(wg, ng, rg["ms"]),
+            "step_algorithmic_GB": round(algorithmic_bytes(wg, ng) / 1e9, 2),
+            "step_algorithmic_GBps": round(algorithmic_bytes(wg, ng) / (rg["ms_step"] * 1e-3) / 1e9, 1),
+            "step_algorithmic_frac_hbm": round(algorithmic_bytes(wg, ng) / (rg["ms_step"] * 1e-3) / 1e9
+                                               / PEAK_HBM_GBS, 4),
             "hbm_peak_GBps": PEAK_HBM_GBS,
         }
     if not args.no_cpu_baseline:

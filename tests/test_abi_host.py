@@ -116,10 +116,10 @@ def r256(n):
     return (n + 255) // 256 * 256
 
 
-def dkv_layout_bytes(B, S_kv, H, D, K, chunk, acc, ds=None):
+def dkv_layout_bytes(B, S_kv, H, D, K, chunk, acc, ds=None, S=None):
     """The dKV workspace layout restated: kv row norms, the selection bitmap (one bit per kv row and
-    chunk token, in 32-bit words) with a pair count and a cursor per word (cleared together as whole
-    16-byte pieces), the scanned offsets (+ total),
+    chunk token of the row's batch, in 32-bit words: ceil(min(chunk, S) / 32) per row) with a pair
+    count and a cursor per word (cleared together as whole 16-byte pieces), the scanned offsets (+ total),
     the scan's tile sums, the fp32 accumulator when chunked with bf16 output, the slots' positions,
     the staging rows (one per slot and 64-head block plus one spare per token and head block; a
     row is D int16 values and one int8 exponent per segment of min(128, D / (heads per workgroup /
@@ -128,7 +128,7 @@ def dkv_layout_bytes(B, S_kv, H, D, K, chunk, acc, ds=None):
     if ds is None:
         ds = D == 512 and H % 64 == 0
     n_rows = B * S_kv
-    words = n_rows * ((chunk + 31) // 32)
+    words = n_rows * ((min(chunk, S if S is not None else chunk) + 31) // 32)
     hb = max(1, H // 64)
     seg = min(128, D // (min(H, 64) // 16))
     rows = chunk * (K + 1) * hb
@@ -143,6 +143,10 @@ def test_workspace_bytes(lib):
     assert full == r256(B * S * H * 4) + dkv_layout_bytes(B, S_kv, H, D, K, B * S, False)
     # at the headline shape the bitmap and offsets are 2 MiB each; the staging rows dominate
     assert dkv_layout_bytes(B, S_kv, H, D, K, B * S, False) > 6.4e9
+    # batched: a kv row's bitmap words cover its own batch's tokens (S of them), not the whole pass
+    bb, sb, skvb = 4, 2048, 65536
+    assert lib.sparse_mqa_bwd_workspace_bytes(bb, sb, skvb, H, D, K) == r256(bb * sb * H * 4) + dkv_layout_bytes(
+        bb, skvb, H, D, K, bb * sb, False, S=sb)
     low = lib.sparse_mqa_bwd_workspace_min_bytes(B, S, S_kv, H, D, K)
     assert low == r256(B * S * H * 4) + dkv_layout_bytes(B, S_kv, H, D, K, 1, True)
     # few tokens over many rows: a single pass (no fp32 running sum) is the smaller layout
@@ -153,7 +157,7 @@ def test_workspace_bytes(lib):
     # H = 128 runs two 64-head workgroups per token: two staging rows per slot (and two spare rows)
     for (b, s_, skv, h, d, k) in ((1, 8, 16, 128, 512, 4), (2, 40, 33, 16, 64, 7), (1, 100, 70, 192, 256, 9)):
         assert lib.sparse_mqa_bwd_workspace_bytes(b, s_, skv, h, d, k) == (
-            r256(b * s_ * h * 4) + dkv_layout_bytes(b, skv, h, d, k, b * s_, False))
+            r256(b * s_ * h * 4) + dkv_layout_bytes(b, skv, h, d, k, b * s_, False, S=s_))
     assert lib.sparse_mqa_bwd_workspace_bytes(0, 1, 1, 16, 64, 1) == 0
     assert lib.sparse_mqa_bwd_workspace_min_bytes(1, 1, 1, 48, 512, 1) == 0
 

@@ -657,7 +657,7 @@ def _plan_arrays(steps, w):
     byte offsets of the documented layout (kv row norms, plan words, offsets, scan tiles, pos)."""
     r256 = lambda n: (n + 255) // 256 * 256
     n_rows, tokens = w.B * w.S_kv, w.B * w.S
-    nw = (tokens + 31) // 32
+    nw = (min(tokens, w.S) + 31) // 32  # a kv row's words cover the tokens of its own batch
     words = n_rows * nw
     o_off = r256(n_rows * 4) + r256((3 * words + 4) * 4)
     o_pos = o_off + r256((words + 1) * 4) + r256(((words + 4095) // 4096) * 4)
@@ -672,7 +672,8 @@ def test_staging_plan_structure(gpu_lib, case):
     """The dKV staging plan as the prepare step leaves it in the workspace: every valid (token,
     slot) pair owns n_hblk consecutive staging rows, the pairs of a kv row fill that row's segment
     [offset[r nw], offset[(r + 1) nw]) exactly, masked slots get -1, and (distinct indices) the
-    order inside a segment is (token mod nw, token div nw), independent of timing."""
+    order inside a segment is (k mod nw, k div nw) for k the token's place in its batch,
+    independent of timing."""
     if case == "distinct":
         w = syn.WORKLOADS["mid_h64_d512_k300"]
         x = syn.workload_inputs(w)
@@ -706,6 +707,7 @@ def test_staging_plan_structure(gpu_lib, case):
     assert bool((p >= offset[r * nw].long()).all()) and bool((p < offset[(r + 1) * nw].long()).all())
     if case == "distinct":
         # inside a row's segment the pairs follow (token mod nw, token div nw)
-        key = r * (32 * nw) + (t % nw) * 32 + t // nw
+        k = t % w.S
+        key = r * (32 * nw) + (k % nw) * 32 + k // nw
         order = torch.argsort(p)
         assert bool((key[order][1:] > key[order][:-1]).all())

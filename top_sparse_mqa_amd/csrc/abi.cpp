@@ -131,9 +131,9 @@ struct DkvPlan {
 
 // Lay out the dKV part of the workspace from `base` for token chunks of `chunk` tokens; returns the
 // end offset.
-size_t dkv_layout(int64_t B, int64_t S_kv, int64_t H, int64_t D, int64_t topk, int64_t chunk, bool use_acc,
-                  bool with_ds, size_t base, DkvPlan* p) {
-  const int64_t n_rows = B * S_kv, words = smqa::dkv_bitmap_words(n_rows, chunk);
+size_t dkv_layout(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk, int64_t chunk,
+                  bool use_acc, bool with_ds, size_t base, DkvPlan* p) {
+  const int64_t n_rows = B * S_kv, words = smqa::dkv_bitmap_words(n_rows, chunk, S);
   size_t o = base;
   p->kvn = o;  // kv row norms
   o += round256((size_t)n_rows * 4);
@@ -181,16 +181,16 @@ bool plan_dkv(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t 
   const int64_t tokens = B * S;
   const int64_t max_chunk = max_chunk_tokens(B, S_kv, H, topk);
   if (max_chunk < 1) return false;
-  if (tokens <= max_chunk && dkv_layout(B, S_kv, H, D, topk, tokens, false, with_ds, base, p) <= bytes) return true;
+  if (tokens <= max_chunk && dkv_layout(B, S, S_kv, H, D, topk, tokens, false, with_ds, base, p) <= bytes) return true;
   const bool use_acc = !dkv_fp32;
-  if (dkv_layout(B, S_kv, H, D, topk, 1, use_acc, with_ds, base, p) > bytes) return false;
+  if (dkv_layout(B, S, S_kv, H, D, topk, 1, use_acc, with_ds, base, p) > bytes) return false;
   int64_t lo = 1, hi = tokens < max_chunk ? tokens : max_chunk;
   while (lo < hi) {  // the largest chunk that fits (the layout grows with the chunk)
     const int64_t mid = lo + (hi - lo + 1) / 2;
-    if (dkv_layout(B, S_kv, H, D, topk, mid, use_acc, with_ds, base, p) <= bytes) lo = mid;
+    if (dkv_layout(B, S, S_kv, H, D, topk, mid, use_acc, with_ds, base, p) <= bytes) lo = mid;
     else hi = mid - 1;
   }
-  dkv_layout(B, S_kv, H, D, topk, lo, use_acc, with_ds, base, p);
+  dkv_layout(B, S, S_kv, H, D, topk, lo, use_acc, with_ds, base, p);
   return true;
 }
 
@@ -227,7 +227,7 @@ int run_dkv(const void* q, const void* kv, const void* d_o, const int32_t* idx, 
     const bool last = t0 + n >= tokens;
     void* out16 = (!dkv_fp32 && last) ? dkv : nullptr;
     if (smqa::launch_reduce_rows(stage, stage_exp, smqa::stage_segments(H, D), offset,
-                                 smqa::dkv_bitmap_words(1, n), acc, out16, t0 > 0 ? 1 : 0, n_rows, D,
+                                 smqa::dkv_row_words(n, S), acc, out16, t0 > 0 ? 1 : 0, n_rows, D,
                                  st) != hipSuccess)
       return SMQA_ERR_HIP;
   }
@@ -330,7 +330,7 @@ extern "C" {
 size_t sparse_mqa_bwd_workspace_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk) {
   if (!sizes_ok(B, S, S_kv, H, D, topk)) return 0;
   DkvPlan p;
-  return delta_bytes(B, S, H) + dkv_layout(B, S_kv, H, D, topk, B * S, false, smqa::dq_from_ds(H, D), 0, &p);
+  return delta_bytes(B, S, H) + dkv_layout(B, S, S_kv, H, D, topk, B * S, false, smqa::dq_from_ds(H, D), 0, &p);
 }
 
 size_t sparse_mqa_bwd_workspace_min_bytes(int64_t B, int64_t S, int64_t S_kv, int64_t H, int64_t D, int64_t topk) {
@@ -341,10 +341,10 @@ size_t sparse_mqa_bwd_workspace_min_bytes(int64_t B, int64_t S, int64_t S_kv, in
   // token chunks of one (with the fp32 running sum), or a single pass over all tokens when that
   // takes less (few tokens over many kv rows)
   const bool with_ds = smqa::dq_from_ds(H, D);
-  const size_t chunked = dkv_layout(B, S_kv, H, D, topk, 1, true, with_ds, 0, &p);
+  const size_t chunked = dkv_layout(B, S, S_kv, H, D, topk, 1, true, with_ds, 0, &p);
   size_t low = chunked;
   if (B * S <= max_chunk) {
-    const size_t one_pass = dkv_layout(B, S_kv, H, D, topk, B * S, false, with_ds, 0, &p);
+    const size_t one_pass = dkv_layout(B, S, S_kv, H, D, topk, B * S, false, with_ds, 0, &p);
     if (one_pass < low) low = one_pass;
   }
   return delta_bytes(B, S, H) + low;
@@ -514,7 +514,7 @@ int sparse_mqa_bwd_dkv_reduce(void* dkv, int dkv_fp32, void* workspace, size_t w
   char* ws = (char*)workspace;
   if (smqa::launch_reduce_rows((const uint16_t*)(ws + p.stage), (const int8_t*)(ws + p.stage_exp),
                                smqa::stage_segments(H, D), (const int32_t*)(ws + p.offset),
-                               smqa::dkv_bitmap_words(1, B * S), dkv_fp32 ? (float*)dkv : nullptr,
+                               smqa::dkv_row_words(B * S, S), dkv_fp32 ? (float*)dkv : nullptr,
                                dkv_fp32 ? nullptr : dkv, 0, B * S_kv, D,
                                (hipStream_t)stream) != hipSuccess)
     return SMQA_ERR_HIP;

@@ -1771,6 +1771,7 @@ mark_kernel(const int32_t* __restrict__ idx, int2* __restrict__ bc, int64_t toke
   __shared__ uint32_t lb[MARK_ROWS];
   __shared__ int32_t lc[MARK_ROWS];
   const int64_t n_units = nw * ((n_rows + MARK_ROWS - 1) / MARK_ROWS);
+  const int64_t c_lo = token0 / S, c_hi = (token0 + n_chunk - 1) / S;  // batches of the chunk
   for (int64_t u = blockIdx.x; u < n_units; u += gridDim.x) {  // the grid is capped
     const int64_t w0 = u % nw;
     const int64_t r0 = (u / nw) * MARK_ROWS;
@@ -1780,20 +1781,24 @@ mark_kernel(const int32_t* __restrict__ idx, int2* __restrict__ bc, int64_t toke
       lc[r] = 0;
     }
     __syncthreads();
-    for (int j = 0; j < 32; j++) {
-      const int64_t ct = w0 + nw * j;
-      if (ct >= n_chunk) break;
-      const int64_t token = token0 + ct;
-      const int64_t rb = (token / S) * S_kv - r0;  // this token's batch rows, relative to the tile
-      if (rb >= nr || rb + S_kv <= 0) continue;    // the token's batch has no row in this tile
-      const int32_t* it = idx + token * topk;
-      for (int t = threadIdx.x; t < topk; t += 256) {
-        const int32_t v = it[t];
-        if (slot_in_range(v, S_kv)) {
-          const int64_t r = rb + v;
-          if (r >= 0 && r < nr) {
-            atomicOr(lb + r, 1u << j);
-            atomicAdd(lc + r, 1);
+    // the batches with rows in this tile; a row of batch b takes bits from batch b's tokens only
+    const int64_t b_lo = r0 / S_kv, b_hi = (r0 + nr - 1) / S_kv;
+    for (int64_t b = (b_lo > c_lo ? b_lo : c_lo); b <= (b_hi < c_hi ? b_hi : c_hi); b++) {
+      const int64_t first = token0 > b * S ? token0 : b * S;
+      const int64_t last = token0 + n_chunk < (b + 1) * S ? token0 + n_chunk : (b + 1) * S;
+      const int64_t rb = b * S_kv - r0;  // the batch's rows, relative to the tile
+      for (int j = 0; j < 32; j++) {
+        const int64_t token = first + w0 + nw * j;
+        if (token >= last) break;
+        const int32_t* it = idx + token * topk;
+        for (int t = threadIdx.x; t < topk; t += 256) {
+          const int32_t v = it[t];
+          if (slot_in_range(v, S_kv)) {
+            const int64_t r = rb + v;
+            if (r >= 0 && r < nr) {
+              atomicOr(lb + r, 1u << j);
+              atomicAdd(lc + r, 1);
+            }
           }
         }
       }
@@ -1817,12 +1822,14 @@ position_kernel(const int32_t* __restrict__ idx, const int2* __restrict__ bc, in
     const int t = (int)(u - ct * tpt) * 256 + (int)threadIdx.x;
     if (t >= topk) continue;
     const int64_t token = token0 + ct;
+    const int64_t b = token / S;
+    const int64_t k = token - (token0 > b * S ? token0 : b * S);  // the token's place among its batch's
     const int32_t v = idx[token * topk + t];
     int32_t r = -1;
     if (slot_in_range(v, S_kv)) {
-      const int64_t e = ((token / S) * S_kv + v) * nw + ct % nw;
+      const int64_t e = (b * S_kv + v) * nw + k % nw;
       const int2 w = bc[e];
-      if (w.y == __popc((uint32_t)w.x)) r = offset[e] + n_hblk * __popc((uint32_t)w.x & ((1u << (ct / nw)) - 1u));
+      if (w.y == __popc((uint32_t)w.x)) r = offset[e] + n_hblk * __popc((uint32_t)w.x & ((1u << (k / nw)) - 1u));
       else r = offset[e] + atomicAdd(cur + e, n_hblk);  // a word with duplicate pairs
     }
     pos[ct * topk + t] = r;
@@ -2125,13 +2132,14 @@ static unsigned grid_for(int64_t n, int64_t per_block, int64_t cap = 65536) {
 }
 
 int64_t scan_tiles(int64_t n) { return (n + SCAN_TILE - 1) / SCAN_TILE; }
-int64_t dkv_bitmap_words(int64_t n_rows, int64_t n_chunk) { return n_rows * ((n_chunk + 31) / 32); }
+int64_t dkv_row_words(int64_t n_chunk, int64_t S) { return ((n_chunk < S ? n_chunk : S) + 31) / 32; }
+int64_t dkv_bitmap_words(int64_t n_rows, int64_t n_chunk, int64_t S) { return n_rows * dkv_row_words(n_chunk, S); }
 
 hipError_t launch_dkv_prepare(const int32_t* idx, uint32_t* plan, int32_t* offset, int32_t* tile_sum, int32_t* pos,
                               int64_t B, int64_t S, int64_t S_kv, int64_t topk, int n_hblk, int64_t token0,
                               int64_t n_chunk, hipStream_t st) {
-  const int64_t nw = (n_chunk + 31) / 32, n_rows = B * S_kv;
-  const int64_t n = dkv_bitmap_words(n_rows, n_chunk);
+  const int64_t nw = dkv_row_words(n_chunk, S), n_rows = B * S_kv;
+  const int64_t n = dkv_bitmap_words(n_rows, n_chunk, S);
   int2* bc = (int2*)plan;             // {bits, count} per word, written whole by mark_kernel
   int32_t* cur = (int32_t*)(plan + 2 * n);  // cursors of words with duplicate pairs
   hipError_t e = launch_fill_zero_f32((float*)cur, (n + 3) / 4 * 4, st);

@@ -81,9 +81,11 @@ hipError_t launch_dkv_prepare(const int32_t* idx, uint32_t* plan, int32_t* offse
                               int64_t B, int64_t S, int64_t S_kv, int64_t topk, int n_hblk, int64_t token0,
                               int64_t n_chunk, hipStream_t st);
 int64_t scan_tiles(int64_t n);
-// Words of the selection bitmap for n_rows kv rows and a chunk of n_chunk tokens (ceil(n_chunk /
-// 32) per row); also the number of scanned offsets before the final total.
-int64_t dkv_bitmap_words(int64_t n_rows, int64_t n_chunk);
+// Words of the selection bitmap per kv row for a chunk of n_chunk tokens: a row takes bits from the
+// tokens of its own batch only, so ceil(min(n_chunk, S) / 32). dkv_bitmap_words: for n_rows rows,
+// also the number of scanned offsets before the final total.
+int64_t dkv_row_words(int64_t n_chunk, int64_t S);
+int64_t dkv_bitmap_words(int64_t n_rows, int64_t n_chunk, int64_t S);
 // Per kv row: sum of its staging segment [offset[row * stride], offset[(row + 1) * stride])
 // (+ acc if accumulate); writes acc (fp32) and/or out (bf16).
 hipError_t launch_reduce_rows(const uint16_t* stage, const int8_t* stage_exp, int nseg, const int32_t* offset,
