@@ -114,6 +114,7 @@ EDGE = [
     ("h32_d128_k40", 1, 7, 60, 32, 128, 40),
     ("h128_d128_k33", 1, 4, 40, 128, 128, 33),
     ("h64_d512_k2200", 1, 3, 2500, 64, 512, 2200),  # more than 64 blocks: the forward's index ring refills
+    ("h64_d512_k3300", 1, 2, 4000, 64, 512, 3300),  # 104 blocks: two refills of the ring
 ]
 
 
