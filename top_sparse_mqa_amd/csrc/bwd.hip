@@ -1787,17 +1787,25 @@ mark_kernel(const int32_t* __restrict__ idx, int2* __restrict__ bc, int64_t toke
       const int64_t first = token0 > b * S ? token0 : b * S;
       const int64_t last = token0 + n_chunk < (b + 1) * S ? token0 + n_chunk : (b + 1) * S;
       const int64_t rb = b * S_kv - r0;  // the batch's rows, relative to the tile
+      // the column's tokens one after another, each token's indices in chunks of MU per thread
+      // whose loads all go out before the chunk's LDS atomics
+      constexpr int MU = 8;
       for (int j = 0; j < 32; j++) {
         const int64_t token = first + w0 + nw * j;
         if (token >= last) break;
         const int32_t* it = idx + token * topk;
-        for (int t = threadIdx.x; t < topk; t += 256) {
-          const int32_t v = it[t];
-          if (slot_in_range(v, S_kv)) {
-            const int64_t r = rb + v;
-            if (r >= 0 && r < nr) {
-              atomicOr(lb + r, 1u << j);
-              atomicAdd(lc + r, 1);
+        for (int t0 = threadIdx.x; t0 < topk; t0 += MU * 256) {
+          int32_t v[MU];
+#pragma unroll
+          for (int u = 0; u < MU; u++) v[u] = t0 + u * 256 < topk ? it[t0 + u * 256] : -1;
+#pragma unroll
+          for (int u = 0; u < MU; u++) {
+            if (slot_in_range(v[u], S_kv)) {
+              const int64_t r = rb + v[u];
+              if (r >= 0 && r < nr) {
+                atomicOr(lb + r, 1u << j);
+                atomicAdd(lc + r, 1);
+              }
             }
           }
         }
