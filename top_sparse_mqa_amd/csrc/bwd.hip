@@ -1818,29 +1818,46 @@ mark_kernel(const int32_t* __restrict__ idx, int2* __restrict__ bc, int64_t toke
 }
 
 // pos[ct, slot] = the slot's first staging row, or -1 for a masked slot. Workgroup unit u covers
-// slots 256 (u % tpt) .. +255 of chunk token u / tpt (tpt = ceil(topk / 256) units per token), so
-// the token and batch come from one wave-uniform division per unit.
+// POS_SLOTS slots of chunk token u / tpt (tpt units per token), so the token and batch come from
+// one wave-uniform division per unit; a thread takes four slots 256 apart and issues each level of
+// its loads (indices, then the words and offsets they name) for all four before using any.
+constexpr int POS_PER_THREAD = 4;
+constexpr int POS_SLOTS = 256 * POS_PER_THREAD;
 __global__ void __launch_bounds__(256)
 position_kernel(const int32_t* __restrict__ idx, const int2* __restrict__ bc, int32_t* __restrict__ cur,
                 const int32_t* __restrict__ offset, int32_t* __restrict__ pos, int64_t token0, int64_t n_chunk,
                 int64_t S, int64_t S_kv, int topk, int64_t nw, int n_hblk) {
-  const int64_t tpt = (topk + 255) / 256;
+  constexpr int PU = POS_PER_THREAD;
+  const int64_t tpt = (topk + POS_SLOTS - 1) / POS_SLOTS;
   for (int64_t u = blockIdx.x; u < n_chunk * tpt; u += gridDim.x) {
     const int64_t ct = u / tpt;
-    const int t = (int)(u - ct * tpt) * 256 + (int)threadIdx.x;
-    if (t >= topk) continue;
+    const int t0 = (int)(u - ct * tpt) * POS_SLOTS + (int)threadIdx.x;
     const int64_t token = token0 + ct;
     const int64_t b = token / S;
     const int64_t k = token - (token0 > b * S ? token0 : b * S);  // the token's place among its batch's
-    const int32_t v = idx[token * topk + t];
-    int32_t r = -1;
-    if (slot_in_range(v, S_kv)) {
-      const int64_t e = (b * S_kv + v) * nw + k % nw;
-      const int2 w = bc[e];
-      if (w.y == __popc((uint32_t)w.x)) r = offset[e] + n_hblk * __popc((uint32_t)w.x & ((1u << (k / nw)) - 1u));
-      else r = offset[e] + atomicAdd(cur + e, n_hblk);  // a word with duplicate pairs
+    int32_t v[PU];
+#pragma unroll
+    for (int q = 0; q < PU; q++) v[q] = t0 + 256 * q < topk ? idx[token * topk + t0 + 256 * q] : -1;
+    int64_t e[PU];
+    int2 w[PU];
+    int32_t off[PU];
+#pragma unroll
+    for (int q = 0; q < PU; q++) {
+      e[q] = slot_in_range(v[q], S_kv) ? (b * S_kv + v[q]) * nw + k % nw : -1;
+      w[q] = e[q] >= 0 ? bc[e[q]] : make_int2(0, 0);
+      off[q] = e[q] >= 0 ? offset[e[q]] : 0;
     }
-    pos[ct * topk + t] = r;
+#pragma unroll
+    for (int q = 0; q < PU; q++) {
+      int32_t r = -1;
+      if (e[q] >= 0) {
+        if (w[q].y == __popc((uint32_t)w[q].x))
+          r = off[q] + n_hblk * __popc((uint32_t)w[q].x & ((1u << (k / nw)) - 1u));
+        else
+          r = off[q] + atomicAdd(cur + e[q], n_hblk);  // a word with duplicate pairs
+      }
+      if (t0 + 256 * q < topk) pos[ct * topk + t0 + 256 * q] = r;
+    }
   }
 }
 
@@ -2164,7 +2181,7 @@ hipError_t launch_dkv_prepare(const int32_t* idx, uint32_t* plan, int32_t* offse
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(scan_add_kernel, dim3((unsigned)tiles), dim3(256), 0, st, offset, (const int32_t*)tile_sum, n);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t n_units = n_chunk * ((topk + 255) / 256);
+  const int64_t n_units = n_chunk * ((topk + POS_SLOTS - 1) / POS_SLOTS);
   hipLaunchKernelGGL(position_kernel, dim3(grid_for(n_units, 1)), dim3(256), 0, st, idx, (const int2*)bc, cur,
                      (const int32_t*)offset, pos, token0, n_chunk, S, S_kv, (int)topk, nw, n_hblk);
   return hipGetLastError();
