@@ -1742,27 +1742,30 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 
 // ---------------------------------------------------------------------------------------------
 // Segmented scatter-add of dKV. Every valid (token, slot) pair gets n_hblk consecutive rows of a
-// staging buffer, grouped by kv row and, within a row, in an order fixed by the token indices
-// (token ct sorts by (ct % nw, ct / nw), nw below). The dKV kernel stores each
-// contribution row there with plain stores, and reduce_rows sums each kv row's segment in that
-// order. This moves the payload through the store and streaming-read paths instead of the fp32
-// atomic units, and the result does not depend on the order in which workgroups run.
+// staging buffer, grouped by kv row and, within a row, in an order fixed by the token indices (a
+// token with place k among its batch's tokens of the chunk sorts by (k % nw, k / nw), nw below). The
+// dKV kernel stores each contribution row there with plain stores, and reduce_rows sums each kv
+// row's segment in that order. This moves the payload through the store and streaming-read paths
+// instead of the fp32 atomic units, and the result does not depend on the order in which
+// workgroups run.
 //
 // The plan takes no global atomics on the common path. For a chunk of n_chunk tokens, kv row `row`
-// has nw = ceil(n_chunk / 32) words of a selection bitmap, and chunk token ct owns bit ct / nw of
-// word ct % nw; a set bit records that the token selects the row. Next to each word sits the count
-// of its pairs (bc[e] = {bits, count}, e = row * nw + word). An exclusive scan of n_hblk * count over
-// the words in (row, word) order gives each word the staging row of its first pair. In a word whose
-// count equals its popcount (each of its tokens selects the row once, as top-k selections do), a
-// pair's staging row is that plus n_hblk times the word's pairs below its bit: positions then
-// depend on the indices only, and row r's segment is [offset[r nw], offset[(r + 1) nw]). A word with
+// of batch b has nw = ceil(min(n_chunk, S) / 32) words of a selection bitmap covering batch b's
+// tokens of the chunk, and the token with place k among them owns bit k / nw of word k % nw; a set
+// bit records that the token selects the row. Next to each word sits the count of its pairs
+// (bc[e] = {bits, count}, e = row * nw + word). An exclusive scan of n_hblk * count over the words
+// in (row, word) order gives each word the staging row of its first pair. In a word whose count
+// equals its popcount (each of its tokens selects the row once, as top-k selections do), a pair's
+// staging row is that plus n_hblk times the word's pairs below its bit: positions then depend on
+// the indices only, and row r's segment is [offset[r nw], offset[(r + 1) nw]). A word with
 // duplicate (token, row) pairs hands out its range [offset[e], offset[e + 1]) through an atomic
 // cursor cur[e] instead.
 
-// One workgroup per (word column w0, tile of MARK_ROWS kv rows): the 32 tokens w0 + nw j of the
-// column own every word of the column, so the workgroup builds the tile's words in LDS (LDS
-// atomics) and writes them out with plain stores. 32 KiB of LDS lets a workgroup sit beside a
-// forward or dQ workgroup (~111 KiB) on one CU when the plan runs on a side stream.
+// One workgroup per (word column w0, tile of MARK_ROWS kv rows): for each batch with rows in the
+// tile, the (up to 32) tokens with places w0 + nw j own every word of the column, so the workgroup
+// builds the tile's words in LDS (LDS atomics) and writes them out with plain stores. 32 KiB of LDS
+// lets a workgroup sit beside a forward or dQ workgroup (~111 KiB) on one CU when the plan runs on
+// a side stream.
 constexpr int MARK_ROWS = 4096;
 
 __global__ void __launch_bounds__(256)

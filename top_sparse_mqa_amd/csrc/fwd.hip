@@ -380,11 +380,10 @@ fwd_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, c
   auto read_idx = [&](int blk) -> int32_t { return ring.read(blk, lane); };
   auto tile_at = [&](int k) -> char* { return k == 0 ? tile0 : (k == 1 ? tile1 : tile2); };
   auto pbuf_at = [&](int k) -> char* { return k == 0 ? pbuf0 : (k == 1 ? pbuf1 : pbuf2); };
-  // The score waves gather the tiles, spreading their parts over the score loop: part k of wave wu
-  // is row wu + 4 k, one kv row per instruction (masked rows read the zero row). The buffer a stage
-  // gathers into is read by neither role during that stage. The O waves gather nothing: their
-  // stage (all of the PV products) is the longer one, and a burst of gather instructions at its
-  // start waited for the texture unit.
+  // Every wave gathers an eighth of each tile, one kv row per instruction (masked rows read the zero
+  // row): part k of wave wu is row wu + 8 k. The score waves spread their parts over the score loop;
+  // the O waves issue theirs first thing in the stage. The buffer a stage gathers into is read by
+  // neither role during that stage.
   const char* kv_b = (const char*)(kv + b * S_kv * D);
   auto gpart = [&](int r, int32_t my_idx, uint64_t mask, char* tile) {
     int ln = lane;
