@@ -668,24 +668,40 @@ def _plan_arrays(steps, w):
     return pos, offset, nw
 
 
-@pytest.mark.parametrize("case", ["distinct", "duplicates"])
+@pytest.mark.parametrize("case", ["distinct", "duplicates", "sparse_distinct", "sparse_duplicates"])
 def test_staging_plan_structure(gpu_lib, case):
     """The dKV staging plan as the prepare step leaves it in the workspace: every valid (token,
     slot) pair owns n_hblk consecutive staging rows, the pairs of a kv row fill that row's segment
     [offset[r nw], offset[(r + 1) nw]) exactly, masked slots get -1, and (distinct indices) the
     order inside a segment is (k mod nw, k div nw) for k the token's place in its batch,
-    independent of timing."""
+    independent of timing. The sparse cases have fewer slots than plan words (most words empty),
+    as on long kv sequences."""
+    g = torch.Generator().manual_seed(77)
+
+    def random_inputs(w, idx):
+        return {"q": torch.randn(w.B, w.S, w.H, w.D, generator=g).to(torch.bfloat16),
+                "kv": torch.randn(w.B, w.S_kv, w.D, generator=g).to(torch.bfloat16),
+                "do": torch.randn(w.B, w.S, w.H, w.D, generator=g).to(torch.bfloat16),
+                "topk_idxs": idx.to(torch.int32)}
     if case == "distinct":
         w = syn.WORKLOADS["mid_h64_d512_k300"]
         x = syn.workload_inputs(w)
         n_hblk = 1
-    else:  # random indices with repeats and out-of-range values, two 64-head blocks
+    elif case == "duplicates":  # random indices with repeats and out-of-range values, two 64-head blocks
         w = syn.Workload("plan_dups", 2, 40, 70, 128, 512, 90, "causal_distinct", 0, 0)
-        g = torch.Generator().manual_seed(77)
-        x = {"q": torch.randn(w.B, w.S, w.H, w.D, generator=g).to(torch.bfloat16),
-             "kv": torch.randn(w.B, w.S_kv, w.D, generator=g).to(torch.bfloat16),
-             "do": torch.randn(w.B, w.S, w.H, w.D, generator=g).to(torch.bfloat16),
-             "topk_idxs": torch.randint(-3, w.S_kv + 3, (w.B, w.S, w.topk), generator=g).to(torch.int32)}
+        x = random_inputs(w, torch.randint(-3, w.S_kv + 3, (w.B, w.S, w.topk), generator=g))
+        n_hblk = 2
+    elif case == "sparse_distinct":  # distinct rows per token out of 4096, a few masked slots
+        w = syn.Workload("plan_sparse", 2, 64, 4096, 64, 512, 64, "causal_distinct", 0, 0)
+        idx = torch.stack([torch.randperm(w.S_kv, generator=g)[:w.topk] for _ in range(w.B * w.S)])
+        idx[torch.rand(idx.shape, generator=g) < 0.05] = -1
+        x = random_inputs(w, idx.view(w.B, w.S, w.topk))
+        n_hblk = 1
+    else:  # sparse, with repeats and out-of-range values, two 64-head blocks
+        w = syn.Workload("plan_sparse_dups", 2, 64, 4096, 128, 512, 64, "causal_distinct", 0, 0)
+        idx = torch.randint(-3, w.S_kv + 3, (w.B, w.S, w.topk), generator=g)
+        idx[:, :, 1::7] = idx[:, :, 0::7][:, :, :idx[:, :, 1::7].shape[2]]  # repeats inside each token
+        x = random_inputs(w, idx)
         n_hblk = 2
     say("case", "staging plan", case)
     xg = gpu({k: x[k] for k in ("q", "kv", "do", "topk_idxs")})
@@ -706,7 +722,7 @@ def test_staging_plan_structure(gpu_lib, case):
     row = (ct // w.S) * w.S_kv + idx.clamp(0, w.S_kv - 1)
     r, t = row[valid], ct[valid]
     assert bool((p >= offset[r * nw].long()).all()) and bool((p < offset[(r + 1) * nw].long()).all())
-    if case == "distinct":
+    if case.endswith("distinct"):
         # inside a row's segment the pairs follow (token mod nw, token div nw)
         k = t % w.S
         key = r * (32 * nw) + (k % nw) * 32 + k // nw

@@ -1820,15 +1820,20 @@ mark_kernel(const int32_t* __restrict__ idx, int2* __restrict__ bc, int64_t toke
   }
 }
 
+// Exclusive scan of the words' staging-row counts, in tiles of SCAN_TILE words (below).
+constexpr int SCAN_TILE = 4096;  // 256 threads x 16
+
 // pos[ct, slot] = the slot's first staging row, or -1 for a masked slot. Workgroup unit u covers
 // POS_SLOTS slots of chunk token u / tpt (tpt units per token), so the token and batch come from
 // one wave-uniform division per unit; a thread takes four slots 256 apart and issues each level of
-// its loads (indices, then the words and offsets they name) for all four before using any.
+// its loads (indices, then the words and tile bases they name) for all four before using any. A
+// word's first staging row is its scan tile's base plus its prefix inside the tile, both left by
+// the scan, so each slot reads one word at random.
 constexpr int POS_PER_THREAD = 4;
 constexpr int POS_SLOTS = 256 * POS_PER_THREAD;
 __global__ void __launch_bounds__(256)
 position_kernel(const int32_t* __restrict__ idx, const int2* __restrict__ bc, int32_t* __restrict__ cur,
-                const int32_t* __restrict__ offset, int32_t* __restrict__ pos, int64_t token0, int64_t n_chunk,
+                const int32_t* __restrict__ tile_base, int32_t* __restrict__ pos, int64_t token0, int64_t n_chunk,
                 int64_t S, int64_t S_kv, int topk, int64_t nw, int n_hblk) {
   constexpr int PU = POS_PER_THREAD;
   const int64_t tpt = (topk + POS_SLOTS - 1) / POS_SLOTS;
@@ -1841,23 +1846,25 @@ position_kernel(const int32_t* __restrict__ idx, const int2* __restrict__ bc, in
     int32_t v[PU];
 #pragma unroll
     for (int q = 0; q < PU; q++) v[q] = t0 + 256 * q < topk ? idx[token * topk + t0 + 256 * q] : -1;
+    // words after scan_tiles_kernel: {bits, prefix inside the scan tile | duplicate flag}
     int64_t e[PU];
     int2 w[PU];
-    int32_t off[PU];
+    int32_t tb[PU];
 #pragma unroll
     for (int q = 0; q < PU; q++) {
       e[q] = slot_in_range(v[q], S_kv) ? (b * S_kv + v[q]) * nw + k % nw : -1;
       w[q] = e[q] >= 0 ? bc[e[q]] : make_int2(0, 0);
-      off[q] = e[q] >= 0 ? offset[e[q]] : 0;
+      tb[q] = e[q] >= 0 ? tile_base[e[q] / SCAN_TILE] : 0;
     }
 #pragma unroll
     for (int q = 0; q < PU; q++) {
       int32_t r = -1;
       if (e[q] >= 0) {
-        if (w[q].y == __popc((uint32_t)w[q].x))
-          r = off[q] + n_hblk * __popc((uint32_t)w[q].x & ((1u << (k / nw)) - 1u));
+        const int32_t off = tb[q] + (w[q].y & 0x7FFFFFFF);  // the word's first staging row
+        if (w[q].y >= 0)
+          r = off + n_hblk * __popc((uint32_t)w[q].x & ((1u << (k / nw)) - 1u));
         else
-          r = off[q] + atomicAdd(cur + e[q], n_hblk);  // a word with duplicate pairs
+          r = off + atomicAdd(cur + e[q], n_hblk);  // a word with duplicate pairs
       }
       if (t0 + 256 * q < topk) pos[ct * topk + t0 + 256 * q] = r;
     }
@@ -1866,7 +1873,6 @@ position_kernel(const int32_t* __restrict__ idx, const int2* __restrict__ bc, in
 
 // Exclusive scan of n int32 counts into offset[0..n] (offset[n] = total), three passes:
 // per-tile scans of SCAN_TILE elements, a scan of the tile totals, then the tile bases.
-constexpr int SCAN_TILE = 4096;  // 256 threads x 16
 
 __device__ __forceinline__ int32_t block_exclusive_scan_256(int32_t v, int32_t* sh, int32_t* total) {
   // v: this thread's value; returns the exclusive prefix over the 256 threads of the block.
@@ -1886,28 +1892,55 @@ __device__ __forceinline__ int32_t block_exclusive_scan_256(int32_t v, int32_t* 
   return base + x - v;
 }
 
-// Scan input: element e is n_hblk times word e's pair count, the staging rows of its pairs.
+// Scan input: element e is n_hblk times word e's pair count, the staging rows of its pairs. The
+// tile passes through LDS (element l at l + l / 32, against bank conflicts) so that global loads
+// and stores run along consecutive elements while each thread scans 16 consecutive ones. The word
+// then trades its count for what position_kernel needs: its exclusive prefix inside the tile, with
+// bit 31 set when the count exceeds the popcount (a word holding duplicate pairs); the tile's base
+// comes from tile_sum once the totals are scanned.
 __global__ void __launch_bounds__(256)
-scan_tiles_kernel(const int2* __restrict__ bc, int32_t* __restrict__ out, int32_t* __restrict__ tile_sum,
+scan_tiles_kernel(int2* __restrict__ bc, int32_t* __restrict__ out, int32_t* __restrict__ tile_sum,
                   int64_t n, int n_hblk) {
   __shared__ int32_t sh[4];
-  const int64_t base = (int64_t)blockIdx.x * SCAN_TILE + threadIdx.x * 16;
+  __shared__ int32_t sv[SCAN_TILE + SCAN_TILE / 32];
+  const int64_t base = (int64_t)blockIdx.x * SCAN_TILE;
+  const int t = threadIdx.x;
+  int2 wd[16];
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const int l = 256 * i + t;
+    wd[i] = base + l < n ? bc[base + l] : make_int2(0, 0);
+    sv[l + l / 32] = n_hblk * wd[i].y;
+  }
+  __syncthreads();
   int32_t v[16];
   int32_t s = 0;
 #pragma unroll
   for (int i = 0; i < 16; i++) {
-    const int64_t e = base + i;
-    v[i] = e < n ? n_hblk * bc[e].y : 0;
+    const int l = 16 * t + i;
+    v[i] = sv[l + l / 32];
     s += v[i];
   }
   int32_t total;
   int32_t run = block_exclusive_scan_256(s, sh, &total);
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
-    if (base + i < n) out[base + i] = run;
+  for (int i = 0; i < 16; i++) {  // each thread overwrites only the elements it read
+    const int l = 16 * t + i;
+    sv[l + l / 32] = run;
     run += v[i];
   }
-  if (threadIdx.x == 0) tile_sum[blockIdx.x] = total;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const int l = 256 * i + t;
+    if (base + l < n) {
+      const int32_t ex = sv[l + l / 32];
+      out[base + l] = ex;
+      const bool dup = wd[i].y != __popc((uint32_t)wd[i].x);
+      bc[base + l] = make_int2(wd[i].x, dup ? (int32_t)(0x80000000u | (uint32_t)ex) : ex);
+    }
+  }
+  if (t == 0) tile_sum[blockIdx.x] = total;
 }
 
 // Single workgroup: exclusive scan of the tile totals (in place), total into out[n].
@@ -1928,11 +1961,11 @@ scan_totals_kernel(int32_t* __restrict__ tile_sum, int64_t n_tiles, int32_t* __r
 
 __global__ void __launch_bounds__(256)
 scan_add_kernel(int32_t* __restrict__ out, const int32_t* __restrict__ tile_sum, int64_t n) {
-  const int64_t base = (int64_t)blockIdx.x * SCAN_TILE + threadIdx.x * 16;
+  const int64_t base = (int64_t)blockIdx.x * SCAN_TILE + threadIdx.x;
   const int32_t add = tile_sum[blockIdx.x];
 #pragma unroll
   for (int i = 0; i < 16; i++)
-    if (base + i < n) out[base + i] += add;
+    if (base + 256 * i < n) out[base + 256 * i] += add;
 }
 
 // One workgroup per kv row: sum the row's staging segment in fp32 (fixed order), optionally add
@@ -2177,8 +2210,7 @@ hipError_t launch_dkv_prepare(const int32_t* idx, uint32_t* plan, int32_t* offse
                      S, S_kv, (int)topk, nw, n_rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t tiles = scan_tiles(n);
-  hipLaunchKernelGGL(scan_tiles_kernel, dim3((unsigned)tiles), dim3(256), 0, st, (const int2*)bc, offset, tile_sum,
-                     n, n_hblk);
+  hipLaunchKernelGGL(scan_tiles_kernel, dim3((unsigned)tiles), dim3(256), 0, st, bc, offset, tile_sum, n, n_hblk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(scan_totals_kernel, dim3(1), dim3(256), 0, st, tile_sum, tiles, offset, n);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -2186,7 +2218,7 @@ hipError_t launch_dkv_prepare(const int32_t* idx, uint32_t* plan, int32_t* offse
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t n_units = n_chunk * ((topk + POS_SLOTS - 1) / POS_SLOTS);
   hipLaunchKernelGGL(position_kernel, dim3(grid_for(n_units, 1)), dim3(256), 0, st, idx, (const int2*)bc, cur,
-                     (const int32_t*)offset, pos, token0, n_chunk, S, S_kv, (int)topk, nw, n_hblk);
+                     (const int32_t*)tile_sum, pos, token0, n_chunk, S, S_kv, (int)topk, nw, n_hblk);
   return hipGetLastError();
 }
 
