@@ -115,10 +115,11 @@ int sparse_mqa_fwd(const void* q, const void* kv, const float* attn_sink, const 
 }  // extern "C"
 
 // ---------------------------------------------------------------------------------------------
-// Backward workspace: [Delta (full bwd only)] [kv row norms] [selection bitmap, pair counts,
-// cursors] [offsets] [scan tiles] [acc (multi-chunk, bf16 output only)] [pos: chunk*topk int32]
-// [staging rows: chunk*(topk+1)*n_hblk rows of D fp16] [their exponents]. The bitmap part and the
-// offsets scale with the chunk (one bit per kv row and chunk token).
+// Backward workspace: [Delta (full bwd only)] [kv row norms] [selection bitmap words (bits and pair
+// count; after the scan, bits and the word's prefix inside its scan tile), cursors] [offsets]
+// [scan tiles] [acc (multi-chunk, bf16 output only)] [pos: chunk*topk int32] [staging rows:
+// chunk*(topk+1)*n_hblk rows of D int16] [their exponents] [dS (full bwd at D = 512)]. The bitmap
+// part and the offsets scale with the chunk (one bit per kv row and chunk token).
 
 namespace {
 
