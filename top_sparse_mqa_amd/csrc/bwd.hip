@@ -1752,14 +1752,14 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 // The plan takes no global atomics on the common path. For a chunk of n_chunk tokens, kv row `row`
 // of batch b has nw = ceil(min(n_chunk, S) / 32) words of a selection bitmap covering batch b's
 // tokens of the chunk, and the token with place k among them owns bit k / nw of word k % nw; a set
-// bit records that the token selects the row. Next to each word sits the count of its pairs
-// (bc[e] = {bits, count}, e = row * nw + word). An exclusive scan of n_hblk * count over the words
-// in (row, word) order gives each word the staging row of its first pair. In a word whose count
-// equals its popcount (each of its tokens selects the row once, as top-k selections do), a pair's
-// staging row is that plus n_hblk times the word's pairs below its bit: positions then depend on
-// the indices only, and row r's segment is [offset[r nw], offset[(r + 1) nw]). A word with
-// duplicate (token, row) pairs hands out its range [offset[e], offset[e + 1]) through an atomic
-// cursor cur[e] instead.
+// bit records that the token selects the row. Next to each word sits the count of its pairs (word
+// e = row * nw + word is stored as {bits, count} at bc[plan_word(row, word)]). An exclusive scan of
+// n_hblk * count over the words in (row, word) order gives each word the staging row of its first
+// pair. In a word whose count equals its popcount (each of its tokens selects the row once, as
+// top-k selections do), a pair's staging row is that plus n_hblk times the word's pairs below its
+// bit: positions then depend on the indices only, and row r's segment is
+// [offset[r nw], offset[(r + 1) nw]). A word with duplicate (token, row) pairs hands out its range
+// [offset[e], offset[e + 1]) through an atomic cursor cur[e] instead.
 
 // One workgroup per (word column w0, tile of MARK_ROWS kv rows): for each batch with rows in the
 // tile, the (up to 32) tokens with places w0 + nw j own every word of the column, so the workgroup
@@ -1767,6 +1767,14 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 // lets a workgroup sit beside a forward or dQ workgroup (~111 KiB) on one CU when the plan runs on
 // a side stream.
 constexpr int MARK_ROWS = 4096;
+// Storage place of word w of kv row `row` among the n_rows * nw words: tile-major, so that the mark
+// kernel's workgroup (word column w, tile of MARK_ROWS rows) writes its words as one contiguous run
+// (the last tile holds fewer rows). The scan walks the words in (row, word) order through this map.
+__device__ __forceinline__ int64_t plan_word(int64_t row, int64_t w, int64_t nw, int64_t n_rows) {
+  const int64_t t = row / MARK_ROWS, r0 = t * MARK_ROWS;
+  const int64_t rows_t = n_rows - r0 < MARK_ROWS ? n_rows - r0 : MARK_ROWS;
+  return r0 * nw + w * rows_t + (row - r0);
+}
 
 __global__ void __launch_bounds__(256)
 mark_kernel(const int32_t* __restrict__ idx, int2* __restrict__ bc, int64_t token0, int64_t n_chunk, int64_t S,
@@ -1815,7 +1823,8 @@ mark_kernel(const int32_t* __restrict__ idx, int2* __restrict__ bc, int64_t toke
       }
     }
     __syncthreads();
-    for (int r = threadIdx.x; r < nr; r += 256) bc[(r0 + r) * nw + w0] = make_int2((int)lb[r], lc[r]);
+    int2* out = bc + plan_word(r0, w0, nw, n_rows);  // the column's words of this tile, contiguous
+    for (int r = threadIdx.x; r < nr; r += 256) out[r] = make_int2((int)lb[r], lc[r]);
     __syncthreads();  // lb and lc are cleared for the next unit
   }
 }
@@ -1834,7 +1843,7 @@ constexpr int POS_SLOTS = 256 * POS_PER_THREAD;
 __global__ void __launch_bounds__(256)
 position_kernel(const int32_t* __restrict__ idx, const int2* __restrict__ bc, int32_t* __restrict__ cur,
                 const int32_t* __restrict__ tile_base, int32_t* __restrict__ pos, int64_t token0, int64_t n_chunk,
-                int64_t S, int64_t S_kv, int topk, int64_t nw, int n_hblk) {
+                int64_t S, int64_t S_kv, int topk, int64_t nw, int n_hblk, int64_t n_rows) {
   constexpr int PU = POS_PER_THREAD;
   const int64_t tpt = (topk + POS_SLOTS - 1) / POS_SLOTS;
   for (int64_t u = blockIdx.x; u < n_chunk * tpt; u += gridDim.x) {
@@ -1846,15 +1855,17 @@ position_kernel(const int32_t* __restrict__ idx, const int2* __restrict__ bc, in
     int32_t v[PU];
 #pragma unroll
     for (int q = 0; q < PU; q++) v[q] = t0 + 256 * q < topk ? idx[token * topk + t0 + 256 * q] : -1;
-    // words after scan_tiles_kernel: {bits, prefix inside the scan tile | duplicate flag}
+    // words after scan_tiles_kernel: {bits, prefix inside the scan tile | duplicate flag}; e is the
+    // word's place in (row, word) order (scan tiles, cursors), pw where it is stored
     int64_t e[PU];
     int2 w[PU];
     int32_t tb[PU];
 #pragma unroll
     for (int q = 0; q < PU; q++) {
-      e[q] = slot_in_range(v[q], S_kv) ? (b * S_kv + v[q]) * nw + k % nw : -1;
-      w[q] = e[q] >= 0 ? bc[e[q]] : make_int2(0, 0);
-      tb[q] = e[q] >= 0 ? tile_base[e[q] / SCAN_TILE] : 0;
+      const bool ok = slot_in_range(v[q], S_kv);
+      e[q] = ok ? (b * S_kv + v[q]) * nw + k % nw : -1;
+      w[q] = ok ? bc[plan_word(b * S_kv + v[q], k % nw, nw, n_rows)] : make_int2(0, 0);
+      tb[q] = ok ? tile_base[e[q] / SCAN_TILE] : 0;
     }
 #pragma unroll
     for (int q = 0; q < PU; q++) {
@@ -1900,16 +1911,22 @@ __device__ __forceinline__ int32_t block_exclusive_scan_256(int32_t v, int32_t* 
 // comes from tile_sum once the totals are scanned.
 __global__ void __launch_bounds__(256)
 scan_tiles_kernel(int2* __restrict__ bc, int32_t* __restrict__ out, int32_t* __restrict__ tile_sum,
-                  int64_t n, int n_hblk) {
+                  int64_t n, int n_hblk, int64_t nw, int64_t n_rows) {
   __shared__ int32_t sh[4];
   __shared__ int32_t sv[SCAN_TILE + SCAN_TILE / 32];
   const int64_t base = (int64_t)blockIdx.x * SCAN_TILE;
   const int t = threadIdx.x;
+  // element base + l is word (w0 + l) % nw of row row0 + (w0 + l) / nw
+  const int64_t row0 = base / nw;
+  const uint32_t w0 = (uint32_t)(base - row0 * nw), unw = (uint32_t)nw;
+  int64_t pw[16];
   int2 wd[16];
 #pragma unroll
   for (int i = 0; i < 16; i++) {
     const int l = 256 * i + t;
-    wd[i] = base + l < n ? bc[base + l] : make_int2(0, 0);
+    const uint32_t x = w0 + (uint32_t)l;
+    pw[i] = plan_word(row0 + x / unw, x % unw, nw, n_rows);
+    wd[i] = base + l < n ? bc[pw[i]] : make_int2(0, 0);
     sv[l + l / 32] = n_hblk * wd[i].y;
   }
   __syncthreads();
@@ -1937,7 +1954,7 @@ scan_tiles_kernel(int2* __restrict__ bc, int32_t* __restrict__ out, int32_t* __r
       const int32_t ex = sv[l + l / 32];
       out[base + l] = ex;
       const bool dup = wd[i].y != __popc((uint32_t)wd[i].x);
-      bc[base + l] = make_int2(wd[i].x, dup ? (int32_t)(0x80000000u | (uint32_t)ex) : ex);
+      bc[pw[i]] = make_int2(wd[i].x, dup ? (int32_t)(0x80000000u | (uint32_t)ex) : ex);
     }
   }
   if (t == 0) tile_sum[blockIdx.x] = total;
@@ -2210,7 +2227,8 @@ hipError_t launch_dkv_prepare(const int32_t* idx, uint32_t* plan, int32_t* offse
                      S, S_kv, (int)topk, nw, n_rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t tiles = scan_tiles(n);
-  hipLaunchKernelGGL(scan_tiles_kernel, dim3((unsigned)tiles), dim3(256), 0, st, bc, offset, tile_sum, n, n_hblk);
+  hipLaunchKernelGGL(scan_tiles_kernel, dim3((unsigned)tiles), dim3(256), 0, st, bc, offset, tile_sum, n, n_hblk, nw,
+                     n_rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(scan_totals_kernel, dim3(1), dim3(256), 0, st, tile_sum, tiles, offset, n);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -2218,7 +2236,7 @@ hipError_t launch_dkv_prepare(const int32_t* idx, uint32_t* plan, int32_t* offse
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t n_units = n_chunk * ((topk + POS_SLOTS - 1) / POS_SLOTS);
   hipLaunchKernelGGL(position_kernel, dim3(grid_for(n_units, 1)), dim3(256), 0, st, idx, (const int2*)bc, cur,
-                     (const int32_t*)tile_sum, pos, token0, n_chunk, S, S_kv, (int)topk, nw, n_hblk);
+                     (const int32_t*)tile_sum, pos, token0, n_chunk, S, S_kv, (int)topk, nw, n_hblk, n_rows);
   return hipGetLastError();
 }
 
