@@ -22,7 +22,8 @@ Beside the headline line's warm-cache step time it reports a cold-cache step tim
 preceded by a 1 GiB write that evicts L2 and the Infinity Cache), the rate counted over all
 B*S*topk slots (nominal) next to the valid pairs, and, as `gather_bound`, the same step timed on
 the batched gather workload (B=4, S=2048, S_kv=65536, uniform indices with masked slots) with each
-gathering kernel's row-gather rate against the HBM peak.
+gathering kernel's row-gather rate against the HBM peak, in the bench's schedule and with every
+kernel alone on one stream (`serial`).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                   [--calibration-copy] [--cold-steps C] [--gather-workload NAME] [--gather-steps G]
@@ -631,6 +632,9 @@ def main():
         xg = syn.workload_inputs(wg)
         ng = int(((xg["topk_idxs"] >= 0) & (xg["topk_idxs"] < wg.S_kv)).sum())
         rg = measure(smqa, wg, xg, args.gather_steps, 1, overlap=not args.serial)
+        # the same steps on one stream: each kernel alone on the GPU (the forward's gather rate
+        # without the staging plan beside it)
+        rs = rg if args.serial else measure(smqa, wg, xg, args.gather_steps, 1, overlap=False)
         del xg
         HDg = wg.H * wg.D
         out["gather_bound"] = {
@@ -640,6 +644,9 @@ def main():
             "tflops": round(14 * HDg * ng / (rg["ms_step"] * 1e-3) / 1e12, 3),
             "kernel_ms": {k: round(v, 4) for k, v in rg["ms"].items()},
             "gather": gather_rates(wg, ng, rg["ms"]),
+            "serial": {"ms_per_step": round(rs["ms_step"], 4),
+                       "kernel_ms": {k: round(v, 4) for k, v in rs["ms"].items()},
+                       "gather": gather_rates(wg, ng, rs["ms"])},
             "step_algorithmic_GB": round(algorithmic_bytes(wg, ng) / 1e9, 2),
             "step_algorithmic_GBps": round(algorithmic_bytes(wg, ng) / (rg["ms_step"] * 1e-3) / 1e9, 1),
             "step_algorithmic_frac_hbm": round(algorithmic_bytes(wg, ng) / (rg["ms_step"] * 1e-3) / 1e9
