@@ -125,7 +125,8 @@ class Step:
         if st != 0:
             raise RuntimeError(f"{name}: status {st} {self.lib.sparse_mqa_status_string(st).decode()}")
 
-    def run(self, timed: bool):
+    def run(self, timed: bool, step_event: bool = False):
+        """One step; timed: events around every kernel and the step, step_event: around the step only."""
         w, L = self.w, self.lib
         B, S, S_kv, H, D, K = w.B, w.S, w.S_kv, w.H, w.D, w.topk
         p = lambda t: t.data_ptr()  # noqa: E731
@@ -153,7 +154,7 @@ class Step:
             if timed:
                 ev[k][1].record(st)
 
-        if timed:
+        if timed or step_event:
             st_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             st_ev[0].record(self.stream)
         if self.side is None:
@@ -172,10 +173,11 @@ class Step:
             self.stream.wait_event(ready)
             for k in ("bwd_dkv_partials", "bwd_dkv_dq", "bwd_dkv_reduce"):
                 launch(k, self.stream)
-        if timed:
+        if timed or step_event:
             st_ev[1].record(self.stream)  # the side stream joined the main one before the partials
-            self.events.append(ev)
             self.step_events.append(st_ev)
+        if timed:
+            self.events.append(ev)
 
     def step_ms_median(self):
         import statistics
@@ -270,8 +272,9 @@ def traffic_for(step: str, workload: str):
 
 def summarize_trace(stats_csv: str, out_path: str, workload: str) -> None:
     """Kernel times of a rocprofv3 --kernel-trace --stats run as a table: the statistics over every
-    dispatch, and, from the per-dispatch trace beside it, the mean over the timed steps' dispatches
-    (the last PROFILE_STEPS of each kernel), which is what the bench line's event times cover."""
+    dispatch, and, from the per-dispatch trace beside it, the mean over the last PROFILE_STEPS
+    dispatches of each kernel: the steps with events around every kernel, which the bench line's
+    kernel times cover."""
     import csv
 
     rows = list(csv.DictReader(open(stats_csv)))
@@ -288,13 +291,14 @@ def summarize_trace(stats_csv: str, out_path: str, workload: str) -> None:
             last = [d for _, d in v[-PROFILE_STEPS:]]
             timed[k] = sum(last) / len(last)
     lines = [f"# Kernel trace: {workload}", "",
-             f"rocprofv3 kernel-trace statistics of a short bench run ({PROFILE_WARMUP} warmup and {PROFILE_STEPS} timed "
-             "steps): every dispatch, and the mean over the timed steps' dispatches.", "",
+             f"rocprofv3 kernel-trace statistics of a short bench run ({PROFILE_WARMUP} warmup steps, {PROFILE_STEPS} timed "
+             f"steps, then {PROFILE_STEPS} steps with events around every kernel): every dispatch, and the mean over "
+             "the last of these, whose times the bench line's kernel times are.", "",
              "Command (from the repository root on one MI355X; `<out>` an output directory):", "", "```",
              f"rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o trace -- python bench.py "
              f"--workload {workload} {PROFILE_ARGS}",
              f"python bench.py --workload {workload} --summarize-trace <out>/trace_kernel_stats.csv --out <this file>",
-             "```", "", "| kernel | calls | avg (us) | timed-step avg (us) | min (us) | max (us) | share |",
+             "```", "", "| kernel | calls | avg (us) | avg, last steps (us) | min (us) | max (us) | share |",
              "|---|---|---|---|---|---|---|"]
     for r in rows:
         name = r["Name"].split("(")[0].replace("void ", "")
@@ -464,8 +468,10 @@ def cpu_info():
 
 
 def measure(smqa, w, x, steps, warmup, overlap=True, cold_steps=0, calibration_copy=False):
-    """Warm step time and per-kernel event times over `steps` steps (after `warmup`), then, if
-    cold_steps, the step time with a cache-evicting write before each step (outside the timed span)."""
+    """Warm step time over `steps` steps (after `warmup`), with events around each step only; then
+    per-kernel event times over as many steps again (events around every kernel, which add a few
+    hundredths of a millisecond per step, so they stay out of the step time); then, if cold_steps,
+    the step time with a cache-evicting write before each step (outside the timed span)."""
     step = Step(smqa, w, x, overlap=overlap)
     if calibration_copy:
         src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda:0")
@@ -480,25 +486,33 @@ def measure(smqa, w, x, steps, warmup, overlap=True, cold_steps=0, calibration_c
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(steps):
-        step.run(timed=True)
+        step.run(timed=False, step_event=True)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    res = {"ms_step": start.elapsed_time(end) / steps, "ms": step.kernel_ms(), "wall": wall,
-           "ms_step_median": step.step_ms_median()}
+    res = {"ms_step": start.elapsed_time(end) / steps, "wall": wall, "ms_step_median": step.step_ms_median()}
+    step.events = []
+    for _ in range(steps):
+        step.run(timed=True)
+    torch.cuda.synchronize()
+    res["ms"] = step.kernel_ms()
     if cold_steps > 0:
         flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
-        step.events = []
         tot = 0.0
-        for _ in range(cold_steps):
+        for _ in range(cold_steps):  # step times
             flush.zero_()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            step.run(timed=True)
+            step.run(timed=False)
             b.record()
             torch.cuda.synchronize()
             tot += a.elapsed_time(b)
         res["cold_ms_step"] = tot / cold_steps
+        step.events = []
+        for _ in range(cold_steps):  # kernel times
+            flush.zero_()
+            step.run(timed=True)
+            torch.cuda.synchronize()
         res["cold_ms"] = step.kernel_ms()
         del flush
     del step
