@@ -689,14 +689,17 @@ bwd_dq_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv
 // Eight waves, two per SIMD. Wave w owns d-columns 64 w .. 64 w + 63 of all 64 heads (dQ^T
 // accumulators) and gathers rows w, w + 8, w + 16, w + 24 of every tile; waves 0-3 also copy one
 // 1 KiB fragment each of the block's dS (stored in B-fragment order) into LDS, so dS crosses the
-// vector memory path once per workgroup instead of once per wave. Three buffers of each: during
-// block j the copies for blocks j + 1 and j + 2 are in flight. Every stage issues its vector memory
-// instructions in one fixed order (masked rows and tiles past the end read the zero row; dS copies
-// past the end repeat the last block), so one fixed vmcnt wait per wave at the top of a stage finds
-// that wave's copies for block j complete while later ones stay in flight; the copies are issued so
-// that the compiler adds no waits of its own (dma16_buf_unordered).
+// vector memory path once per workgroup instead of once per wave. Two buffers of each: during block
+// j the copies for block j + 1 are in flight, and at 72 KiB of LDS and at most 128 registers two
+// workgroups share a CU, each covering the other's waits (against three buffers and one workgroup
+// per CU: 0.62 against 0.76 ms on the headline workload, 5.7 against 6.6 ms on the long-context
+// one, within noise with a 256 MiB kv table). Every stage issues its vector memory instructions in
+// one fixed order (masked rows and tiles past the end read the zero row; dS copies past the end
+// repeat the last block), so the wait at the top of a stage for block j's copies, the wave's newest
+// accesses, is a plain vmcnt(0); the copies are issued so that the compiler adds no waits of its own
+// (dma16_buf_unordered).
 template <int D>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(512, 2)
 bwd_dq_ds_kernel(const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx, const uint16_t* __restrict__ ds,
                  uint16_t* __restrict__ dq, int S, int64_t S_kv, int H, int topk, float sm_scale, int n_hblk,
                  int token0, int n_tokens) {
@@ -709,10 +712,8 @@ bwd_dq_ds_kernel(const uint16_t* __restrict__ kv, const int32_t* __restrict__ id
   static_assert(ROWB == 1024 && NDT * 32 == DW && NP == 4, "one kv row per gather instruction, four per wave");
   __shared__ __attribute__((aligned(16))) char tile0[TB];
   __shared__ __attribute__((aligned(16))) char tile1[TB];
-  __shared__ __attribute__((aligned(16))) char tile2[TB];
   __shared__ __attribute__((aligned(16))) char dsb0[DSB];
   __shared__ __attribute__((aligned(16))) char dsb1[DSB];
-  __shared__ __attribute__((aligned(16))) char dsb2[DSB];
   __shared__ int last_s[NWV];
 
   const int lane = threadIdx.x & 63;
@@ -754,8 +755,8 @@ bwd_dq_ds_kernel(const uint16_t* __restrict__ kv, const int32_t* __restrict__ id
     const int t = blk * T + lane;
     return (blk < nblk && lane < T && t < topk) ? idx_tok[t] : -1;
   };
-  auto tile_at = [&](int k) -> char* { return k == 0 ? tile0 : (k == 1 ? tile1 : tile2); };
-  auto dsb_at = [&](int k) -> char* { return k == 0 ? dsb0 : (k == 1 ? dsb1 : dsb2); };
+  auto tile_at = [&](int k) -> char* { return k == 0 ? tile0 : tile1; };
+  auto dsb_at = [&](int k) -> char* { return k == 0 ? dsb0 : dsb1; };
   const char* kv_b = (const char*)(kv + b * S_kv * D);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kv_b, (int)(uint32_t)(S_kv * ROWB));
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(g_zero_row_bwd, ROWB);
@@ -792,26 +793,22 @@ bwd_dq_ds_kernel(const uint16_t* __restrict__ kv, const int32_t* __restrict__ id
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[dt][hh][r] = 0.f;
 
-  // indices of blocks j, j + 1, j + 2 at the top of stage j
-  int32_t ia = load_idx(0), ib = load_idx(1), ic = load_idx(2);
+  // indices of blocks j and j + 1 at the top of stage j
+  int32_t ia = load_idx(0), ib = load_idx(1);
   copy_block(0, ia, tile0, dsb0);
   __builtin_amdgcn_sched_barrier(0);
-  copy_block(1, ib, tile1, dsb1);
-  __builtin_amdgcn_sched_barrier(0);
 
-  // Stage j issues, in this order: the index of block j + 3 (none past the end), then the copies of
-  // block j + 2. At the top of stage j the copies of block j (stage j - 2) are needed; issued after
-  // them are the index of block j + 2 (needed too) and the copies of block j + 1: four row copies and,
-  // on waves 0-3, one dS copy.
+  // Stage j issues, in this order: the index of block j + 2 (none past the end), then the copies of
+  // block j + 1. At the top of stage j the copies of block j (stage j - 1), the newest accesses of
+  // every wave, are needed.
   auto stage = [&](auto buf_tag, int j) {
     constexpr int BUF = decltype(buf_tag)::value;
-    if (wu < 4) __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5); lgkmcnt and expcnt at their maxima
-    else __builtin_amdgcn_s_waitcnt(0x0F74);         // vmcnt(4)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); lgkmcnt and expcnt at their maxima
     lds_barrier();  // every wave's copies of block j; every wave done with the buffers of block j - 1
     const uint64_t mask = __ballot(slot_in_range(ia, S_kv));
-    const int32_t id = load_idx(j + 3);
+    const int32_t ic = load_idx(j + 2);
     __builtin_amdgcn_sched_barrier(0);
-    copy_block(j + 2, ic, tile_at((BUF + 2) % 3), dsb_at((BUF + 2) % 3));  // into the buffers of block j - 1
+    copy_block(j + 1, ib, tile_at(1 - BUF), dsb_at(1 - BUF));  // into the buffers of block j - 1
     __builtin_amdgcn_sched_barrier(0);
     if (mask) {
       const char* tile = tile_at(BUF);
@@ -837,12 +834,10 @@ bwd_dq_ds_kernel(const uint16_t* __restrict__ kv, const int32_t* __restrict__ id
     }
     ia = ib;
     ib = ic;
-    ic = id;
   };
-  for (int j = 0; j < nblk; j += 3) {
+  for (int j = 0; j < nblk; j += 2) {
     stage(IntTag<0>{}, j);
     if (j + 1 < nblk) stage(IntTag<1>{}, j + 1);
-    if (j + 2 < nblk) stage(IntTag<2>{}, j + 2);
   }
   wait_all_mem();  // no copy may still write LDS when the workgroup ends
   // dQ = sm_scale * (dS K), bf16; dQ^T C layout: lane holds head 32 hh + (lane & 31),
