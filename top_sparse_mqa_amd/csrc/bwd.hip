@@ -1759,8 +1759,8 @@ bwd_dkv_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 // One workgroup per (word column w0, tile of MARK_ROWS kv rows): for each batch with rows in the
 // tile, the (up to 32) tokens with places w0 + nw j own every word of the column, so the workgroup
 // builds the tile's words in LDS (LDS atomics) and writes them out with plain stores. 32 KiB of LDS
-// lets a workgroup sit beside a forward or dQ workgroup (~111 KiB) on one CU when the plan runs on
-// a side stream.
+// lets a workgroup sit beside a forward workgroup (~117 KiB) on one CU when the plan runs on a side
+// stream.
 constexpr int MARK_ROWS = 4096;
 // Storage place of word w of kv row `row` among the n_rows * nw words: tile-major, so that the mark
 // kernel's workgroup (word column w, tile of MARK_ROWS rows) writes its words as one contiguous run
