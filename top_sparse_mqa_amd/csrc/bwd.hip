@@ -693,11 +693,11 @@ bwd_dq_ws_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv
 // j the copies for block j + 1 are in flight, and at 72 KiB of LDS and at most 128 registers two
 // workgroups share a CU, each covering the other's waits (against three buffers and one workgroup
 // per CU: 0.62 against 0.76 ms on the headline workload, 5.7 against 6.6 ms on the long-context
-// one, within noise with a 256 MiB kv table). Every stage issues its vector memory instructions in
-// one fixed order (masked rows and tiles past the end read the zero row; dS copies past the end
-// repeat the last block), so the wait at the top of a stage for block j's copies, the wave's newest
-// accesses, is a plain vmcnt(0); the copies are issued so that the compiler adds no waits of its own
-// (dma16_buf_unordered).
+// one, 2.55-2.62 against 2.50-2.57 ms with a 256 MiB kv table). Every stage issues its vector
+// memory instructions in one fixed order (masked rows and tiles past the end read the zero row; dS
+// copies past the end repeat the last block), so the wait at the top of a stage for block j's
+// copies, the wave's newest accesses, is a plain vmcnt(0); the copies are issued so that the
+// compiler adds no waits of its own (dma16_buf_unordered).
 template <int D>
 __global__ void __launch_bounds__(512, 2)
 bwd_dq_ds_kernel(const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx, const uint16_t* __restrict__ ds,
