@@ -2,19 +2,21 @@
 """Throughput of the top-k sparse MQA hot path (forward + backward) on one MI355X.
 
 One step = one pass of the whole path over one batch of seeded synthetic input: the forward
-(O, LSE), then the backward on those outputs (Delta preprocess, dQ kernel, and the dKV stage:
-the staging plan (selection bitmap, scan, positions), the dKV kernel writing each pair's
-contribution row, and the per-row reduction that also emits the bf16 dKV). Inputs are resident in HBM before timing starts.
+(O, LSE), then the backward on those outputs: the Delta preprocess, the staging plan (selection
+bitmap, scan, positions; on a second stream beside the forward), the dKV partials kernel writing
+each pair's contribution row and the dS, dQ from that dS, and the per-row reduction that also
+emits the bf16 dKV. Inputs are resident in HBM before timing starts.
 
 Prints one JSON line. `value` is the step's algorithmic TFLOP/s: (4 + 10) * H * D flops per valid
 (token, slot) pair (forward 4HD: QK^T and PV; backward 10HD: score recompute, dP, dQ, dKV) divided
-by the measured step time. Per-kernel times come from HIP events recorded on the stream the
-kernels run on; the dKV stage runs as its three library steps (prepare, partials, reduce) so the
-partials kernel is timed alone.
+by the measured step time, which is taken with events around each step only. Per-kernel times come
+from as many steps again with HIP events recorded around every kernel on the stream it runs on;
+the backward runs as its library steps (preprocess, prepare, partials, dq, reduce), so each kernel
+is timed alone.
 
 `roofline` is for the longest single-kernel step, with its own algorithmic flops per valid pair
-(forward 4HD; dQ kernel 6HD: S and dP recompute, dQ; dKV partials kernel 8HD: S and dP recompute,
-dS^T Q and P^T dO). `traffic` is that kernel's HBM bytes per launch from the rocprofv3 FETCH_SIZE
+(forward 4HD; dQ from the stored dS 2HD; dKV partials kernel 8HD: S and dP recompute, dS^T Q and
+P^T dO). `traffic` is that kernel's HBM bytes per launch from the rocprofv3 FETCH_SIZE
 and WRITE_SIZE summary under profiles/, scaled by the same counters' reading for a copy of known
 size, and null once the kernel source differs from the one the counters were taken on.
 
